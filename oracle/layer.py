@@ -1,0 +1,169 @@
+"""The hybrid attention layer, computed plainly in float64 (oracle; test infrastructure).
+
+Sources, all in the VDN-MiniMax-H3 article (modelscope.csdn.net):
+
+* "局部精确计算，远程线性记忆", paragraph 1: exact softmax attention over the local
+  window plus the two anchor frames; bidirectional linear attention over the rest.
+* same section, paragraph 2: the forward and backward states are aligned to the
+  query's position and read with the query; their reads form the linear output.
+* same section, paragraph 3: text tokens are keys of every frame in the softmax branch;
+  in the linear branch text initialises both states at half weight so it counts once.
+* "独立门控，融合两条注意力分支": each branch has its own input-dependent sigmoid gate and
+  its own output projection into the residual stream; the linear branch is RMS-normalised
+  before an elementwise gate.
+
+Array layouts: q, k, v, gates [N, H, d] with token n in frame n // T; text_k, text_v
+[L, H, d]; w_rms [H, d]; w_s, w_l [D, H*d] (output rows, input columns); x [N, D].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import sets
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def frame_tokens(frame_list, tokens_per_frame: int) -> np.ndarray:
+    """Token indices of the listed frames, in frame order."""
+    if len(frame_list) == 0:
+        return np.zeros(0, np.int64)
+    return np.concatenate([np.arange(g * tokens_per_frame, (g + 1) * tokens_per_frame)
+                           for g in frame_list])
+
+
+def softmax_branch(q, k, v, text_k, text_v, frames: int, chunk_frames: int,
+                   neighbor_chunks: int = 1, scale: float | None = None, rows=None) -> np.ndarray:
+    """o_soft [len(rows) or N, H, d]: exact softmax over the query frame's key set.
+
+    The keys of a query in frame f are all text tokens and the tokens of every frame in
+    ``sets.softmax_frames(f)``, each once.  s_j = scale q.k_j, o = sum_j e^(s_j - max) v_j
+    / sum_j e^(s_j - max).
+    """
+    q, k, v, text_k, text_v = map(_f64, (q, k, v, text_k, text_v))
+    N, H, d = q.shape
+    T = N // frames
+    scale = d ** -0.5 if scale is None else scale
+    rows = np.arange(N) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((len(rows), H, d))
+    row_frame = rows // T
+    for f in np.unique(row_frame):
+        sel = np.nonzero(row_frame == f)[0]
+        idx = frame_tokens(sets.softmax_frames(int(f), frames, chunk_frames, neighbor_chunks), T)
+        keys = np.concatenate([text_k, k[idx]], axis=0)      # [L + |idx|, H, d]
+        vals = np.concatenate([text_v, v[idx]], axis=0)
+        for h in range(H):
+            s = scale * (q[rows[sel], h, :] @ keys[:, h, :].T)
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            out[sel, h, :] = (p @ vals[:, h, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def frame_states(k, v, frames: int) -> np.ndarray:
+    """S [F, H, d, d]: S[g, h] = sum over tokens t of frame g of k_t^T v_t.
+
+    Anchor frames are not part of either linear state, so their slots are zero.
+    """
+    k, v = _f64(k), _f64(v)
+    N, H, d = k.shape
+    T = N // frames
+    S = np.zeros((frames, H, d, d))
+    for g in range(frames):
+        if sets.is_anchor(g, frames):
+            continue
+        kg, vg = k[g * T:(g + 1) * T], v[g * T:(g + 1) * T]
+        for h in range(H):
+            S[g, h] = kg[:, h, :].T @ vg[:, h, :]
+    return S
+
+
+def text_state(text_k, text_v) -> np.ndarray:
+    """Tx [H, d, d] = sum over text tokens of k^T v."""
+    text_k, text_v = _f64(text_k), _f64(text_v)
+    L, H, d = text_k.shape
+    Tx = np.zeros((H, d, d))
+    for h in range(H):
+        Tx[h] = text_k[:, h, :].T @ text_v[:, h, :]
+    return Tx
+
+
+def side_states(S, Tx, frames: int, chunk_frames: int, neighbor_chunks: int = 1):
+    """(S_fwd, S_bwd), each [F, H, d, d], aligned to every query frame f.
+
+    S_fwd[f] = Tx/2 + sum of S[g] over the forward frames of f;
+    S_bwd[f] = Tx/2 + sum of S[g] over the backward frames of f.
+    """
+    S, Tx = _f64(S), _f64(Tx)
+    fwd = np.zeros_like(S)
+    bwd = np.zeros_like(S)
+    for f in range(frames):
+        fwd[f] = 0.5 * Tx
+        bwd[f] = 0.5 * Tx
+        for g in sets.forward_frames(f, frames, chunk_frames, neighbor_chunks):
+            fwd[f] += S[g]
+        for g in sets.backward_frames(f, frames, chunk_frames, neighbor_chunks):
+            bwd[f] += S[g]
+    return fwd, bwd
+
+
+def linear_read(q, S_fwd, S_bwd, frames: int, rows=None) -> np.ndarray:
+    """u [len(rows) or N, H, d] = q.S_fwd[frame] + q.S_bwd[frame] (two reads, summed)."""
+    q = _f64(q)
+    N, H, d = q.shape
+    T = N // frames
+    rows = np.arange(N) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((len(rows), H, d))
+    for i, n in enumerate(rows):
+        f = n // T
+        for h in range(H):
+            out[i, h] = q[n, h] @ S_fwd[f, h] + q[n, h] @ S_bwd[f, h]
+    return out
+
+
+def linear_branch(q, k, v, text_k, text_v, frames: int, chunk_frames: int,
+                  neighbor_chunks: int = 1, rows=None) -> np.ndarray:
+    S = frame_states(k, v, frames)
+    Tx = text_state(text_k, text_v)
+    fwd, bwd = side_states(S, Tx, frames, chunk_frames, neighbor_chunks)
+    return linear_read(q, fwd, bwd, frames, rows)
+
+
+def rms_norm(u, w, eps: float = 1e-6) -> np.ndarray:
+    """u / sqrt(mean over head_dim of u^2 + eps), times the weight of (head, channel)."""
+    u, w = _f64(u), _f64(w)
+    return u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps) * w
+
+
+def sigmoid(x) -> np.ndarray:
+    x = _f64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def project(a_s, a_l, w_s, w_l, x) -> np.ndarray:
+    """out = x + a_s W_s^T + a_l W_l^T with heads concatenated head-major."""
+    a_s, a_l, w_s, w_l, x = map(_f64, (a_s, a_l, w_s, w_l, x))
+    n = a_s.shape[0]
+    return x + a_s.reshape(n, -1) @ w_s.T + a_l.reshape(n, -1) @ w_l.T
+
+
+def layer(q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, frames: int,
+          chunk_frames: int, neighbor_chunks: int = 1, eps: float = 1e-6,
+          scale: float | None = None, q_lin=None, k_lin=None, v_lin=None) -> dict:
+    """Full layer.  Returns codes, o_soft, u, a_s, a_l, out.
+
+    q_lin/k_lin/v_lin, when given, feed the linear branch instead of q/k/v (the
+    softmax branch may see a lower-precision copy of the same activations).
+    """
+    ql = q if q_lin is None else q_lin
+    kl = k if k_lin is None else k_lin
+    vl = v if v_lin is None else v_lin
+    o_soft = softmax_branch(q, k, v, text_k, text_v, frames, chunk_frames, neighbor_chunks, scale)
+    u = linear_branch(ql, kl, vl, text_k, text_v, frames, chunk_frames, neighbor_chunks)
+    a_s = sigmoid(g_s) * o_soft
+    a_l = sigmoid(g_l) * rms_norm(u, w_rms, eps)
+    out = project(a_s, a_l, w_s, w_l, x)
+    return dict(codes=sets.code_matrix(frames, chunk_frames, neighbor_chunks),
+                o_soft=o_soft, u=u, a_s=a_s, a_l=a_l, out=out)

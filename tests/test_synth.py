@@ -1,0 +1,57 @@
+"""The seeded input generator (CPU only): determinism, storage rounding, fp8 scales."""
+import numpy as np
+import torch
+
+from video_diffusion_hybrid_sparse_amd import shapes, synth
+
+
+def test_deterministic_and_seed_sensitive():
+    a = synth.make_inputs(shapes.TOY)
+    b = synth.make_inputs(shapes.TOY)
+    c = synth.make_inputs(shapes.TOY, seed=7)
+    for name in ("q", "k", "v", "text_k", "text_v", "g_s", "g_l", "w_rms", "w_s", "w_l", "x"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+        assert not torch.equal(getattr(a, name), getattr(c, name)), name
+
+
+def test_shapes_and_dtypes():
+    s = shapes.MID
+    inp = synth.make_inputs(s)
+    N, H, d, L, D = s.tokens, s.heads, s.head_dim, s.text_len, s.dmodel
+    assert inp.q.shape == (N, H, d) and inp.q.dtype == torch.bfloat16
+    assert inp.text_k.shape == (L, H, d) and inp.g_l.shape == (N, H, d)
+    assert inp.w_rms.shape == (H, d) and inp.w_rms.dtype == torch.float32
+    assert inp.w_s.shape == (D, H * d) and inp.x.shape == (N, D)
+    # mid-size inputs are scaled by d^-1/2
+    assert abs(float(inp.q.float().std()) - d ** -0.5) < 0.01
+
+
+def test_chunked_draws_do_not_depend_on_threads():
+    n = (1 << 22) + 12345
+    a = synth._normal(5, 3, n)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([5, 3, 1])))
+    np.testing.assert_array_equal(a[1 << 22:], g.standard_normal(12345, dtype=np.float32))
+
+
+def test_e4m3_quantiser():
+    t = torch.from_numpy(np.random.default_rng(0).standard_normal(10000).astype(np.float32)).bfloat16()
+    codes, scale = synth.quantize_e4m3(t)
+    assert codes.dtype == torch.uint8
+    assert abs(scale - float(t.abs().max()) / 448.0) < 1e-12
+    vals = synth.e4m3_values(codes)
+    assert float(vals.abs().max()) == 448.0
+    # e4m3 keeps 3 mantissa bits: relative error at most 2^-4 above the subnormal range
+    x = t.float() / scale
+    big = x.abs() > 2 ** -6
+    assert float(((vals - x).abs() / x.abs())[big].max()) <= 2 ** -4 + 1e-7
+    # every e4m3 value is exact in bf16
+    assert torch.equal(vals.bfloat16().float(), vals)
+
+
+def test_membership_probe_inputs():
+    s = shapes.WORKED
+    p = synth.membership_probe_inputs(s)
+    assert float(p.q.abs().sum()) == 0.0
+    frame = torch.arange(s.tokens) // s.tokens_per_frame
+    assert torch.equal(p.v[:, 0, :].float().argmax(-1), frame)
+    assert float(p.text_v[:, :, s.frames].float().min()) == 1.0
