@@ -1,0 +1,154 @@
+"""Benchmark of one VDN-H3 hybrid attention layer forward on one MI355X.
+
+A step is one full layer forward (state build, state scan, linear read + RMSNorm +
+gate, block-sparse softmax + gate, both projections + residual) over the 768p layer
+shape: 60 latent frames x 1008 tokens, 48 heads, head_dim 128, 512 text tokens, chunks
+of 5 frames, model dim 6144, bf16, on seeded synthetic inputs already resident in HBM.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole layer; per-step
+kernel times come from HIP events the library records on its stream during the timed
+steps.  The CPU baseline times the fp64 oracle on a bounded sample of the same layer.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "hybrid-attn layer ms + TFLOP/s (% MFMA peak) at 768p 60-frame shape, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(shape, inp, budget_s: float = 20.0) -> dict:
+    """Time the oracle (as it is) on a bounded sample of the layer: all four steps for a
+    subset of heads and the query tokens of a few frames, on the host cores."""
+    import numpy as np
+
+    import oracle
+    from video_diffusion_hybrid_sparse_amd import synth
+
+    F, T, C, R, H, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.neighbor_chunks, shape.heads, shape.head_dim
+    frames = [0, 1, F // 2, F - 2]
+    rows = np.concatenate([np.arange(f * T, (f + 1) * T) for f in frames])
+    heads = list(range(2))
+    cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
+
+    def sub(t):
+        return np.ascontiguousarray(synth.f64(t)[:, heads, :])
+
+    q, k, v, tk, tv = (sub(t) for t in (inp.q, inp.k, inp.v, inp.text_k, inp.text_v))
+    g_s, g_l = sub(inp.g_s)[rows], sub(inp.g_l)[rows]
+    w = synth.f64(inp.w_rms)[heads]
+    w_s, w_l = synth.f64(inp.w_s)[:, cols], synth.f64(inp.w_l)[:, cols]
+    x = synth.f64(inp.x)[rows]
+    t0 = time.perf_counter()
+    o = oracle.layer.softmax_branch(q, k, v, tk, tv, F, C, R, rows=rows)
+    u = oracle.layer.linear_branch(q, k, v, tk, tv, F, C, R, rows=rows)
+    a_s = oracle.layer.sigmoid(g_s) * o
+    a_l = oracle.layer.sigmoid(g_l) * oracle.layer.rms_norm(u, w, shape.rms_eps)
+    oracle.layer.project(a_s, a_l, w_s, w_l, x)
+    dt = time.perf_counter() - t0
+    from video_diffusion_hybrid_sparse_amd import workload
+    kpf = workload.keys_per_frame(shape)
+    nh = len(heads)
+    fl = (4 * d * nh * sum(kpf[f] * T for f in frames) + 2 * d * d * nh * (T * (F - 2) + shape.text_len)
+          + 2 * d * d * nh * len(rows) + 2 * len(rows) * 2 * nh * d * shape.dmodel)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"fp64 oracle, all four steps for heads {heads} of {H} and the query tokens of frames "
+                      f"{frames} ({len(rows)} tokens); projection restricted to those heads' input columns; "
+                      f"{fl / 1e9:.1f} GFLOP of the layer's algorithmic work"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer is not sharded across GPUs (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth, workload
+
+    shape = shapes.P768
+    log("bench: generating inputs", shape.name)
+    inp = synth.make_inputs(shape)
+    dl = runner.upload(inp)
+    torch.cuda.synchronize()
+    log("bench: warmup", args.warmup)
+    for _ in range(args.warmup):
+        dl.run()
+    torch.cuda.synchronize()
+    binding.profile_enable(True)
+    binding.profile_read()  # clear
+    log("bench: timing", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dl.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms, calls = binding.profile_read()
+    binding.profile_enable(False)
+    assert calls == args.steps
+    ms = (t1 - t0) * 1e3 / args.steps
+    fl = workload.flops(shape)
+    by = workload.bytes_moved(shape)
+    per = {k: v / args.steps for k, v in step_ms.items()}
+    sm_ms = per["softmax"]
+    achieved = fl["softmax"] / (sm_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(fl["total"] / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations and gate logits, scaled N(0,1) weights, 768p layer shape",
+        "config": {"workload": shape.name, "frames": shape.frames, "tokens_per_frame": shape.tokens_per_frame,
+                   "heads": shape.heads, "head_dim": shape.head_dim, "text_len": shape.text_len,
+                   "chunk_frames": shape.chunk_frames, "model_dim": shape.dmodel,
+                   "layer_tflop": round(fl["total"] / 1e12, 3)},
+        "pct_mfma_peak": round(100 * fl["total"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"kernel": "softmax_bf16_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "steps_ms": {k: round(v, 4) for k, v in per.items()},
+        "steps_rate": {
+            "softmax_tflops": round(achieved, 1),
+            "projection_tflops": round(fl["projection"] / (per["projection"] * 1e-3) / 1e12, 1),
+            "state_build_gbs": round(by["state_build"] / (per["state_build"] * 1e-3) / 1e9, 1),
+            "state_scan_gbs": round(by["state_scan"] / (per["state_scan"] * 1e-3) / 1e9, 1),
+            "linear_read_gbs": round(by["linear_read"] / (per["linear_read"] * 1e-3) / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle on a sample)")
+        res["cpu_baseline"] = cpu_baseline(shape, inp)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,158 @@
+/*
+ * vdn_hybrid_attn.h -- C ABI of the MI355X (gfx950) VDN-H3 hybrid attention layer.
+ *
+ * The layer is the one described in the VDN-MiniMax-H3 article on modelscope.csdn.net
+ * ("VDN-MiniMax-H3 开源：全新混合注意力加速视频生成"):
+ *   - section "局部精确计算，远程线性记忆", paragraph 1: video tokens are grouped by latent
+ *     frame; chunks of C consecutive frames attend (exact softmax) to their own chunk and
+ *     the neighbouring chunk on each side; the first and last frames are two-way anchors;
+ *     a bidirectional linear branch summarises the frames before and after the window,
+ *     leaving out window and anchor frames;
+ *   - same section, paragraph 3: every frame attends to all text tokens in the softmax
+ *     branch; text initialises both linear states at half weight;
+ *   - section "独立门控，融合两条注意力分支": per-branch sigmoid gates, RMSNorm then an
+ *     elementwise gate on the linear branch, separate output projections added into the
+ *     residual stream.
+ *
+ * Readings where the article is silent (the same in every kernel): chunks start at
+ * frame 0 and the window is clipped at the clip ends; anchor query frames read every
+ * frame by softmax and only text through the linear states; linear attention uses the
+ * identity feature map, an additive per-frame state k^T v, no normaliser; the forward
+ * and backward reads are summed; softmax scale head_dim^-1/2 unless given; gates are
+ * elementwise over [token, head, channel] and act before the projections; RMSNorm is
+ * over head_dim with a per-(head, channel) float32 weight; no projection bias.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense, row-major, 16-byte aligned device pointers owned by the
+ *     caller.  The library allocates no tensor memory; scratch space comes from the
+ *     caller's workspace.  (The projection GEMM library handle is created once per
+ *     device on first use.)
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) of the current HIP device; no entry point except
+ *     vdn_hybrid_attn_membership synchronises.
+ *   - Every argument is checked on the host before anything is enqueued.  On error
+ *     nothing is launched, a status other than VDN_OK is returned, and
+ *     vdn_last_error() returns a message (thread-local, valid until the next call from
+ *     the same thread).  A failed launch returns VDN_ERR_HIP.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *
+ * Symbols: F frames, T tokens per frame, N = F*T video tokens (token n lies in frame
+ * n / T), H heads, d head_dim, L text tokens, D model_dim, C chunk_frames, R
+ * neighbor_chunks, nC = ceil(F / C) chunks.
+ */
+#ifndef VDN_HYBRID_ATTN_H
+#define VDN_HYBRID_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VDN_OK = 0,
+  VDN_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size */
+  VDN_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim, dtype combination, too many chunks */
+  VDN_ERR_WORKSPACE = 3,    /* workspace smaller than vdn_hybrid_attn_workspace_bytes() */
+  VDN_ERR_HIP = 4,          /* a HIP runtime or GEMM library call failed */
+  VDN_ERR_NO_DEVICE = 5     /* no HIP device is visible */
+} vdn_status;
+
+typedef enum { VDN_F32 = 0, VDN_BF16 = 1, VDN_FP8_E4M3 = 2 } vdn_dtype;
+
+typedef struct {
+  int32_t frames;           /* F >= 3 */
+  int32_t tokens_per_frame; /* T >= 1 */
+  int32_t heads;            /* H >= 1 */
+  int32_t head_dim;         /* d: 64 or 128 (bf16/fp8), 32, 64 or 128 (f32) */
+  int32_t text_len;         /* L >= 0 */
+  int32_t model_dim;        /* D >= 1: output width of each projection */
+  int32_t chunk_frames;     /* C >= 1 (the article's model: 5) */
+  int32_t neighbor_chunks;  /* R >= 1 (the article: 1) */
+  float softmax_scale;      /* 0 => head_dim^-1/2 */
+  float rms_eps;            /* > 0, e.g. 1e-6 */
+  int32_t qkv_dtype;        /* vdn_dtype of the softmax branch's q, k, v */
+  int32_t act_dtype;        /* vdn_dtype (F32 or BF16) of text_kv, gates, w_out,
+                               residual, out and the linear branch's q, k, v */
+  float q_scale, k_scale, v_scale; /* per-tensor dequantisation scales; FP8 only */
+  int32_t linear_variant;   /* 0 = additive state, identity feature map (the only one) */
+} vdn_hybrid_cfg;
+
+/* Byte offsets of the intermediate tensors inside the workspace.  They are exported so
+ * that tests can read the per-step results of one vdn_hybrid_attn_fwd call. */
+typedef struct {
+  size_t frame_states;  /* float32 [F, H, d, d]: k^T v summed over each frame's tokens;
+                           anchor frames hold zeros */
+  size_t text_state;    /* float32 [H, d, d]: k^T v summed over the text tokens */
+  size_t fwd_states;    /* float32 [nC, H, d, d]: text/2 + frames before chunk c's window */
+  size_t bwd_states;    /* float32 [nC, H, d, d]: text/2 + frames after chunk c's window */
+  size_t branch_out;    /* act_dtype [N, 2*H*d]: row n = gated softmax output of token n
+                           (heads concatenated) followed by its gated linear output */
+  size_t gemm_ws;       /* GEMM library scratch */
+  size_t gemm_ws_bytes;
+  size_t total;         /* == vdn_hybrid_attn_workspace_bytes() */
+} vdn_workspace_layout;
+
+/* Workspace size for `cfg`, or 0 if cfg is invalid (then vdn_last_error() says why). */
+size_t vdn_hybrid_attn_workspace_bytes(const vdn_hybrid_cfg* cfg);
+
+/* Fills *layout for `cfg`.  VDN_ERR_INVALID_ARG/UNSUPPORTED as for the forward call. */
+vdn_status vdn_hybrid_attn_workspace_layout(const vdn_hybrid_cfg* cfg,
+                                            vdn_workspace_layout* layout);
+
+/*
+ * One forward pass of the hybrid attention layer.
+ *
+ *   q, k, v      [N, H, d] qkv_dtype (FP8: e4m3fn codes, value = code * {q,k,v}_scale):
+ *                the softmax branch's inputs.  Also the linear branch's unless
+ *                qkv_lin is given.
+ *   text_kv      [2, L, H, d] act_dtype: text keys then text values.  May be NULL if L == 0.
+ *   gates        [2, N, H, d] act_dtype: sigmoid logits, [0] softmax branch, [1] linear branch.
+ *   rms_weight   [H, d] float32: RMSNorm weight of the linear branch.
+ *   w_out        [D, 2*H*d] act_dtype: row o = W_s[o, :] followed by W_l[o, :]
+ *                (nn.Linear [out, in] layouts of the two projections, concatenated along in).
+ *   residual     [N, D] act_dtype.
+ *   out          [N, D] act_dtype: residual + a_s W_s^T + a_l W_l^T.  May alias residual.
+ *   qkv_lin      NULL or [3, N, H, d] act_dtype: the linear branch's q, k, v (required when
+ *                qkv_dtype is FP8).
+ *   o_soft_dbg   NULL or [N, H, d] float32: the softmax branch output before its gate.
+ *   u_lin_dbg    NULL or [N, H, d] float32: the summed linear read before RMSNorm.
+ *   workspace    device memory of at least vdn_hybrid_attn_workspace_bytes(cfg) bytes.
+ *
+ * Steps, all enqueued on `stream`: per-frame and text state build; forward/backward
+ * state scan; linear read + RMSNorm + gate; block-sparse softmax + gate; one GEMM for both
+ * projections with the residual added.
+ */
+vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
+                               const void* text_kv, const void* gates,
+                               const float* rms_weight, const void* w_out,
+                               const void* residual, void* out,
+                               const vdn_hybrid_cfg* cfg, const void* qkv_lin,
+                               float* o_soft_dbg, float* u_lin_dbg,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Membership export: runs, on the current device, the same index functions the kernels
+ * use and writes codes_host[f * F + g] (host memory, F*F bytes) = how query frame f reads
+ * key frame g: 1 softmax, 2 forward state, 3 backward state, 0 not at all.
+ * Synchronises the device.
+ */
+vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_host);
+
+/* Per-step timing.  While enabled, vdn_hybrid_attn_fwd records HIP events on its stream
+ * around each step.  vdn_profile_read waits for the recorded events and writes the summed
+ * milliseconds of each step into ms[0..n_steps) (0 build, 1 scan, 2 linear read,
+ * 3 softmax, 4 projection) and the number of recorded calls into *calls; it also clears
+ * the record.  At most 4096 calls are recorded between reads (VDN_ERR_INVALID_ARG after). */
+#define VDN_PROFILE_STEPS 5
+vdn_status vdn_profile_enable(int on);
+vdn_status vdn_profile_read(double* ms, int n_steps, int64_t* calls);
+
+const char* vdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_HYBRID_ATTN_H */

@@ -1,0 +1,131 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function its
+header declares, and rejects bad arguments with the documented status before
+launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from video_diffusion_hybrid_sparse_amd import binding, shapes
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vdn_hybrid_attn.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, NO_DEVICE = range(6)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert header_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.lib()
+    for name in header_functions():
+        assert getattr(lib, name) is not None, name
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(binding.Cfg) == 16 * 4
+    assert ctypes.sizeof(binding.WorkspaceLayout) == 8 * ctypes.sizeof(ctypes.c_size_t)
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768], ids=lambda s: s.name)
+def test_workspace_layout(shape):
+    cfg = binding.make_cfg(shape)
+    L = binding.workspace_layout(cfg)
+    F, H, d, N = shape.frames, shape.heads, shape.head_dim, shape.tokens
+    st = H * d * d * 4
+    ab = 4 if shape.act_dtype == "f32" else 2
+    assert L.frame_states == 0
+    assert L.text_state == _align(F * st)
+    assert L.fwd_states == _align(L.text_state + st)
+    assert L.bwd_states == _align(L.fwd_states + shape.n_chunks * st)
+    assert L.branch_out == _align(L.bwd_states + shape.n_chunks * st)
+    assert L.gemm_ws == _align(L.branch_out + N * 2 * H * d * ab)
+    assert L.total == _align(L.gemm_ws + L.gemm_ws_bytes) == binding.workspace_bytes(cfg)
+
+
+BAD = [
+    (dict(frames=2), INVALID, "frames"),
+    (dict(tokens_per_frame=0), INVALID, "tokens_per_frame"),
+    (dict(heads=0), INVALID, "heads"),
+    (dict(text_len=-1), INVALID, "text_len"),
+    (dict(model_dim=0), INVALID, "model_dim"),
+    (dict(chunk_frames=0), INVALID, "chunk_frames"),
+    (dict(neighbor_chunks=0), INVALID, "neighbor_chunks"),
+    (dict(rms_eps=0.0), INVALID, "rms_eps"),
+    (dict(softmax_scale=-1.0), INVALID, "softmax_scale"),
+    (dict(linear_variant=1), UNSUPPORTED, "linear_variant"),
+    (dict(head_dim=96), UNSUPPORTED, "head_dim"),
+    (dict(head_dim=32), UNSUPPORTED, "head_dim"),  # bf16 path
+    (dict(act_dtype=binding.F32), UNSUPPORTED, "dtype"),
+    (dict(frames=5 * 33), UNSUPPORTED, "chunks"),
+]
+
+
+@pytest.mark.parametrize("change,status,word", BAD, ids=[b[2] + str(i) for i, b in enumerate(BAD)])
+def test_invalid_cfg_is_rejected(change, status, word):
+    cfg = binding.make_cfg(shapes.MID)
+    for k, v in change.items():
+        setattr(cfg, k, v)
+    assert binding.lib().vdn_hybrid_attn_workspace_bytes(ctypes.byref(cfg)) == 0
+    with pytest.raises(binding.VdnError) as e:
+        binding.workspace_layout(cfg)
+    assert e.value.status == status
+    assert word in binding.last_error()
+
+
+def _fwd(cfg, ptrs, ws_bytes):
+    return binding.lib().vdn_hybrid_attn_fwd(*ptrs[:9], ctypes.byref(cfg), *ptrs[9:], ws_bytes, None)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check: fake pointers must never reach a GPU")
+def test_fwd_argument_checks_launch_nothing():
+    cfg = binding.make_cfg(shapes.TOY)
+    need = binding.workspace_bytes(cfg)
+    good = [0x10000 * (i + 1) for i in range(9)] + [None, None, None, 0x100000]
+    assert _fwd(cfg, good, need) == NO_DEVICE  # every check passed; no device in this container
+    for i in range(9):
+        bad = list(good)
+        bad[i] = None
+        assert _fwd(cfg, bad, need) == INVALID, i
+        assert "NULL" in binding.last_error()
+        bad[i] = good[i] + 2
+        assert _fwd(cfg, bad, need) == INVALID, i
+        assert "aligned" in binding.last_error()
+    assert _fwd(cfg, good[:12] + [None], need) == INVALID  # workspace
+    assert _fwd(cfg, good, need - 1) == WORKSPACE
+    assert "smaller" in binding.last_error()
+    bad = list(good)
+    bad[3] = None  # text_kv with text_len > 0
+    assert _fwd(cfg, bad, need) == INVALID
+    cfg.text_len = 0
+    assert _fwd(cfg, bad, binding.workspace_bytes(cfg)) == NO_DEVICE
+    fp8 = binding.make_cfg(shapes.LONG)
+    assert _fwd(fp8, good, need) == UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check")
+def test_membership_needs_a_device():
+    cfg = binding.make_cfg(shapes.TOY)
+    with pytest.raises(binding.VdnError) as e:
+        binding.membership(cfg)
+    assert e.value.status == NO_DEVICE
+    assert binding.lib().vdn_hybrid_attn_membership(ctypes.byref(cfg), None) == INVALID
+
+
+def test_binding_checks_shapes_before_calling():
+    cfg = binding.make_cfg(shapes.TOY)
+    q = torch.zeros(3, 1, 32)
+    with pytest.raises(ValueError):
+        binding.hybrid_attn_fwd(q, q, q, None, None, None, None, None, None, cfg)

@@ -1,0 +1,158 @@
+"""GPU parity of the HIP layer against the CPU oracle, through the C ABI.
+
+Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16) are compared element
+by element on every output and intermediate state.  Tolerances: rel-L2 <= 1e-5 for the
+fp32 workloads and <= 1.5e-2 for bf16; index sets bit-exact everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [shapes.TOY, shapes.WORKED, shapes.MID]
+TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 1.5e-2}
+
+
+def rel_l2(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+def _np(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+_ORACLE = {}
+
+
+def oracle_for(shape):
+    if shape.name not in _ORACLE:
+        inp = synth.make_inputs(shape)
+        q, k, v = inp.qkv_values()
+        ql, kl, vl = inp.linear_qkv_values()
+        f = synth.f64
+        ref = oracle.layer.layer(q, k, v, f(inp.text_k), f(inp.text_v), f(inp.g_s), f(inp.g_l), f(inp.w_rms),
+                                 f(inp.w_s), f(inp.w_l), f(inp.x), shape.frames, shape.chunk_frames,
+                                 shape.neighbor_chunks, shape.rms_eps, q_lin=ql, k_lin=kl, v_lin=vl)
+        S = oracle.layer.frame_states(kl, vl, shape.frames)
+        Tx = oracle.layer.text_state(f(inp.text_k), f(inp.text_v))
+        fwd, bwd = oracle.layer.side_states(S, Tx, shape.frames, shape.chunk_frames, shape.neighbor_chunks)
+        ref.update(S=S, Tx=Tx, fwd=fwd, bwd=bwd)
+        _ORACLE[shape.name] = (inp, ref)
+    return _ORACLE[shape.name]
+
+
+@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768, shapes.LONG],
+                         ids=lambda s: s.name)
+def test_membership_export_bit_exact(shape):
+    cfg = binding.make_cfg(shape.with_(qkv_dtype="bf16") if shape.qkv_dtype == "fp8" else shape)
+    got = binding.membership(cfg)
+    want = oracle.sets.code_matrix(shape.frames, shape.chunk_frames, shape.neighbor_chunks)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
+def test_layer_parity(shape):
+    inp, ref = oracle_for(shape)
+    dl = runner.upload(inp, debug=True, sentinel=float("nan"))
+    dl.run()
+    torch.cuda.synchronize()
+    tol = TOL[shape.qkv_dtype]
+    hd = shape.hd
+    ws = dl.workspace_tensors()
+    x = synth.f64(inp.x)
+    got = dict(o_soft=_np(dl.o_soft_dbg), u=_np(dl.u_lin_dbg),
+               a_s=_np(ws["branch_out"][:, :hd]).reshape(ref["a_s"].shape),
+               a_l=_np(ws["branch_out"][:, hd:]).reshape(ref["a_l"].shape),
+               out=_np(dl.out))
+    got["y"] = got["out"] - x
+    ref = dict(ref, y=ref["out"] - x)
+    errs = {k: rel_l2(got[k], ref[k]) for k in ("o_soft", "u", "a_s", "a_l", "y", "out")}
+    print(shape.name, {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+    for k in ("o_soft", "u", "out"):
+        assert np.isfinite(got[k]).all(), k
+
+    # per-step states: frame states, text state, and each chunk's forward/backward state
+    F, C = shape.frames, shape.chunk_frames
+    S = _np(ws["frame_states"])
+    assert rel_l2(S, ref["S"]) <= tol
+    assert rel_l2(_np(ws["text_state"]), ref["Tx"]) <= tol
+    fw, bw = _np(ws["fwd_states"]), _np(ws["bwd_states"])
+    for c in range(shape.n_chunks):
+        frames = [f for f in range(c * C, min(F, (c + 1) * C)) if f not in (0, F - 1)]
+        if not frames:
+            continue
+        f = frames[0]
+        for got_s, want_s in ((fw[c], ref["fwd"][f]), (bw[c], ref["bwd"][f])):
+            if np.linalg.norm(want_s) == 0:
+                assert np.abs(got_s).max() == 0
+            else:
+                assert rel_l2(got_s, want_s) <= tol, c
+
+
+@pytest.mark.parametrize("shape", SMALL + [shapes.P768], ids=lambda s: s.name)
+def test_membership_probe_through_kernels(shape):
+    """Uniform softmax over one-hot frame values and a unit linear read: the outputs
+    show, bit for bit, which frames (and how many tokens of each) every query reads."""
+    inp = synth.membership_probe_inputs(shape)
+    dl = runner.upload(inp, debug=True)
+    dl.run()
+    torch.cuda.synchronize()
+    F, T, L = shape.frames, shape.tokens_per_frame, shape.text_len
+    rows = np.unique(np.concatenate([np.arange(0, shape.tokens, max(1, T // 3)), [shape.tokens - 1]]))
+    rows_t = torch.from_numpy(rows).cuda()
+    o = _np(dl.o_soft_dbg.index_select(0, rows_t))[:, :, : F + 1]
+    u = _np(dl.u_lin_dbg.index_select(0, rows_t))[:, :, : F + 1]
+    codes = oracle.sets.code_matrix(F, shape.chunk_frames, shape.neighbor_chunks)
+    for i, n in enumerate(rows):
+        f = n // T
+        soft = codes[f] == oracle.sets.SOFTMAX
+        lin = (codes[f] == oracle.sets.FORWARD) | (codes[f] == oracle.sets.BACKWARD)
+        nk = T * soft.sum() + L
+        want_o = np.zeros(F + 1)
+        want_o[:F][soft] = T / nk
+        want_o[F] = L / nk
+        want_u = np.zeros(F + 1)
+        want_u[:F][lin] = T
+        want_u[F] = L
+        for h in range(shape.heads):
+            assert ((o[i, h] != 0) == (want_o != 0)).all(), (n, h)
+            np.testing.assert_allclose(o[i, h], want_o, rtol=2e-6, atol=0)
+            np.testing.assert_array_equal(u[i, h], want_u)
+
+
+def test_determinism_and_aliasing():
+    shape = shapes.MID
+    inp, _ = oracle_for(shape)
+    dl = runner.upload(inp, debug=True)
+    dl.run()
+    dl.run()
+    torch.cuda.synchronize()
+    first = [t.clone() for t in (dl.out, dl.o_soft_dbg, dl.u_lin_dbg)]
+    dl.run()
+    torch.cuda.synchronize()
+    for a, b in zip(first, (dl.out, dl.o_soft_dbg, dl.u_lin_dbg)):
+        assert torch.equal(a, b)
+    alias = runner.upload(inp, out_aliases_residual=True)
+    alias.run()
+    torch.cuda.synchronize()
+    assert torch.equal(alias.out, first[0])
+
+
+def test_runs_on_a_side_stream():
+    shape = shapes.WORKED
+    inp, ref = oracle_for(shape)
+    dl = runner.upload(inp, debug=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dl.run(stream=s)
+    s.synchronize()
+    assert rel_l2(_np(dl.out), ref["out"]) <= TOL["f32"]

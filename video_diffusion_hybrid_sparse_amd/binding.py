@@ -1,0 +1,177 @@
+"""ctypes binding of libvdn_hybrid_attn.so: argument marshalling only.
+
+Every step of the layer runs inside the HIP library.  This module turns torch tensors
+into device pointers plus sizes, passes the current HIP stream, and raises VdnError
+with the library's message when a call fails.  It fails loudly when the library has not
+been built (run ``python -m video_diffusion_hybrid_sparse_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+from .shapes import LayerShape
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvdn_hybrid_attn.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+PROFILE_STEPS = ("state_build", "state_scan", "linear_read", "softmax", "projection")
+
+EXPORTS = ("vdn_hybrid_attn_workspace_bytes", "vdn_hybrid_attn_workspace_layout", "vdn_hybrid_attn_fwd",
+           "vdn_hybrid_attn_membership", "vdn_profile_enable", "vdn_profile_read", "vdn_last_error")
+
+
+class VdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"vdn status {status}: {message}")
+        self.status = status
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("text_len", ctypes.c_int32), ("model_dim", ctypes.c_int32),
+                ("chunk_frames", ctypes.c_int32), ("neighbor_chunks", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("qkv_dtype", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float), ("linear_variant", ctypes.c_int32)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("frame_states", "text_state", "fwd_states", "bwd_states",
+                                               "branch_out", "gemm_ws", "gemm_ws_bytes", "total")]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m video_diffusion_hybrid_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.vdn_hybrid_attn_workspace_bytes.argtypes = [ctypes.POINTER(Cfg)]
+        L.vdn_hybrid_attn_workspace_bytes.restype = sz
+        L.vdn_hybrid_attn_workspace_layout.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(WorkspaceLayout)]
+        L.vdn_hybrid_attn_workspace_layout.restype = i32
+        L.vdn_hybrid_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Cfg), vp, vp, vp, vp,
+                                          sz, vp]
+        L.vdn_hybrid_attn_fwd.restype = i32
+        L.vdn_hybrid_attn_membership.argtypes = [ctypes.POINTER(Cfg), vp]
+        L.vdn_hybrid_attn_membership.restype = i32
+        L.vdn_profile_enable.argtypes = [i32]
+        L.vdn_profile_enable.restype = i32
+        L.vdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(ctypes.c_int64)]
+        L.vdn_profile_read.restype = i32
+        L.vdn_last_error.argtypes = []
+        L.vdn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().vdn_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise VdnError(status, last_error())
+
+
+def make_cfg(shape: LayerShape, q_scale: float = 1.0, k_scale: float = 1.0, v_scale: float = 1.0,
+             softmax_scale: float = 0.0) -> Cfg:
+    return Cfg(shape.frames, shape.tokens_per_frame, shape.heads, shape.head_dim, shape.text_len, shape.dmodel,
+               shape.chunk_frames, shape.neighbor_chunks, softmax_scale, shape.rms_eps, _DT[shape.qkv_dtype],
+               _DT[shape.act_dtype], q_scale, k_scale, v_scale, 0)
+
+
+def workspace_bytes(cfg: Cfg) -> int:
+    n = lib().vdn_hybrid_attn_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise VdnError(-1, last_error())
+    return n
+
+
+def workspace_layout(cfg: Cfg) -> WorkspaceLayout:
+    out = WorkspaceLayout()
+    _check(lib().vdn_hybrid_attn_workspace_layout(ctypes.byref(cfg), ctypes.byref(out)))
+    return out
+
+
+def membership(cfg: Cfg) -> np.ndarray:
+    codes = np.zeros((cfg.frames, cfg.frames), np.int8)
+    _check(lib().vdn_hybrid_attn_membership(ctypes.byref(cfg), codes.ctypes.data_as(ctypes.c_void_p)))
+    return codes
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib().vdn_profile_enable(1 if on else 0))
+
+
+def profile_read() -> tuple[dict, int]:
+    ms = (ctypes.c_double * len(PROFILE_STEPS))()
+    calls = ctypes.c_int64(0)
+    _check(lib().vdn_profile_read(ms, len(PROFILE_STEPS), ctypes.byref(calls)))
+    return dict(zip(PROFILE_STEPS, list(ms))), int(calls.value)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape: tuple, dtypes: tuple) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+_TORCH = {F32: (torch.float32,), BF16: (torch.bfloat16,), FP8_E4M3: (torch.uint8, torch.float8_e4m3fn)}
+
+
+def hybrid_attn_fwd(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg: Cfg, qkv_lin=None,
+                    o_soft_dbg=None, u_lin_dbg=None, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue one layer forward on `stream` (default: torch's current stream).
+
+    Shapes (N = frames * tokens_per_frame): q/k/v [N,H,d]; text_kv [2,L,H,d]; gates
+    [2,N,H,d]; rms_weight [H,d] float32; w_out [D,2*H*d]; residual/out [N,D]; qkv_lin
+    [3,N,H,d] or None; o_soft_dbg/u_lin_dbg [N,H,d] float32 or None; workspace a uint8
+    device tensor of at least workspace_bytes(cfg) bytes (allocated here if None).
+    """
+    N, H, d, L, D = cfg.frames * cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.text_len, cfg.model_dim
+    qd, ad = _TORCH[cfg.qkv_dtype], _TORCH[cfg.act_dtype]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, n, (N, H, d), qd)
+    _expect(text_kv, "text_kv", (2, L, H, d), ad)
+    _expect(gates, "gates", (2, N, H, d), ad)
+    _expect(rms_weight, "rms_weight", (H, d), (torch.float32,))
+    _expect(w_out, "w_out", (D, 2 * H * d), ad)
+    _expect(residual, "residual", (N, D), ad)
+    _expect(out, "out", (N, D), ad)
+    _expect(qkv_lin, "qkv_lin", (3, N, H, d), ad)
+    _expect(o_soft_dbg, "o_soft_dbg", (N, H, d), (torch.float32,))
+    _expect(u_lin_dbg, "u_lin_dbg", (N, H, d), (torch.float32,))
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(lib().vdn_hybrid_attn_fwd(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None, _ptr(gates, "gates"),
+        _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(residual, "residual"), _ptr(out, "out"),
+        ctypes.byref(cfg), _ptr(qkv_lin, "qkv_lin"), _ptr(o_soft_dbg, "o_soft_dbg"), _ptr(u_lin_dbg, "u_lin_dbg"),
+        _ptr(workspace, "workspace"), workspace.numel(), handle))

@@ -1,0 +1,291 @@
+// C ABI of the hybrid attention library: argument checks, workspace layout, and the
+// launch sequence of one layer forward.  See include/vdn_hybrid_attn.h for the contract.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gemm.h"
+#include "kernels.h"
+#include "vdn_hybrid_attn.h"
+
+using namespace vdn;
+
+namespace {
+
+thread_local std::string g_err;
+
+vdn_status fail(vdn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+vdn_status fail(vdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+constexpr size_t kGemmWs = 64u << 20;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+vdn_status check_cfg(const vdn_hybrid_cfg* c) {
+  if (!c) return fail(VDN_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->frames < 3) return fail(VDN_ERR_INVALID_ARG, "frames must be >= 3 (got %d)", c->frames);
+  if (c->tokens_per_frame < 1) return fail(VDN_ERR_INVALID_ARG, "tokens_per_frame must be >= 1");
+  if (c->heads < 1) return fail(VDN_ERR_INVALID_ARG, "heads must be >= 1");
+  if (c->text_len < 0) return fail(VDN_ERR_INVALID_ARG, "text_len must be >= 0");
+  if (c->model_dim < 1) return fail(VDN_ERR_INVALID_ARG, "model_dim must be >= 1");
+  if (c->chunk_frames < 1) return fail(VDN_ERR_INVALID_ARG, "chunk_frames must be >= 1");
+  if (c->neighbor_chunks < 1) return fail(VDN_ERR_INVALID_ARG, "neighbor_chunks must be >= 1");
+  if (!(c->rms_eps > 0.0f) || !isfinite(c->rms_eps)) return fail(VDN_ERR_INVALID_ARG, "rms_eps must be > 0");
+  if (!(c->softmax_scale >= 0.0f) || !isfinite(c->softmax_scale))
+    return fail(VDN_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (c->linear_variant != 0) return fail(VDN_ERR_UNSUPPORTED, "linear_variant %d is not built", c->linear_variant);
+  const int qd = c->qkv_dtype, ad = c->act_dtype;
+  const bool f32 = qd == VDN_F32 && ad == VDN_F32;
+  const bool bf16 = qd == VDN_BF16 && ad == VDN_BF16;
+  if (!f32 && !bf16) {
+    if (qd == VDN_FP8_E4M3 && ad == VDN_BF16)
+      return fail(VDN_ERR_UNSUPPORTED, "fp8 e4m3 softmax inputs are not built yet");
+    return fail(VDN_ERR_UNSUPPORTED, "dtype combination qkv=%d act=%d is not supported", qd, ad);
+  }
+  const int d = c->head_dim;
+  if (bf16 && d != 64 && d != 128) return fail(VDN_ERR_UNSUPPORTED, "bf16 path needs head_dim 64 or 128 (got %d)", d);
+  if (f32 && d != 32 && d != 64 && d != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "f32 path needs head_dim 32, 64 or 128 (got %d)", d);
+  const int64_t nC = (c->frames + c->chunk_frames - 1) / c->chunk_frames;
+  if (nC > kMaxChunks) return fail(VDN_ERR_UNSUPPORTED, "%lld chunks exceed the scan limit of %d", (long long)nC, kMaxChunks);
+  const int64_t N = (int64_t)c->frames * c->tokens_per_frame;
+  const int64_t row = (int64_t)c->heads * d;
+  if (N * 2 * row >= (int64_t)1 << 31 || (int64_t)c->text_len * row >= (int64_t)1 << 31 ||
+      N * c->model_dim >= (int64_t)1 << 31 || (int64_t)c->model_dim * 2 * row >= (int64_t)1 << 31)
+    return fail(VDN_ERR_UNSUPPORTED, "tensor sizes exceed 2^31 elements");
+  return VDN_OK;
+}
+
+Geo make_geo(const vdn_hybrid_cfg* c) {
+  Geo g;
+  g.F = c->frames;
+  g.T = c->tokens_per_frame;
+  g.C = c->chunk_frames;
+  g.R = c->neighbor_chunks;
+  g.L = c->text_len;
+  g.H = c->heads;
+  g.d = c->head_dim;
+  g.nC = (c->frames + c->chunk_frames - 1) / c->chunk_frames;
+  return g;
+}
+
+size_t act_bytes(const vdn_hybrid_cfg* c) { return c->act_dtype == VDN_F32 ? 4 : 2; }
+
+void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
+  const size_t F = c->frames, H = c->heads, d = c->head_dim, N = (size_t)c->frames * c->tokens_per_frame;
+  const size_t nC = (c->frames + c->chunk_frames - 1) / c->chunk_frames;
+  const size_t st = H * d * d * 4;
+  size_t off = 0;
+  L->frame_states = off; off = align_up(off + F * st);
+  L->text_state = off; off = align_up(off + st);
+  L->fwd_states = off; off = align_up(off + nC * st);
+  L->bwd_states = off; off = align_up(off + nC * st);
+  L->branch_out = off; off = align_up(off + N * 2 * H * d * act_bytes(c));
+  L->gemm_ws = off; L->gemm_ws_bytes = kGemmWs; off = align_up(off + kGemmWs);
+  L->total = off;
+}
+
+// ---- profiling ----------------------------------------------------------------------
+constexpr int kProfSlots = 4096;
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // kProfSlots * (VDN_PROFILE_STEPS + 1)
+  int used = 0;
+  int device = -1;
+} g_prof;
+
+}  // namespace
+
+extern "C" {
+
+const char* vdn_last_error(void) { return g_err.c_str(); }
+
+size_t vdn_hybrid_attn_workspace_bytes(const vdn_hybrid_cfg* cfg) {
+  if (check_cfg(cfg) != VDN_OK) return 0;
+  vdn_workspace_layout L;
+  layout_of(cfg, &L);
+  return L.total;
+}
+
+vdn_status vdn_hybrid_attn_workspace_layout(const vdn_hybrid_cfg* cfg, vdn_workspace_layout* layout) {
+  vdn_status s = check_cfg(cfg);
+  if (s != VDN_OK) return s;
+  if (!layout) return fail(VDN_ERR_INVALID_ARG, "layout is NULL");
+  layout_of(cfg, layout);
+  return VDN_OK;
+}
+
+vdn_status vdn_profile_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (on && g_prof.ev.empty()) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+    g_prof.ev.resize((size_t)kProfSlots * (VDN_PROFILE_STEPS + 1));
+    for (auto& e : g_prof.ev)
+      if (hipEventCreate(&e) != hipSuccess) return fail(VDN_ERR_HIP, "hipEventCreate failed");
+    g_prof.device = dev;
+  }
+  g_prof.on = on != 0;
+  return VDN_OK;
+}
+
+vdn_status vdn_profile_read(double* ms, int n_steps, int64_t* calls) {
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!ms || n_steps < 0) return fail(VDN_ERR_INVALID_ARG, "ms is NULL or n_steps < 0");
+  for (int i = 0; i < n_steps; ++i) ms[i] = 0.0;
+  const int used = g_prof.used;
+  for (int s = 0; s < used; ++s) {
+    hipEvent_t* e = &g_prof.ev[(size_t)s * (VDN_PROFILE_STEPS + 1)];
+    if (hipEventSynchronize(e[VDN_PROFILE_STEPS]) != hipSuccess) return fail(VDN_ERR_HIP, "hipEventSynchronize failed");
+    for (int i = 0; i < VDN_PROFILE_STEPS && i < n_steps; ++i) {
+      float t = 0.0f;
+      if (hipEventElapsedTime(&t, e[i], e[i + 1]) != hipSuccess) return fail(VDN_ERR_HIP, "hipEventElapsedTime failed");
+      ms[i] += t;
+    }
+  }
+  if (calls) *calls = used;
+  g_prof.used = 0;
+  return VDN_OK;
+}
+
+vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_host) {
+  vdn_status s = check_cfg(cfg);
+  if (s != VDN_OK) return s;
+  if (!codes_host) return fail(VDN_ERR_INVALID_ARG, "codes_host is NULL");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+  const Geo g = make_geo(cfg);
+  const size_t bytes = (size_t)g.F * g.F;
+  int8_t* dev = nullptr;
+  if (hipMalloc(&dev, bytes) != hipSuccess) return fail(VDN_ERR_HIP, "hipMalloc of %zu bytes failed", bytes);
+  hipError_t e = launch_membership(g, dev, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(codes_host, dev, bytes, hipMemcpyDeviceToHost);
+  hipFree(dev);
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "membership kernel: %s", hipGetErrorString(e));
+  return VDN_OK;
+}
+
+vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_kv,
+                               const void* gates, const float* rms_weight, const void* w_out,
+                               const void* residual, void* out, const vdn_hybrid_cfg* cfg,
+                               const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg, void* workspace,
+                               size_t workspace_bytes, void* stream_ptr) {
+  vdn_status s = check_cfg(cfg);
+  if (s != VDN_OK) return s;
+  const struct { const void* p; const char* name; } req[] = {
+      {q, "q"}, {k, "k"}, {v, "v"}, {gates, "gates"}, {rms_weight, "rms_weight"}, {w_out, "w_out"},
+      {residual, "residual"}, {out, "out"}, {workspace, "workspace"}};
+  for (const auto& r : req) {
+    if (!r.p) return fail(VDN_ERR_INVALID_ARG, "%s is NULL", r.name);
+    if (!aligned16(r.p)) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", r.name);
+  }
+  if (cfg->text_len > 0 && !text_kv) return fail(VDN_ERR_INVALID_ARG, "text_kv is NULL but text_len > 0");
+  const void* opt[] = {text_kv, qkv_lin, o_soft_dbg, u_lin_dbg};
+  const char* optn[] = {"text_kv", "qkv_lin", "o_soft_dbg", "u_lin_dbg"};
+  for (int i = 0; i < 4; ++i)
+    if (opt[i] && !aligned16(opt[i])) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", optn[i]);
+  vdn_workspace_layout L;
+  layout_of(cfg, &L);
+  if (workspace_bytes < L.total)
+    return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, L.total);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  const Geo g = make_geo(cfg);
+  const size_t N = (size_t)g.F * g.T, row = (size_t)g.H * g.d, ab = act_bytes(cfg);
+  char* ws = static_cast<char*>(workspace);
+  float* S = reinterpret_cast<float*>(ws + L.frame_states);
+  float* St = reinterpret_cast<float*>(ws + L.text_state);
+  float* Sf = reinterpret_cast<float*>(ws + L.fwd_states);
+  float* Sb = reinterpret_cast<float*>(ws + L.bwd_states);
+  void* acat = ws + L.branch_out;
+  const char* tkv = static_cast<const char*>(text_kv);
+  const void* tk = tkv;
+  const void* tv = tkv ? tkv + (size_t)g.L * row * ab : nullptr;
+  const char* gb = static_cast<const char*>(gates);
+  const void* gs = gb;
+  const void* gl = gb + N * row * ab;
+  const char* lin = static_cast<const char*>(qkv_lin);
+  const void* ql = lin ? lin : q;
+  const void* kl = lin ? lin + N * row * ab : k;
+  const void* vl = lin ? lin + 2 * N * row * ab : v;
+  if (!tk) tk = tv = q;  // L == 0: never dereferenced
+  const bool bf16 = cfg->qkv_dtype == VDN_BF16;
+  const float scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / sqrtf((float)g.d);
+
+  // profiling slot
+  hipEvent_t* ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    if (g_prof.on) {
+      if (g_prof.used >= kProfSlots) return fail(VDN_ERR_INVALID_ARG, "profile record is full; call vdn_profile_read");
+      ev = &g_prof.ev[(size_t)g_prof.used * (VDN_PROFILE_STEPS + 1)];
+      g_prof.used++;
+    }
+  }
+  auto mark = [&](int i) { if (ev) hipEventRecord(ev[i], stream); };
+
+  hipError_t e = hipSuccess;
+  mark(0);
+  if (bf16) {
+    BuildArgs<__bf16> ba{(const __bf16*)kl, (const __bf16*)vl, (const __bf16*)tk, (const __bf16*)tv, S, St, g};
+    e = launch_build_bf16(ba, stream);
+  } else {
+    BuildArgs<float> ba{(const float*)kl, (const float*)vl, (const float*)tk, (const float*)tv, S, St, g};
+    e = launch_build_f32(ba, stream);
+  }
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "state build launch: %s", hipGetErrorString(e));
+  mark(1);
+  ScanArgs sa{S, St, Sf, Sb, g, (int64_t)(g.H * (size_t)g.d * g.d / 4)};
+  e = launch_scan(sa, stream);
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  mark(2);
+  if (bf16) {
+    ReadoutArgs<__bf16> ra{(const __bf16*)ql, Sf, Sb, St, (const __bf16*)gl, rms_weight, (__bf16*)acat, u_lin_dbg, g,
+                           cfg->rms_eps};
+    e = launch_readout_bf16(ra, stream);
+  } else {
+    ReadoutArgs<float> ra{(const float*)ql, Sf, Sb, St, (const float*)gl, rms_weight, (float*)acat, u_lin_dbg, g,
+                          cfg->rms_eps};
+    e = launch_readout_f32(ra, stream);
+  }
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "linear read launch: %s", hipGetErrorString(e));
+  mark(3);
+  if (bf16) {
+    SoftmaxArgs sm{(const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv,
+                   (const __bf16*)gs, (__bf16*)acat, o_soft_dbg, g, scale * 1.4426950408889634f};
+    e = launch_softmax_bf16(sm, stream);
+  } else {
+    SoftmaxF32Args sm{(const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,
+                      (const float*)gs, (float*)acat, o_soft_dbg, g, scale};
+    e = launch_softmax_f32(sm, stream);
+  }
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "softmax launch: %s", hipGetErrorString(e));
+  mark(4);
+  const char* gerr = nullptr;
+  if (projection_gemm(bf16, (int64_t)N, cfg->model_dim, (int64_t)(2 * row), acat, w_out, residual, out,
+                      ws + L.gemm_ws, L.gemm_ws_bytes, stream, &gerr) != 0)
+    return fail(VDN_ERR_HIP, "projection: %s", gerr);
+  mark(5);
+  return VDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Linear branch, bf16 inputs, gfx950 MFMA: per-frame state build and the state read
+// with RMSNorm and the elementwise gate.
+//
+// The linear branch keeps, per frame, the state k^T v summed over the frame's tokens
+// (frame-wise updates; identity feature map, additive state).  A query reads the forward
+// state (text/2 + frames before its window) and the backward state (text/2 + frames
+// after it) and adds the two reads (VDN-MiniMax-H3 article, modelscope.csdn.net,
+// section "局部精确计算，远程线性记忆", paragraphs 1-3).  The read is RMS-normalised over
+// head_dim, then gated elementwise by a sigmoid (section "独立门控，融合两条注意力分支").
+#include "kernels.h"
+
+namespace vdn {
+
+// ---- state build: S = K^T V over the tokens of one frame (or the text), one head ------
+//
+// One workgroup per (frame or text, head).  Tokens are walked 32 at a time; K and V are
+// transposed into LDS as [channel][token] so that both MFMA operands (contraction over
+// tokens) read 16 contiguous bytes per lane.  Wave w owns a (D/2 x D/2) quadrant of the
+// d x d state.
+template <int D>
+__global__ __launch_bounds__(256) void build_bf16_kernel(BuildArgs<__bf16> a) {
+  constexpr int TB = 32, PAD = TB + 8, TPW = D / 64, NPO = TB / 2 * D / 8;
+  __shared__ __attribute__((aligned(16))) __bf16 Kt[2][D * PAD];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * PAD];
+  const Geo g = a.geo;
+  const int fr = blockIdx.x, h = blockIdx.y;
+  const size_t rs = (size_t)g.H * D;
+  float* out = fr < g.F ? a.S + ((size_t)fr * g.H + h) * D * D : a.Stext + (size_t)h * D * D;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int r0 = (wave >> 1) * 32 * TPW, c0 = (wave & 1) * 32 * TPW;
+
+  const __bf16 *kb, *vb;
+  int ntok;
+  if (fr < g.F) {
+    kb = a.k + (size_t)fr * g.T * rs + h * D;
+    vb = a.v + (size_t)fr * g.T * rs + h * D;
+    ntok = is_anchor(g, fr) ? 0 : g.T;  // anchors are in neither linear state
+  } else {
+    kb = a.tk + h * D;
+    vb = a.tv + h * D;
+    ntok = g.L;
+  }
+
+  f32x16 acc[TPW][TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) acc[i][j] = 0.0f;
+
+  const int nsteps = (ntok + TB - 1) / TB;
+  // loader unit: tokens (2p, 2p+1) x 8 channels; p = tid % 16, channel octet = tid / 16
+  const int pr = tid & 15, oc = tid >> 4;
+  uint4 kr[2], vr[2];
+  auto load = [&](int step) {
+    if (tid < NPO) {
+      // rows past the end are loaded clamped, then replaced by zeros (selects on values)
+      const int t = step * TB + 2 * pr, col = oc * 8;
+      const size_t o0 = (size_t)imin(t, ntok - 1) * rs + col, o1 = (size_t)imin(t + 1, ntok - 1) * rs + col;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 k0 = *reinterpret_cast<const uint4*>(kb + o0), v0 = *reinterpret_cast<const uint4*>(vb + o0);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(kb + o1), v1 = *reinterpret_cast<const uint4*>(vb + o1);
+      kr[0] = t < ntok ? k0 : z;
+      vr[0] = t < ntok ? v0 : z;
+      kr[1] = t + 1 < ntok ? k1 : z;
+      vr[1] = t + 1 < ntok ? v1 : z;
+    }
+  };
+  auto store = [&](int buf) {
+    if (tid < NPO) {
+      const int col = oc * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k0 = u4_at(kr[0], e), k1 = u4_at(kr[1], e), v0 = u4_at(vr[0], e), v1 = u4_at(vr[1], e);
+        uint32_t* kt = reinterpret_cast<uint32_t*>(&Kt[buf][(col + 2 * e) * PAD + 2 * pr]);
+        uint32_t* vt = reinterpret_cast<uint32_t*>(&Vt[buf][(col + 2 * e) * PAD + 2 * pr]);
+        kt[0] = (k0 & 0xffffu) | (k1 << 16);
+        kt[PAD / 2] = (k0 >> 16) | (k1 & 0xffff0000u);
+        vt[0] = (v0 & 0xffffu) | (v1 << 16);
+        vt[PAD / 2] = (v0 >> 16) | (v1 & 0xffff0000u);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) load(st + 1);
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ++ks) {
+      bf16x8 av[TPW], bv[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        av[i] = *reinterpret_cast<const bf16x8*>(&Kt[buf][(r0 + 32 * i + l32) * PAD + 16 * ks + 8 * half]);
+        bv[i] = *reinterpret_cast<const bf16x8*>(&Vt[buf][(c0 + 32 * i + l32) * PAD + 16 * ks + 8 * half]);
+      }
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+    }
+    if (st + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator: row r0 + 32 i + 8 (r/4) + 4 half + r%4, column c0 + 32 j + l32
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        out[row * D + c0 + 32 * j + l32] = acc[i][j][r];
+      }
+}
+
+hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
+  dim3 grid(a.geo.F + 1, a.geo.H), block(256);
+  if (a.geo.d == 128)
+    hipLaunchKernelGGL(build_bf16_kernel<128>, grid, block, 0, stream, a);
+  else if (a.geo.d == 64)
+    hipLaunchKernelGGL(build_bf16_kernel<64>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---- state read: u = q.S_fwd + q.S_bwd, RMSNorm, gate --------------------------------
+//
+// One workgroup = 128 query tokens of one query group and one head.  The group's two
+// states are summed in float32 (the identity feature map makes q.S_fwd + q.S_bwd equal
+// to q.(S_fwd + S_bwd); only rounding differs), split into bf16 hi + lo parts and
+// stored transposed in LDS, so u^T = S^T q^T runs as two bf16 MFMA passes with float32
+// accumulation (about 16 mantissa bits of the state kept).  Lanes own one token each.
+template <int D>
+__global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
+  constexpr int BM = 128, PAD = D + 8, KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 Shi[D * PAD];
+  __shared__ __attribute__((aligned(16))) __bf16 Slo[D * PAD];
+  const Geo g = a.geo;
+  const int h = blockIdx.y;
+  int grp, t0, t1;
+  if (!locate_tile(g, blockIdx.x, BM, grp, t0, t1)) return;
+  const int chunk = group_chunk(grp);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const size_t rs = (size_t)g.H * D;
+  const size_t hs = (size_t)h * D * D;
+
+  // S_sum^T into LDS: unit = rows (i, i+1) x columns j..j+3
+  {
+    const float* ta = a.Stext + hs;
+    const float* fa = chunk >= 0 ? a.Sfwd + (size_t)chunk * g.H * D * D + hs : ta;
+    const float* ba = chunk >= 0 ? a.Sbwd + (size_t)chunk * g.H * D * D + hs : ta;
+    const float wf = chunk >= 0 ? 1.0f : 0.5f;  // anchor rows: text/2 + text/2
+    for (int u = tid; u < D * D / 8; u += 256) {
+      const int i = 2 * (u / (D / 4)), j = 4 * (u % (D / 4));
+      const float4 f0 = *reinterpret_cast<const float4*>(fa + i * D + j);
+      const float4 f1 = *reinterpret_cast<const float4*>(fa + (i + 1) * D + j);
+      const float4 b0 = *reinterpret_cast<const float4*>(ba + i * D + j);
+      const float4 b1 = *reinterpret_cast<const float4*>(ba + (i + 1) * D + j);
+      const float s0[4] = {wf * f0.x + wf * b0.x, wf * f0.y + wf * b0.y, wf * f0.z + wf * b0.z, wf * f0.w + wf * b0.w};
+      const float s1[4] = {wf * f1.x + wf * b1.x, wf * f1.y + wf * b1.y, wf * f1.z + wf * b1.z, wf * f1.w + wf * b1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 h0 = (__bf16)s0[e], h1 = (__bf16)s1[e];
+        const float l0 = s0[e] - (float)h0, l1 = s1[e] - (float)h1;
+        bf16x2 hv = {h0, h1};
+        *reinterpret_cast<uint32_t*>(&Shi[(j + e) * PAD + i]) = __builtin_bit_cast(uint32_t, hv);
+        *reinterpret_cast<uint32_t*>(&Slo[(j + e) * PAD + i]) = pack_bf16x2(l0, l1);
+      }
+    }
+  }
+  __syncthreads();
+
+  int tok = t0 + wave * 32 + l32;
+  const bool ok = tok < t1;
+  tok = ok ? tok : t1 - 1;
+  bf16x8 qreg[KS];
+  const size_t qrow = (size_t)tok * rs + h * D;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+
+  f32x16 u[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    u[dt] = 0.0f;
+    const __bf16* hp = &Shi[(32 * dt + l32) * PAD + 8 * half];
+    const __bf16* lp = &Slo[(32 * dt + l32) * PAD + 8 * half];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u[dt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(lp + 16 * ks), qreg[ks], u[dt]);
+      u[dt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(hp + 16 * ks), qreg[ks], u[dt]);
+    }
+  }
+  // lane holds channels 32 dt + 8 i + 4 half + e of token `tok`
+  float ss = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ss += u[dt][r] * u[dt][r];
+  ss += __shfl_xor(ss, 32);
+  const float rinv = rsqrtf(ss / D + a.eps);
+  if (!ok) return;
+  __bf16* arow = a.acat + (size_t)tok * 2 * rs + rs + h * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * dt + 8 * i + 4 * half;
+      const float4 w4 = *reinterpret_cast<const float4*>(a.w + h * D + d0);
+      const uint2 graw = *reinterpret_cast<const uint2*>(a.gl + qrow + d0);
+      const float gv[4] = {bf16_to_f32(graw.x & 0xffff), bf16_to_f32(graw.x >> 16),
+                           bf16_to_f32(graw.y & 0xffff), bf16_to_f32(graw.y >> 16)};
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = sigmoid(gv[e]) * (u[dt][4 * i + e] * rinv * wv[e]);
+      uint2 ov;
+      ov.x = pack_bf16x2(r[0], r[1]);
+      ov.y = pack_bf16x2(r[2], r[3]);
+      *reinterpret_cast<uint2*>(arow + d0) = ov;
+      if (a.u_dbg)
+        *reinterpret_cast<float4*>(a.u_dbg + qrow + d0) =
+            make_float4(u[dt][4 * i], u[dt][4 * i + 1], u[dt][4 * i + 2], u[dt][4 * i + 3]);
+    }
+}
+
+hipError_t launch_readout_bf16(const ReadoutArgs<__bf16>& a, hipStream_t stream) {
+  const int tiles = count_tiles(a.geo, 128);
+  if (tiles == 0) return hipSuccess;
+  dim3 grid(tiles, a.geo.H), block(256);
+  if (a.geo.d == 128)
+    hipLaunchKernelGGL(readout_bf16_kernel<128>, grid, block, 0, stream, a);
+  else if (a.geo.d == 64)
+    hipLaunchKernelGGL(readout_bf16_kernel<64>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace vdn

@@ -1,0 +1,87 @@
+// Forward/backward state scan over frames (float32, HBM-bound).
+//
+// For query chunk c the forward state is text/2 plus the states of the non-anchor
+// frames before its window; the backward state is text/2 plus those after it
+// (VDN-MiniMax-H3 article, modelscope.csdn.net, section "局部精确计算，远程线性记忆",
+// paragraphs 1-3: window and anchor frames are left out, text is written into each
+// state at half weight).  Windows start and end on chunk boundaries, so one pass over
+// the per-frame states forms per-chunk sums (anchor frames skipped) in registers; an
+// exclusive prefix and an exclusive suffix over the chunk sums then give every chunk's
+// two states, read at the window edges through fwd_prefix_chunk / bwd_prefix_chunk.
+// No subtraction is involved, so the states carry only summation rounding.
+//
+// Each thread owns one float4 of the flattened [H, d, d] state and walks the frames in
+// order: every step is a fully coalesced 16-byte load per lane across the grid.
+#include "kernels.h"
+
+namespace vdn {
+
+template <int MAXC>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  const Geo g = a.geo;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= a.n4) return;
+  const float4* S = reinterpret_cast<const float4*>(a.S);
+  float4* Sf = reinterpret_cast<float4*>(a.Sfwd);
+  float4* Sb = reinterpret_cast<float4*>(a.Sbwd);
+  const float4 t = reinterpret_cast<const float4*>(a.Stext)[e];
+  const float4 half = make_float4(0.5f * t.x, 0.5f * t.y, 0.5f * t.z, 0.5f * t.w);
+  const int64_t n4 = a.n4;
+
+  float4 cs[MAXC];
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    cs[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j < g.nC) {
+      const int f0 = j * g.C, f1 = imin(g.F, f0 + g.C);
+      for (int f = f0; f < f1; ++f) {
+        if (is_anchor(g, f)) continue;
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(&S[f * n4 + e]));
+        cs[j].x += x[0]; cs[j].y += x[1]; cs[j].z += x[2]; cs[j].w += x[3];
+      }
+    }
+  }
+
+  // forward: chunks whose window starts at frame <= C - 1 read text/2 alone
+  for (int c = 0; c < g.nC; ++c)
+    if (fwd_prefix_chunk(g, c) < 0) Sf[c * n4 + e] = half;
+  float4 pre = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    if (j < g.nC) {
+      pre.x += cs[j].x; pre.y += cs[j].y; pre.z += cs[j].z; pre.w += cs[j].w;
+      for (int c = 0; c < g.nC; ++c)
+        if (fwd_prefix_chunk(g, c) == j)
+          Sf[c * n4 + e] = make_float4(half.x + pre.x, half.y + pre.y, half.z + pre.z, half.w + pre.w);
+    }
+  }
+  // backward: suffix over the chunks after the one holding the window's last frame
+  float4 suf = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = MAXC - 1; j >= 0; --j) {
+    if (j < g.nC) {
+      for (int c = 0; c < g.nC; ++c)
+        if (bwd_prefix_chunk(g, c) == j)
+          Sb[c * n4 + e] = make_float4(half.x + suf.x, half.y + suf.y, half.z + suf.z, half.w + suf.w);
+      suf.x += cs[j].x; suf.y += cs[j].y; suf.z += cs[j].z; suf.w += cs[j].w;
+    }
+  }
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
+  const int nC = a.geo.nC;
+  dim3 grid((unsigned)((a.n4 + 255) / 256)), block(256);
+  if (nC <= 4)
+    hipLaunchKernelGGL(scan_kernel<4>, grid, block, 0, stream, a);
+  else if (nC <= 8)
+    hipLaunchKernelGGL(scan_kernel<8>, grid, block, 0, stream, a);
+  else if (nC <= 16)
+    hipLaunchKernelGGL(scan_kernel<16>, grid, block, 0, stream, a);
+  else if (nC <= kMaxChunks)
+    hipLaunchKernelGGL(scan_kernel<kMaxChunks>, grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace vdn

@@ -1,0 +1,61 @@
+"""Algorithmic work of one layer forward: FLOPs and bytes per step, for rooflines.
+
+Counts what the method must do, not what a kernel happens to do:
+* softmax branch: 4 d FLOPs per (query, key) pair of the sparse key sets (q.k and p.v),
+  per head; exp/max are not counted;
+* state build: 2 T d^2 per non-anchor frame and head, plus 2 L d^2 per head for text;
+* linear read: 2 d^2 per query token and head (one read of the summed state);
+* projections: 2 N (2 H d) D.
+Key-set sizes follow the layer's geometry (chunk windows clipped at the clip ends, two
+anchor frames that read everything, all text tokens), counted here independently.
+"""
+from __future__ import annotations
+
+from .shapes import LayerShape
+
+
+def keys_per_frame(s: LayerShape) -> list[int]:
+    """Number of softmax keys of a query in each frame."""
+    F, C, R, T, L = s.frames, s.chunk_frames, s.neighbor_chunks, s.tokens_per_frame, s.text_len
+    n_chunks = s.n_chunks
+    out = []
+    for f in range(F):
+        if f == 0 or f == F - 1:
+            out.append(F * T + L)
+            continue
+        c = f // C
+        lo = max(0, c - R) * C
+        hi = min(F - 1, (min(n_chunks - 1, c + R) + 1) * C - 1)
+        frames = hi - lo + 1 + (1 if lo > 0 else 0) + (1 if hi < F - 1 else 0)
+        out.append(frames * T + L)
+    return out
+
+
+def pairs_per_head(s: LayerShape) -> int:
+    return sum(k * s.tokens_per_frame for k in keys_per_frame(s))
+
+
+def flops(s: LayerShape) -> dict:
+    H, d, T, L, N, D, F = s.heads, s.head_dim, s.tokens_per_frame, s.text_len, s.tokens, s.dmodel, s.frames
+    f = dict(softmax=4 * d * H * pairs_per_head(s),
+             state_build=2 * d * d * H * (T * (F - 2) + L),
+             state_scan=0,
+             linear_read=2 * d * d * H * N,
+             projection=2 * N * 2 * H * d * D)
+    f["total"] = sum(f.values())
+    return f
+
+
+def bytes_moved(s: LayerShape) -> dict:
+    """Algorithmic HBM bytes per step (each input read once, each output written once)."""
+    H, d, T, L, N, D, F, nC = s.heads, s.head_dim, s.tokens_per_frame, s.text_len, s.tokens, s.dmodel, s.frames, s.n_chunks
+    a = 4 if s.act_dtype == "f32" else 2
+    qb = {"f32": 4, "bf16": 2, "fp8": 1}[s.qkv_dtype]
+    st = H * d * d * 4
+    return dict(
+        state_build=2 * ((F - 2) * T + L) * H * d * a + (F + 1) * st,
+        state_scan=(F - 2) * st + st + 2 * nC * st,
+        linear_read=3 * N * H * d * a + 2 * nC * st + st,
+        softmax=3 * N * H * d * qb + 2 * L * H * d * a + 2 * N * H * d * a,
+        projection=(N * 2 * H * d + D * 2 * H * d + 2 * N * D) * a,
+    )
