@@ -5,42 +5,71 @@
 // cover (VDN-MiniMax-H3 article, modelscope.csdn.net, section "局部精确计算，远程线性记忆",
 // paragraphs 1 and 3), multiplies it by the sigmoid of the softmax gate logits (section
 // "独立门控，融合两条注意力分支") and stores it as bf16 into the first half of the branch
-// output row.  The mask is never materialised: each query group's keys are at most
-// three contiguous video token ranges after the text, and a tile's rows are gathered
-// through seg_token().
+// output row.  The mask is never materialised: a query group's keys are the text tokens
+// and at most three contiguous video token ranges (group_keys), walked one segment at a
+// time in tiles of 64 contiguous keys; only a segment's last tile is partial and masked.
 //
 // Work split: one workgroup = 4 waves = 128 query tokens of one query group and one
-// head; each wave owns 32 queries.  Keys are walked in tiles of 64, double-buffered in
-// LDS.  The wave computes S^T = K Q^T (keys x queries) so a lane holds the scores of
-// one query: the softmax max/sum need one lane swap per tile and the O rescale is
-// lane-local.  P^T then feeds O^T += V^T P^T straight from the accumulator registers;
-// V^T is stored in LDS with keys permuted inside every 16-key group so that the MFMA's
-// k-slot order matches the accumulator layout and each lane reads 16 contiguous bytes.
+// head (two workgroups per CU); each wave owns 32 queries.  Key and value tiles go from
+// HBM straight into LDS (global_load_lds, 16 bytes per lane), double-buffered, rows
+// stored with an XOR swizzle of their 16-byte chunks that makes both LDS read patterns
+// below conflict-free.
+//   S^T = K Q^T (keys x queries): K is the MFMA A operand (row = key, 16-byte LDS reads);
+//     Q^T stays in registers.  A lane holds the scores of one query, so the softmax
+//     statistics need one lane swap per tile and the O rescale is lane-local.
+//   O^T += V^T P^T: P^T comes straight from the S^T accumulators (converted to bf16);
+//     the V^T operand is gathered from row-major V with the transposing LDS read
+//     (ds_read_b64_tr_b16), in the key order the accumulator layout implies.
+// Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and the
+// running max only moves when a tile exceeds it by more than 8, so the O rescale is
+// rare; any fixed reference point gives the same softmax.
 #include "kernels.h"
 
 namespace vdn {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row, per row (see header).
 template <int D>
-__global__ __launch_bounds__(256) void softmax_bf16_kernel(SoftmaxArgs a) {
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return ((row & 2) << 1) | ((row >> 2) & 3);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+  return __builtin_bit_cast(
+      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p)));
+}
+
+__device__ __forceinline__ void load_lds16(const __bf16* g, __bf16* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bf16_kernel(SoftmaxArgs a) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KS = D / 16;   // MFMA k-steps over head_dim
-  constexpr int DT = D / 32;   // 32-row tiles of O^T
-  constexpr int KPAD = D + 8;  // K row stride in LDS (bf16)
-  constexpr int VPAD = BN + 8; // V^T row stride in LDS (bf16)
-  constexpr int KCH = BN * D / 8 / 256;      // 16-byte K chunks per thread per tile
-  constexpr int VPO = BN / 2 * D / 8 / 256;  // (key pair, 8 channels) units per thread
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KPAD];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VPAD];
+  constexpr int KS = D / 16;           // MFMA k-steps over head_dim
+  constexpr int DT = D / 32;           // 32-row tiles of O^T
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;        // rows one wave-wide 16-byte load covers
+  constexpr int NI = BN * CPR / 256;   // loads per thread per tile (per tensor)
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * D];
 
   const Geo g = a.geo;
   const int h = blockIdx.y;
   int grp, t0, t1;
   if (!locate_tile(g, blockIdx.x, BM, grp, t0, t1)) return;
-  const KeySegs segs = group_keys(g, grp);
-  const int nkeys = g.L + segs.total;
-  const int ntiles = (nkeys + BN - 1) / BN;
+  const KeySegs ks_ = group_keys(g, grp);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)g.H * D;  // row stride of [*, H, D] tensors
+
+  // Segments in walk order: 0 = text, 1..3 = video ranges (zero-length ones skipped).
+  auto seg_len = [&](int s) { return s == 0 ? g.L : s == 1 ? ks_.l0 : s == 2 ? ks_.l1 : ks_.l2; };
+  auto seg_start = [&](int s) { return s == 1 ? ks_.s0 : s == 2 ? ks_.s1 : ks_.s2; };
+  int ntiles = 0;
+  for (int s = 0; s < 4; ++s) ntiles += (seg_len(s) + BN - 1) / BN;
 
   int qtok = t0 + wave * 32 + l32;
   const bool qok = qtok < t1;
@@ -52,46 +81,32 @@ __global__ __launch_bounds__(256) void softmax_bf16_kernel(SoftmaxArgs a) {
     for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(qp + 16 * s);
   }
 
-  // Global -> register -> LDS staging of one key tile.  K rows are copied as 16-byte
-  // chunks; V is transposed to [channel][key] two keys at a time.  Rows past the end of
-  // the key list are clamped to the last key (finite values; their scores are masked).
-  uint4 kreg[KCH], vreg[VPO][2];
-#define VDN_LOAD_TILE(J)                                                                      \
-  {                                                                                           \
-    const int base_ = (J) * BN;                                                               \
-    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                         \
-      const int c = tid + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;                \
-      const int vk = imin(base_ + row, nkeys - 1);                                            \
-      const __bf16* p = vk < g.L ? a.tk + (size_t)vk * rs : a.k + (size_t)seg_token(segs, vk - g.L) * rs; \
-      kreg[i] = *reinterpret_cast<const uint4*>(p + h * D + col);                             \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < VPO; ++i) {                                         \
-      const int c = tid + 256 * i, pair = c / (D / 8), col = (c % (D / 8)) * 8;               \
-      _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                         \
-        const int vk = imin(base_ + 2 * pair + u, nkeys - 1);                                 \
-        const __bf16* p = vk < g.L ? a.tv + (size_t)vk * rs : a.v + (size_t)seg_token(segs, vk - g.L) * rs; \
-        vreg[i][u] = *reinterpret_cast<const uint4*>(p + h * D + col);                        \
-      }                                                                                       \
-    }                                                                                         \
+  // Per-lane constants of the tile loads: row inside the tile and swizzled source column.
+  int lrow[NI], lcol[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    lrow[i] = (wave * NI + i) * RPI + lane / CPR;
+    lcol[i] = ((lane % CPR) ^ swz<D>(lrow[i])) * 8;
   }
-#define VDN_STORE_TILE(BUF)                                                                   \
-  {                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                         \
-      const int c = tid + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;                \
-      *reinterpret_cast<uint4*>(&Ks[BUF][row * KPAD + col]) = kreg[i];                        \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < VPO; ++i) {                                         \
-      const int c = tid + 256 * i, pair = c / (D / 8), col = (c % (D / 8)) * 8;               \
-      const int key = 2 * pair, k16 = key & 15;                                               \
-      /* swap bits 2 and 3 of the key inside its 16-key group (see header comment) */        \
-      const int pos = (key & ~15) | (k16 & 3) | ((k16 & 4) << 1) | ((k16 & 8) >> 1);         \
-      _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                         \
-        const uint32_t a0 = u4_at(vreg[i][0], e), a1 = u4_at(vreg[i][1], e);                 \
-        *reinterpret_cast<uint32_t*>(&Vt[BUF][(col + 2 * e) * VPAD + pos]) = (a0 & 0xffffu) | (a1 << 16); \
-        *reinterpret_cast<uint32_t*>(&Vt[BUF][(col + 2 * e + 1) * VPAD + pos]) = (a0 >> 16) | (a1 & 0xffff0000u); \
-      }                                                                                       \
-    }                                                                                         \
-  }
+  // Issue the loads of the tile at (segment s, key offset off) into LDS buffer buf.
+  auto issue = [&](int s, int off, int buf) {
+    const int len = seg_len(s);
+    const __bf16* kb = (s == 0 ? a.tk : a.k + (size_t)seg_start(s) * rs) + h * D;
+    const __bf16* vb = (s == 0 ? a.tv : a.v + (size_t)seg_start(s) * rs) + h * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = imin(off + lrow[i], len - 1);  // rows past the segment: masked later
+      const size_t o = (size_t)row * rs + lcol[i];
+      load_lds16(kb + o, &Ks[buf][(wave * NI + i) * RPI * D]);
+      load_lds16(vb + o, &Vs[buf][(wave * NI + i) * RPI * D]);
+    }
+  };
+
+  int cs = 0, coff = 0;  // segment and key offset of the current tile
+  while (seg_len(cs) == 0) ++cs;  // the walk always has a non-empty segment
+  issue(cs, coff, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   f32x16 o[DT];
 #pragma unroll
@@ -99,68 +114,96 @@ __global__ __launch_bounds__(256) void softmax_bf16_kernel(SoftmaxArgs a) {
   float m = -INFINITY, l = 0.0f;
   const float c2 = a.scale_log2;
 
-  VDN_LOAD_TILE(0);
-  VDN_STORE_TILE(0);
-  __syncthreads();
+  // LDS read offsets (elements), the same for every tile
+  int krd[2][KS];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int row = rt * 32 + l32;
+      krd[rt][k] = row * D + (((2 * k + half) ^ swz<D>(row)) * 8);
+    }
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int vrd[DT][4][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int G = 0; G < 4; ++G)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        // source lane i16 of group grp16 points at key row K0 + i16/4, channels d..d+3;
+        // the transposing read hands lane j of the group channel d0 + j of keys K0..K0+3
+        const int row = 16 * G + 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
+        const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+        vrd[dt][G][c] = row * D + (((d >> 3) ^ swz<D>(row)) * 8) + (d & 7);
+      }
+
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
-    // the last iteration reloads its own tile into the idle buffer: no branch around the
-    // loads, and nothing reads that buffer afterwards
-    VDN_LOAD_TILE(imin(j + 1, ntiles - 1));
+    const int tlen = seg_len(cs) - coff;  // valid keys in this tile (>= BN when full)
+    int ns = cs, noff = coff + BN;
+    while (ns < 4 && noff >= seg_len(ns)) { ++ns; noff = 0; }
+    if (j + 1 < ntiles) issue(ns, noff, buf ^ 1);
 
+    const __bf16* K = Ks[buf];
+    const __bf16* V = Vs[buf];
     f32x16 s[2];
+    s[0] = 0.0f;
+    s[1] = 0.0f;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      s[rt] = 0.0f;
-      const __bf16* kp = &Ks[buf][(rt * 32 + l32) * KPAD + half * 8];
+    for (int k = 0; k < KS; ++k)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kp + 16 * ks), qreg[ks], s[rt]);
-    }
-    const int kbase = j * BN;
-    if (kbase + BN > nkeys) {
+      for (int rt = 0; rt < 2; ++rt)
+        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + krd[rt][k]), qreg[k], s[rt]);
+    if (tlen < BN) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kbase + rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nkeys) s[rt][r] = -INFINITY;
+          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= tlen) s[rt][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    if (__any(mx > m + 8.0f)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
 
-    bf16x8 pb[2][2];
+    bf16x8 pb[4];
     float psum = 0.0f;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[rt][r] * c2 - mnew);
+        const float p = __builtin_amdgcn_exp2f(s[rt][r] * c2 - m);
         psum += p;
-        pb[rt][r >> 3][r & 7] = (__bf16)p;
+        pb[2 * rt + (r >> 3)][r & 7] = (__bf16)p;
       }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    l += psum;
 
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const __bf16* vp = &Vt[buf][(dt * 32 + l32) * VPAD + half * 8];
+    for (int G = 0; G < 4; ++G)
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        o[dt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vp + 16 * st), pb[st >> 1][st & 1], o[dt]);
-    }
-    VDN_STORE_TILE(buf ^ 1);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x4 lo = lds_read_tr(V + vrd[dt][G][0]);
+        const bf16x4 hi = lds_read_tr(V + vrd[dt][G][1]);
+        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dt] = mfma32x32x16(va, pb[G], o[dt]);
+      }
+
+    cs = ns;
+    coff = noff;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-#undef VDN_LOAD_TILE
-#undef VDN_STORE_TILE
 
   l += __shfl_xor(l, 32);
   const float inv = 1.0f / l;
