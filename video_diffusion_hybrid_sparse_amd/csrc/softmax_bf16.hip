@@ -7,27 +7,52 @@
 // "独立门控，融合两条注意力分支") and stores it as bf16 into the first half of the branch
 // output row.  The mask is never materialised: a query group's keys are the text tokens
 // and at most three contiguous video token ranges (group_keys), walked one segment at a
-// time in tiles of 64 contiguous keys; only a segment's last tile is partial and masked.
+// time in stages of 128 contiguous keys; only a segment's last stage is partial and
+// masked.
 //
-// Work split: one workgroup = 4 waves = 128 query tokens of one query group and one
-// head (two workgroups per CU); each wave owns 32 queries.  Key and value tiles go from
-// HBM straight into LDS (global_load_lds, 16 bytes per lane), double-buffered, rows
-// stored with an XOR swizzle of their 16-byte chunks that makes both LDS read patterns
-// below conflict-free.
-//   S^T = K Q^T (keys x queries): K is the MFMA A operand (row = key, 16-byte LDS reads);
-//     Q^T stays in registers.  A lane holds the scores of one query, so the softmax
-//     statistics need one lane swap per tile and the O rescale is lane-local.
-//   O^T += V^T P^T: P^T comes straight from the S^T accumulators (converted to bf16);
-//     the V^T operand is gathered from row-major V with the transposing LDS read
-//     (ds_read_b64_tr_b16), in the key order the accumulator layout implies.
-// Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and the
-// running max only moves when a tile exceeds it by more than 8, so the O rescale is
-// rare; any fixed reference point gives the same softmax.
+// Work split: one workgroup = 8 waves (two per SIMD) = 256 query tokens of one query
+// group and one head; each wave owns 32 queries.  Workgroups are numbered so that each
+// XCD runs a contiguous range of (head, group, query tile): tiles that read the same keys
+// share one L2.  Key and value stages go from HBM straight into LDS (global_load_lds, 16
+// bytes per lane), double-buffered, one barrier per 128-key stage; rows are stored with
+// an XOR swizzle of their 16-byte chunks that makes both LDS read patterns below
+// conflict-free.  Each stage is computed as two 64-key sub-tiles:
+//   S^T = K Q^T (keys x queries): K is the MFMA A operand (16-byte LDS reads); Q^T stays
+//     in registers.  A lane holds the scores of one query, so the softmax statistics need
+//     one VALU lane swap (v_permlane32_swap) per sub-tile and the O rescale is lane-local.
+//   O^T += V^T P^T: P^T comes straight from the S^T accumulators (bf16); the V^T operand is
+//     gathered from row-major V with the transposing LDS read (ds_read_b64_tr_b16) in the
+//     key order the accumulator layout implies.
+// Scores stay in the log2 domain (scale * log2 e folded into one FMA); the running max
+// only moves when a sub-tile exceeds it by more than 8, so the O rescale is rare.  Any
+// fixed reference point gives the same softmax; the row sum is taken over the same bf16
+// probabilities that multiply V.
 #include "kernels.h"
 
 namespace vdn {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Value of the lane pair (l, l ^ 32): v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, so with both holding x they end up
+// holding x and the partner's x.  The compiler does not look inside the asm, so the asm
+// carries the wait states a VALU write before, and a read after, the swap need.
+__device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_swap(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_swap(x, a, b);
+  return a + b;
+}
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row, per row (see header).
 template <int D>
@@ -46,30 +71,56 @@ __device__ __forceinline__ void load_lds16(const __bf16* g, __bf16* lds_wave_bas
                                    (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
 
+// Key stages of a query group: ceil(len / BN) stages per segment, segments in the order
+// text, video range 0, 1, 2.  stage_at gives a stage's first key (token index in the text
+// or video tensor) and its number of valid keys.
+template <int BN>
+struct KeyWalk {
+  int L, s0, l0, s1, l1, s2, l2;
+  int n0, n1, n2, n3;
+  __device__ KeyWalk(int text_len, const KeySegs& sg)
+      : L(text_len), s0(sg.s0), l0(sg.l0), s1(sg.s1), l1(sg.l1), s2(sg.s2), l2(sg.l2),
+        n0((text_len + BN - 1) / BN), n1((sg.l0 + BN - 1) / BN), n2((sg.l1 + BN - 1) / BN),
+        n3((sg.l2 + BN - 1) / BN) {}
+  __device__ int stages() const { return n0 + n1 + n2 + n3; }
+  __device__ void stage_at(int j, bool& text, int& start, int& valid) const {
+    int len, base;
+    if (j < n0) { text = true; base = 0; len = L; }
+    else if ((j -= n0) < n1) { text = false; base = s0; len = l0; }
+    else if ((j -= n1) < n2) { text = false; base = s1; len = l1; }
+    else { j -= n2; text = false; base = s2; len = l2; }
+    start = base + BN * j;
+    valid = len - BN * j;
+  }
+};
+
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bf16_kernel(SoftmaxArgs a) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int KS = D / 16;           // MFMA k-steps over head_dim
-  constexpr int DT = D / 32;           // 32-row tiles of O^T
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;        // rows one wave-wide 16-byte load covers
-  constexpr int NI = BN * CPR / 256;   // loads per thread per tile (per tensor)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bf16_kernel(SoftmaxArgs a) {
+  constexpr int BM = 256, NW = 8;
+  constexpr int BN = 128, BC = 64;           // keys per stage, keys per compute sub-tile
+  constexpr int KS = D / 16;                 // MFMA k-steps over head_dim
+  constexpr int DT = D / 32;                 // 32-row tiles of O^T
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;              // rows one wave-wide 16-byte load covers
+  constexpr int NI = BN * CPR / (64 * NW);   // loads per lane per stage (per tensor)
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * D];
 
   const Geo g = a.geo;
-  const int h = blockIdx.y;
+  // XCD-aware order: hardware block ids go round-robin over the 8 XCDs; XCD x gets the
+  // contiguous logical range starting at x * (total / 8) + min(x, total % 8).
+  const int per_head = count_tiles(g, BM);
+  const int total = per_head * g.H;
+  const int hid = blockIdx.x, xcd = hid & 7;
+  const int lid = xcd * (total >> 3) + imin(xcd, total & 7) + (hid >> 3);
+  const int h = lid / per_head;
   int grp, t0, t1;
-  if (!locate_tile(g, blockIdx.x, BM, grp, t0, t1)) return;
-  const KeySegs ks_ = group_keys(g, grp);
+  if (!locate_tile(g, lid - h * per_head, BM, grp, t0, t1)) return;
+  const KeyWalk<BN> kw(g.L, group_keys(g, grp));
+  const int nst = kw.stages();
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)g.H * D;  // row stride of [*, H, D] tensors
-
-  // Segments in walk order: 0 = text, 1..3 = video ranges (zero-length ones skipped).
-  auto seg_len = [&](int s) { return s == 0 ? g.L : s == 1 ? ks_.l0 : s == 2 ? ks_.l1 : ks_.l2; };
-  auto seg_start = [&](int s) { return s == 1 ? ks_.s0 : s == 2 ? ks_.s1 : ks_.s2; };
-  int ntiles = 0;
-  for (int s = 0; s < 4; ++s) ntiles += (seg_len(s) + BN - 1) / BN;
 
   int qtok = t0 + wave * 32 + l32;
   const bool qok = qtok < t1;
@@ -81,131 +132,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(qp + 16 * s);
   }
 
-  // Per-lane constants of the tile loads: row inside the tile and swizzled source column.
+  // Per-lane constants of the stage loads: row inside the stage and swizzled column.
   int lrow[NI], lcol[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    lcol[i] = ((lane % CPR) ^ swz<D>(lrow[i])) * 8;
+    lcol[i] = ((lane % CPR) ^ swz<D>(lrow[i])) * 8 + h * D;
   }
-  // Issue the loads of the tile at (segment s, key offset off) into LDS buffer buf.
-  auto issue = [&](int s, int off, int buf) {
-    const int len = seg_len(s);
-    const __bf16* kb = (s == 0 ? a.tk : a.k + (size_t)seg_start(s) * rs) + h * D;
-    const __bf16* vb = (s == 0 ? a.tv : a.v + (size_t)seg_start(s) * rs) + h * D;
+  auto issue = [&](int j, int buf) {
+    bool text;
+    int start, valid;
+    kw.stage_at(j, text, start, valid);
+    const __bf16* kb = text ? a.tk : a.k;
+    const __bf16* vb = text ? a.tv : a.v;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = imin(off + lrow[i], len - 1);  // rows past the segment: masked later
+      const int row = start + imin(lrow[i], valid - 1);  // rows past the segment: masked later
       const size_t o = (size_t)row * rs + lcol[i];
       load_lds16(kb + o, &Ks[buf][(wave * NI + i) * RPI * D]);
       load_lds16(vb + o, &Vs[buf][(wave * NI + i) * RPI * D]);
     }
   };
 
-  int cs = 0, coff = 0;  // segment and key offset of the current tile
-  while (seg_len(cs) == 0) ++cs;  // the walk always has a non-empty segment
-  issue(cs, coff, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // LDS read offsets (elements), the same for every sub-tile (the swizzle depends on the
+  // low 4 bits of the row only, so sub-tile and row-tile offsets are plain additions)
+  int krd[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<D>(l32)) * 8);
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int vrd[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // source lane i16 of group grp16 points at key row K0 + i16/4, channels d..d+3;
+      // the transposing read hands lane j of the group channel d0 + j of keys K0..K0+3
+      const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
+      const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      vrd[dt][c] = row * D + (((d >> 3) ^ swz<D>(row)) * 8) + (d & 7);
+    }
 
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = 0.0f;
   float m = -INFINITY, l = 0.0f;
   const float c2 = a.scale_log2;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // LDS read offsets (elements), the same for every tile
-  int krd[2][KS];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const int row = rt * 32 + l32;
-      krd[rt][k] = row * D + (((2 * k + half) ^ swz<D>(row)) * 8);
-    }
-  const int grp16 = lane >> 4, i16 = lane & 15;
-  int vrd[DT][4][2];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int G = 0; G < 4; ++G)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        // source lane i16 of group grp16 points at key row K0 + i16/4, channels d..d+3;
-        // the transposing read hands lane j of the group channel d0 + j of keys K0..K0+3
-        const int row = 16 * G + 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
-        const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
-        vrd[dt][G][c] = row * D + (((d >> 3) ^ swz<D>(row)) * 8) + (d & 7);
-      }
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
+  for (int j = 0; j < nst; ++j) {
     const int buf = j & 1;
-    const int tlen = seg_len(cs) - coff;  // valid keys in this tile (>= BN when full)
-    int ns = cs, noff = coff + BN;
-    while (ns < 4 && noff >= seg_len(ns)) { ++ns; noff = 0; }
-    if (j + 1 < ntiles) issue(ns, noff, buf ^ 1);
+    bool text;
+    int start, svalid;
+    kw.stage_at(j, text, start, svalid);
+    if (j + 1 < nst) issue(j + 1, buf ^ 1);
 
-    const __bf16* K = Ks[buf];
-    const __bf16* V = Vs[buf];
-    f32x16 s[2];
-    s[0] = 0.0f;
-    s[1] = 0.0f;
+    for (int sub = 0; sub < BN / BC; ++sub) {
+      const int valid = svalid - sub * BC;  // valid keys of this sub-tile (>= BC when full)
+      if (valid <= 0) break;
+      const __bf16* K = Ks[buf] + sub * BC * D;
+      const __bf16* V = Vs[buf] + sub * BC * D;
+
+      f32x16 s[2];
+      s[0] = 0.0f;
+      s[1] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[k]), qreg[k], s[rt]);
+      if (valid < BC) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= valid) s[rt][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
-        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + krd[rt][k]), qreg[k], s[rt]);
-    if (tlen < BN) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rt][r]);
+      mx = pair_max(mx) * c2;
+      if (__any(mx > m + 8.0f)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      }
+
+      bf16x8 pb[4];
+      float psum = 0.0f;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= tlen) s[rt][r] = -INFINITY;
+        for (int r = 0; r < 16; r += 2) {
+          const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(s[rt][r] * c2 - m),
+                                          __builtin_amdgcn_exp2f(s[rt][r + 1] * c2 - m));
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one2, psum, false);
+          uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
+          const int e = (r & 7) >> 1;
+          if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
+          pb[2 * rt + (r >> 3)] = __builtin_bit_cast(bf16x8, w);
+        }
+      l += psum;
+
+#pragma unroll
+      for (int G = 0; G < 4; ++G)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x4 lo = lds_read_tr(V + 16 * G * D + vrd[dt][0]);
+          const bf16x4 hi = lds_read_tr(V + 16 * G * D + vrd[dt][1]);
+          const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[dt] = mfma32x32x16(va, pb[G], o[dt]);
+        }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    if (__any(mx > m + 8.0f)) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-
-    bf16x8 pb[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[rt][r] * c2 - m);
-        psum += p;
-        pb[2 * rt + (r >> 3)][r & 7] = (__bf16)p;
-      }
-    l += psum;
-
-#pragma unroll
-    for (int G = 0; G < 4; ++G)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 lo = lds_read_tr(V + vrd[dt][G][0]);
-        const bf16x4 hi = lds_read_tr(V + vrd[dt][G][1]);
-        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[dt] = mfma32x32x16(va, pb[G], o[dt]);
-      }
-
-    cs = ns;
-    coff = noff;
+    // the next stage has landed in every wave, and every wave is done with this one
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  l += __shfl_xor(l, 32);
+  l = pair_sum(l);
   const float inv = 1.0f / l;
   if (!qok) return;
   const size_t orow = (size_t)qtok * rs + h * D;
@@ -230,9 +282,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 }
 
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream) {
-  const int tiles = count_tiles(a.geo, 128);
+  const int tiles = count_tiles(a.geo, 256);
   if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles, a.geo.H), block(256);
+  dim3 grid(tiles * a.geo.H), block(512);
   if (a.geo.d == 128)
     hipLaunchKernelGGL(softmax_bf16_kernel<128>, grid, block, 0, stream, a);
   else if (a.geo.d == 64)
