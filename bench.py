@@ -22,6 +22,23 @@ import time
 METRIC = "hybrid-attn layer ms + TFLOP/s (% MFMA peak) at 768p 60-frame shape, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
+# scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
+# the kernel source it was measured on.
+PMC_TRAFFIC = {"source_sha256_16": "d9eaf8eabe30b91c", "bytes": 12.860e9}
+SOFTMAX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/softmax_bf16.hip",
+                   "video_diffusion_hybrid_sparse_amd/csrc/common.h",
+                   "video_diffusion_hybrid_sparse_amd/csrc/kernels.h")
+
+
+def softmax_traffic():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in SOFTMAX_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return PMC_TRAFFIC["bytes"] if h.hexdigest()[:16] == PMC_TRAFFIC["source_sha256_16"] else None
 
 
 def log(*a):
@@ -37,9 +54,9 @@ def cpu_baseline(shape, inp, budget_s: float = 20.0) -> dict:
     from video_diffusion_hybrid_sparse_amd import synth
 
     F, T, C, R, H, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.neighbor_chunks, shape.heads, shape.head_dim
-    frames = [0, 1, F // 2, F - 2]
+    frames = [0, 1, 5, 10, F // 2, F - 5, F - 2]
     rows = np.concatenate([np.arange(f * T, (f + 1) * T) for f in frames])
-    heads = list(range(2))
+    heads = list(range(24))
     cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
 
     def sub(t):
@@ -133,7 +150,7 @@ def main() -> int:
         "pct_mfma_peak": round(100 * fl["total"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"kernel": "softmax_bf16_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": softmax_traffic()},
         "steps_ms": {k: round(v, 4) for k, v in per.items()},
         "steps_rate": {
             "softmax_tflops": round(achieved, 1),

@@ -168,3 +168,51 @@ def test_runs_on_a_side_stream():
         dl.run(stream=s)
     s.synchronize()
     assert rel_l2(_np(dl.out), ref["out"]) <= TOL["f32"]
+
+
+def test_768p_sampled_parity():
+    """The 768p layer in the bench's launch configuration, checked against the oracle on
+    sampled query tokens: o_soft and u on 8 heads for tokens of 13 frames (anchors, chunk
+    edges, interior), y = out - x on 6 tokens with all 48 heads (the projection mixes
+    heads)."""
+    shape = shapes.P768
+    F, T, C = shape.frames, shape.tokens_per_frame, shape.chunk_frames
+    inp = synth.make_inputs(shape)
+    dl = runner.upload(inp, debug=True)
+    dl.run()
+    torch.cuda.synchronize()
+    print("768p: layer ran", flush=True)
+    frames = [0, 1, 4, 5, 9, 10, 30, 49, 50, 54, 55, 58, 59]
+    rows = np.array([f * T + t for f in frames for t in (0, T // 2, T - 1)])
+    heads = [0, 7, 15, 23, 24, 31, 40, 47]
+    rows_t = torch.from_numpy(rows).cuda()
+    o_gpu = _np(dl.o_soft_dbg.index_select(0, rows_t))[:, heads]
+    u_gpu = _np(dl.u_lin_dbg.index_select(0, rows_t))[:, heads]
+
+    def sub(t):
+        return np.ascontiguousarray(synth.f64(t)[:, heads])
+
+    q, k, v, tk, tv = (sub(t) for t in (inp.q, inp.k, inp.v, inp.text_k, inp.text_v))
+    o_ref = oracle.layer.softmax_branch(q, k, v, tk, tv, F, C, rows=rows)
+    print("768p: oracle softmax rows done", flush=True)
+    u_ref = oracle.layer.linear_branch(q, k, v, tk, tv, F, C, rows=rows)
+    del q, k, v
+    e_o, e_u = rel_l2(o_gpu, o_ref), rel_l2(u_gpu, u_ref)
+    print(f"768p sampled rel-L2: o_soft {e_o:.2e} u {e_u:.2e}", flush=True)
+    assert e_o <= TOL["bf16"] and e_u <= TOL["bf16"]
+
+    # y on all heads for a few tokens
+    yrows = np.array([0 * T + 3, 5 * T + 100, 5 * T + 900, 30 * T + 500, 59 * T + 7, 57 * T + 1000])
+    f = synth.f64
+    qa, ka, va = f(inp.q), f(inp.k), f(inp.v)
+    o_all = oracle.layer.softmax_branch(qa, ka, va, f(inp.text_k), f(inp.text_v), F, C, rows=yrows)
+    u_all = oracle.layer.linear_branch(qa, ka, va, f(inp.text_k), f(inp.text_v), F, C, rows=yrows)
+    del qa, ka, va
+    a_s = oracle.layer.sigmoid(f(inp.g_s)[yrows]) * o_all
+    a_l = oracle.layer.sigmoid(f(inp.g_l)[yrows]) * oracle.layer.rms_norm(u_all, f(inp.w_rms), shape.rms_eps)
+    x = f(inp.x)[yrows]
+    y_ref = oracle.layer.project(a_s, a_l, f(inp.w_s), f(inp.w_l), x) - x
+    y_gpu = _np(dl.out.index_select(0, torch.from_numpy(yrows).cuda())) - x
+    e_y = rel_l2(y_gpu, y_ref)
+    print(f"768p sampled rel-L2: y {e_y:.2e}", flush=True)
+    assert e_y <= TOL["bf16"]
