@@ -65,7 +65,7 @@ typedef struct {
   int32_t frames;           /* F >= 3 */
   int32_t tokens_per_frame; /* T >= 1 */
   int32_t heads;            /* H >= 1 */
-  int32_t head_dim;         /* d: 64 or 128 (bf16/fp8), 32, 64 or 128 (f32) */
+  int32_t head_dim;         /* d: 64 or 128 (bf16), 128 (fp8), 32, 64 or 128 (f32) */
   int32_t text_len;         /* L >= 0 */
   int32_t model_dim;        /* D >= 1: output width of each projection */
   int32_t chunk_frames;     /* C >= 1 (the article's model: 5) */
@@ -75,7 +75,7 @@ typedef struct {
   int32_t qkv_dtype;        /* vdn_dtype of the softmax branch's q, k, v */
   int32_t act_dtype;        /* vdn_dtype (F32 or BF16) of text_kv, gates, w_out,
                                residual, out and the linear branch's q, k, v */
-  float q_scale, k_scale, v_scale; /* per-tensor dequantisation scales; FP8 only */
+  float q_scale, k_scale, v_scale; /* per-tensor dequantisation scales (> 0); FP8 only */
   int32_t linear_variant;   /* 0 = additive state, identity feature map (the only one) */
 } vdn_hybrid_cfg;
 
@@ -89,6 +89,8 @@ typedef struct {
   size_t bwd_states;    /* float32 [nC, H, d, d]: text/2 + frames after chunk c's window */
   size_t branch_out;    /* act_dtype [N, 2*H*d]: row n = gated softmax output of token n
                            (heads concatenated) followed by its gated linear output */
+  size_t value_stage;   /* FP8 only, bf16 [N + L, H, d]: the value codes converted to bf16,
+                           then text values divided by v_scale (no bytes otherwise) */
   size_t gemm_ws;       /* GEMM library scratch */
   size_t gemm_ws_bytes;
   size_t total;         /* == vdn_hybrid_attn_workspace_bytes() */
@@ -116,6 +118,10 @@ vdn_status vdn_hybrid_attn_workspace_layout(const vdn_hybrid_cfg* cfg,
  *   out          [N, D] act_dtype: residual + a_s W_s^T + a_l W_l^T.  May alias residual.
  *   qkv_lin      NULL or [3, N, H, d] act_dtype: the linear branch's q, k, v (required when
  *                qkv_dtype is FP8).
+ *   Supported (qkv_dtype, act_dtype): (F32, F32), (BF16, BF16), (FP8_E4M3, BF16).  With
+ *   FP8 the softmax scores use the e4m3 codes of q and k (video keys) or q's codes and the
+ *   bf16 text keys, times the scales; softmax probabilities multiply the value codes in
+ *   bf16 and the output is scaled by v_scale.
  *   o_soft_dbg   NULL or [N, H, d] float32: the softmax branch output before its gate.
  *   u_lin_dbg    NULL or [N, H, d] float32: the summed linear read before RMSNorm.
  *   workspace    device memory of at least vdn_hybrid_attn_workspace_bytes(cfg) bytes.

@@ -32,14 +32,14 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(binding.Cfg) == 16 * 4
-    assert ctypes.sizeof(binding.WorkspaceLayout) == 8 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(binding.WorkspaceLayout) == 9 * ctypes.sizeof(ctypes.c_size_t)
 
 
 def _align(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768, shapes.LONG], ids=lambda s: s.name)
 def test_workspace_layout(shape):
     cfg = binding.make_cfg(shape)
     L = binding.workspace_layout(cfg)
@@ -51,7 +51,9 @@ def test_workspace_layout(shape):
     assert L.fwd_states == _align(L.text_state + st)
     assert L.bwd_states == _align(L.fwd_states + shape.n_chunks * st)
     assert L.branch_out == _align(L.bwd_states + shape.n_chunks * st)
-    assert L.gemm_ws == _align(L.branch_out + N * 2 * H * d * ab)
+    assert L.value_stage == _align(L.branch_out + N * 2 * H * d * ab)
+    stage = (N + shape.text_len) * H * d * 2 if shape.qkv_dtype == "fp8" else 0
+    assert L.gemm_ws == _align(L.value_stage + stage)
     assert L.total == _align(L.gemm_ws + L.gemm_ws_bytes) == binding.workspace_bytes(cfg)
 
 
@@ -112,7 +114,16 @@ def test_fwd_argument_checks_launch_nothing():
     cfg.text_len = 0
     assert _fwd(cfg, bad, binding.workspace_bytes(cfg)) == NO_DEVICE
     fp8 = binding.make_cfg(shapes.LONG)
-    assert _fwd(fp8, good, need) == UNSUPPORTED
+    need8 = binding.workspace_bytes(fp8)
+    assert _fwd(fp8, good, need8) == INVALID  # fp8 needs qkv_lin
+    assert "qkv_lin" in binding.last_error()
+    lin = good[:9] + [0x200000] + good[10:]  # qkv_lin
+    assert _fwd(fp8, lin, need8) == NO_DEVICE
+    fp8.k_scale = 0.0
+    assert _fwd(fp8, lin, need8) == INVALID
+    fp8 = binding.make_cfg(shapes.LONG)
+    fp8.head_dim = 64
+    assert _fwd(fp8, lin, need8) == UNSUPPORTED
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check")

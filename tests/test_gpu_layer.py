@@ -1,8 +1,9 @@
 """GPU parity of the HIP layer against the CPU oracle, through the C ABI.
 
-Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16, and ragged bf16 cases
-at both head dims, one without text) are compared element by element on every output
-and intermediate state.  Tolerances: rel-L2 <= 1e-5 for the
+Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16, ragged bf16 cases at
+both head dims, one without text, and a ragged fp8 case) are compared element by element
+on every output and intermediate state; the 768p and 120-frame fp8 layers are compared
+on sampled tokens.  Tolerances: rel-L2 <= 1e-5 for the
 fp32 workloads and <= 1.5e-2 for bf16; index sets bit-exact everywhere.
 """
 import numpy as np
@@ -22,7 +23,11 @@ RAGGED64 = shapes.LayerShape("ragged_f10_t37_c2_h2_d64_bf16", frames=10, tokens_
                              head_dim=64, text_len=5, chunk_frames=2, model_dim=96, seed=2002)
 NOTEXT = shapes.LayerShape("notext_f7_t70_c1_h1_d128_bf16", frames=7, tokens_per_frame=70, heads=1,
                            head_dim=128, text_len=0, chunk_frames=1, model_dim=64, seed=2003)
-SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT]
+# fp8 (e4m3) softmax inputs with bf16 linear-branch copies, ragged sizes
+FP8_SMALL = shapes.LayerShape("fp8_f12_t100_c3_h3_d128", frames=12, tokens_per_frame=100, heads=3, head_dim=128,
+                              text_len=40, chunk_frames=3, model_dim=200, qkv_dtype="fp8", act_dtype="bf16",
+                              seed=2004)
+SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8_SMALL]
 TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 1.5e-2}
 
 
@@ -59,7 +64,7 @@ def oracle_for(shape):
 @pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768, shapes.LONG],
                          ids=lambda s: s.name)
 def test_membership_export_bit_exact(shape):
-    cfg = binding.make_cfg(shape.with_(qkv_dtype="bf16") if shape.qkv_dtype == "fp8" else shape)
+    cfg = binding.make_cfg(shape)
     got = binding.membership(cfg)
     want = oracle.sets.code_matrix(shape.frames, shape.chunk_frames, shape.neighbor_chunks)
     np.testing.assert_array_equal(got, want)
@@ -109,7 +114,7 @@ def test_layer_parity(shape):
                 assert rel_l2(got_s, want_s) <= tol, c
 
 
-@pytest.mark.parametrize("shape", SMALL + [shapes.P768], ids=lambda s: s.name)
+@pytest.mark.parametrize("shape", SMALL + [shapes.P768, shapes.LONG], ids=lambda s: s.name)
 def test_membership_probe_through_kernels(shape):
     """Uniform softmax over one-hot frame values and a unit linear read: the outputs
     show, bit for bit, which frames (and how many tokens of each) every query reads."""
@@ -216,3 +221,31 @@ def test_768p_sampled_parity():
     e_y = rel_l2(y_gpu, y_ref)
     print(f"768p sampled rel-L2: y {e_y:.2e}", flush=True)
     assert e_y <= TOL["bf16"]
+
+
+def test_long_fp8_sampled_parity():
+    """The 120-frame layer with e4m3 softmax inputs (bf16 linear branch), checked on
+    sampled tokens against the oracle fed the dequantised values."""
+    shape = shapes.LONG
+    F, T, C = shape.frames, shape.tokens_per_frame, shape.chunk_frames
+    inp = synth.make_inputs(shape)
+    dl = runner.upload(inp, debug=True)
+    dl.run()
+    torch.cuda.synchronize()
+    print("long fp8: layer ran", flush=True)
+    frames = [0, 1, 4, 5, 30, 60, 114, 115, 118, 119]
+    rows = np.array([f * T + t for f in frames for t in (0, T // 2, T - 1)])
+    heads = [0, 13, 29, 47]
+    rows_t = torch.from_numpy(rows).cuda()
+    o_gpu = _np(dl.o_soft_dbg.index_select(0, rows_t))[:, heads]
+    u_gpu = _np(dl.u_lin_dbg.index_select(0, rows_t))[:, heads]
+    q, k, v = (np.ascontiguousarray(a[:, heads]) for a in inp.qkv_values())
+    tk, tv = (np.ascontiguousarray(synth.f64(t)[:, heads]) for t in (inp.text_k, inp.text_v))
+    o_ref = oracle.layer.softmax_branch(q, k, v, tk, tv, F, C, rows=rows)
+    del q, k, v
+    ql, kl, vl = (np.ascontiguousarray(a[:, heads]) for a in inp.linear_qkv_values())
+    u_ref = oracle.layer.linear_branch(ql, kl, vl, tk, tv, F, C, rows=rows)
+    del ql, kl, vl
+    e_o, e_u = rel_l2(o_gpu, o_ref), rel_l2(u_gpu, u_ref)
+    print(f"long fp8 sampled rel-L2: o_soft {e_o:.2e} u {e_u:.2e}", flush=True)
+    assert e_o <= TOL["fp8"] and e_u <= TOL["fp8"]

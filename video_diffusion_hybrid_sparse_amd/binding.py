@@ -43,7 +43,7 @@ class Cfg(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("frame_states", "text_state", "fwd_states", "bwd_states",
-                                               "branch_out", "gemm_ws", "gemm_ws_bytes", "total")]
+                                               "branch_out", "value_stage", "gemm_ws", "gemm_ws_bytes", "total")]
 
 
 _lib: Optional[ctypes.CDLL] = None

@@ -53,12 +53,16 @@ vdn_status check_cfg(const vdn_hybrid_cfg* c) {
   const int qd = c->qkv_dtype, ad = c->act_dtype;
   const bool f32 = qd == VDN_F32 && ad == VDN_F32;
   const bool bf16 = qd == VDN_BF16 && ad == VDN_BF16;
-  if (!f32 && !bf16) {
-    if (qd == VDN_FP8_E4M3 && ad == VDN_BF16)
-      return fail(VDN_ERR_UNSUPPORTED, "fp8 e4m3 softmax inputs are not built yet");
+  const bool fp8 = qd == VDN_FP8_E4M3 && ad == VDN_BF16;
+  if (!f32 && !bf16 && !fp8)
     return fail(VDN_ERR_UNSUPPORTED, "dtype combination qkv=%d act=%d is not supported", qd, ad);
-  }
   const int d = c->head_dim;
+  if (fp8) {
+    if (d != 128) return fail(VDN_ERR_UNSUPPORTED, "fp8 path needs head_dim 128 (got %d)", d);
+    const float sc[3] = {c->q_scale, c->k_scale, c->v_scale};
+    for (float x : sc)
+      if (!(x > 0.0f) || !isfinite(x)) return fail(VDN_ERR_INVALID_ARG, "fp8 q/k/v scales must be finite and > 0");
+  }
   if (bf16 && d != 64 && d != 128) return fail(VDN_ERR_UNSUPPORTED, "bf16 path needs head_dim 64 or 128 (got %d)", d);
   if (f32 && d != 32 && d != 64 && d != 128)
     return fail(VDN_ERR_UNSUPPORTED, "f32 path needs head_dim 32, 64 or 128 (got %d)", d);
@@ -97,6 +101,10 @@ void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
   L->fwd_states = off; off = align_up(off + nC * st);
   L->bwd_states = off; off = align_up(off + nC * st);
   L->branch_out = off; off = align_up(off + N * 2 * H * d * act_bytes(c));
+  // fp8 inputs: bf16 copies of the value codes and of text values / v_scale
+  const size_t L_txt = c->text_len;
+  L->value_stage = off;
+  if (c->qkv_dtype == VDN_FP8_E4M3) off = align_up(off + (N + L_txt) * H * d * 2);
   L->gemm_ws = off; L->gemm_ws_bytes = kGemmWs; off = align_up(off + kGemmWs);
   L->total = off;
 }
@@ -197,6 +205,8 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
     if (!aligned16(r.p)) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", r.name);
   }
   if (cfg->text_len > 0 && !text_kv) return fail(VDN_ERR_INVALID_ARG, "text_kv is NULL but text_len > 0");
+  if (cfg->qkv_dtype == VDN_FP8_E4M3 && !qkv_lin)
+    return fail(VDN_ERR_INVALID_ARG, "qkv_lin (bf16 linear-branch q/k/v) is required with fp8 inputs");
   const void* opt[] = {text_kv, qkv_lin, o_soft_dbg, u_lin_dbg};
   const char* optn[] = {"text_kv", "qkv_lin", "o_soft_dbg", "u_lin_dbg"};
   for (int i = 0; i < 4; ++i)
@@ -228,7 +238,8 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
   const void* kl = lin ? lin + N * row * ab : k;
   const void* vl = lin ? lin + 2 * N * row * ab : v;
   if (!tk) tk = tv = q;  // L == 0: never dereferenced
-  const bool bf16 = cfg->qkv_dtype == VDN_BF16;
+  const bool fp8 = cfg->qkv_dtype == VDN_FP8_E4M3;
+  const bool bf16 = cfg->act_dtype == VDN_BF16;  // linear branch, epilogues, projection
   const float scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / sqrtf((float)g.d);
 
   // profiling slot
@@ -269,9 +280,20 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
   }
   if (e != hipSuccess) return fail(VDN_ERR_HIP, "linear read launch: %s", hipGetErrorString(e));
   mark(3);
-  if (bf16) {
-    SoftmaxArgs sm{(const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv,
-                   (const __bf16*)gs, (__bf16*)acat, o_soft_dbg, g, scale * 1.4426950408889634f};
+  const float c2 = scale * 1.4426950408889634f;
+  if (fp8) {
+    __bf16* vst = reinterpret_cast<__bf16*>(ws + L.value_stage);
+    __bf16* tvst = vst + N * row;
+    DequantArgs da{(const uint8_t*)v, (const __bf16*)tv, vst, tvst, (int64_t)(N * row), (int64_t)g.L * (int64_t)row,
+                   1.0f / cfg->v_scale};
+    e = launch_dequant_values(da, stream);
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "value staging launch: %s", hipGetErrorString(e));
+    SoftmaxArgs sm{q, k, vst, (const __bf16*)tk, tvst, (const __bf16*)gs, (__bf16*)acat, o_soft_dbg, g,
+                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale};
+    e = launch_softmax_fp8(sm, stream);
+  } else if (bf16) {
+    SoftmaxArgs sm{q, k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv, (const __bf16*)gs, (__bf16*)acat,
+                   o_soft_dbg, g, c2, c2, 1.0f};
     e = launch_softmax_bf16(sm, stream);
   } else {
     SoftmaxF32Args sm{(const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,

@@ -5,10 +5,15 @@
 
 namespace vdn {
 
-// Softmax branch (bf16).  q/k/v [N,H,d]; tk/tv [L,H,d]; gs [N,H,d]; acat [N, 2*H*d].
+// Softmax branch.  q/k/v [N,H,d]; tk/tv [L,H,d]; gs [N,H,d]; acat [N, 2*H*d].
+// bf16 inputs: q, k, v, tk, tv are bf16; c2_text = c2_video = scale * log2(e);
+//   out_scale = 1.
+// fp8 inputs: q, k are e4m3 codes (uint8); v is the bf16 copy of the value codes, tv the
+//   bf16 text values divided by the value scale (dequant_values); c2_text = scale *
+//   log2(e) * q_scale, c2_video = c2_text * k_scale, out_scale = v_scale.
 struct SoftmaxArgs {
-  const __bf16* q;
-  const __bf16* k;
+  const void* q;
+  const void* k;
   const __bf16* v;
   const __bf16* tk;
   const __bf16* tv;
@@ -16,7 +21,19 @@ struct SoftmaxArgs {
   __bf16* acat;
   float* o_dbg;  // nullable [N,H,d]
   Geo geo;
-  float scale_log2;  // softmax scale * log2(e)
+  float c2_text, c2_video;
+  float out_scale;
+};
+
+// fp8 value staging: vout[n] = bf16(code value of v8[n]) for the video values and
+// tvout[n] = bf16(tv[n] / v_scale) for the text values.
+struct DequantArgs {
+  const uint8_t* v8;   // [N,H,d] e4m3 codes
+  const __bf16* tv;    // [L,H,d]
+  __bf16* vout;        // [N,H,d]
+  __bf16* tvout;       // [L,H,d]
+  int64_t n_video, n_text;
+  float inv_v_scale;
 };
 
 // Softmax branch (float32), same layouts with float tensors.
@@ -72,6 +89,8 @@ struct ReadoutArgs {
 };
 
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);
+hipError_t launch_softmax_fp8(const SoftmaxArgs& a, hipStream_t stream);
+hipError_t launch_dequant_values(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_softmax_f32(const SoftmaxF32Args& a, hipStream_t stream);
 hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream);
 hipError_t launch_build_f32(const BuildArgs<float>& a, hipStream_t stream);

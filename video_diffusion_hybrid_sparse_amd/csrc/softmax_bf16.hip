@@ -1,4 +1,4 @@
-// Block-sparse flash softmax branch, bf16 inputs, gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+// Block-sparse flash softmax branch on gfx950 MFMA, bf16 or fp8 (e4m3) inputs.
 //
 // Computes, for every video query token n and head h, the exact softmax attention over
 // the text tokens and the tokens of the frames its chunk window and the two anchors
@@ -15,7 +15,7 @@
 // XCD runs a contiguous range of (head, group, query tile): tiles that read the same keys
 // share one L2.  Key and value stages go from HBM straight into LDS (global_load_lds, 16
 // bytes per lane), double-buffered, one barrier per 128-key stage; rows are stored with
-// an XOR swizzle of their 16-byte chunks that makes both LDS read patterns below
+// an XOR swizzle of their 16-byte chunks that makes the LDS read patterns below
 // conflict-free.  Each stage is computed as two 64-key sub-tiles:
 //   S^T = K Q^T (keys x queries): K is the MFMA A operand (16-byte LDS reads); Q^T stays
 //     in registers.  A lane holds the scores of one query, so the softmax statistics need
@@ -23,15 +23,22 @@
 //   O^T += V^T P^T: P^T comes straight from the S^T accumulators (bf16); the V^T operand is
 //     gathered from row-major V with the transposing LDS read (ds_read_b64_tr_b16) in the
 //     key order the accumulator layout implies.
-// Scores stay in the log2 domain (scale * log2 e folded into one FMA); the running max
-// only moves when a sub-tile exceeds it by more than 8, so the O rescale is rare.  Any
-// fixed reference point gives the same softmax; the row sum is taken over the same bf16
-// probabilities that multiply V.
+// Scores stay in the log2 domain (scale * log2 e, and the fp8 scales, folded into one
+// FMA); the running max only moves when a sub-tile exceeds it by more than 8, so the O
+// rescale is rare.  Any fixed reference point gives the same softmax; the row sum is
+// taken over the same bf16 probabilities that multiply V.
+//
+// fp8 inputs: video keys stay e4m3 in LDS and S^T uses v_mfma_f32_32x32x64_f8f6f4 with
+// the e4m3 query codes; text keys are bf16, so the text stages (walked first, in a loop
+// of their own) use the bf16 MFMA with the query codes converted exactly to bf16.  P V
+// stays bf16 on the value codes converted exactly to bf16 (dequant_values), and the
+// per-tensor scales are applied to the scores and to the output.
 #include "kernels.h"
 
 namespace vdn {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Value of the lane pair (l, l ^ 32): v_permlane32_swap exchanges the upper half of its
@@ -54,10 +61,11 @@ __device__ __forceinline__ float pair_sum(float x) {
   return a + b;
 }
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row, per row (see header).
-template <int D>
+// XOR swizzle of the 16-byte chunk index inside an LDS row, for rows of 16 chunks
+// (bf16, head_dim 128) and rows of 8 chunks (bf16 head_dim 64, or e4m3 head_dim 128).
+template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return ((row & 2) << 1) | ((row >> 2) & 3);
 }
 
@@ -66,9 +74,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
       bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p)));
 }
 
-__device__ __forceinline__ void load_lds16(const __bf16* g, __bf16* lds_wave_base) {
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
                                    (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // e4m3 x e4m3 (format selectors 0), unit block scales (E8M0 127 = 2^0)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // Key stages of a query group: ceil(len / BN) stages per segment, segments in the order
@@ -94,15 +107,20 @@ struct KeyWalk {
   }
 };
 
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bf16_kernel(SoftmaxArgs a) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_kernel(SoftmaxArgs a) {
   constexpr int BM = 256, NW = 8;
   constexpr int BN = 128, BC = 64;           // keys per stage, keys per compute sub-tile
-  constexpr int KS = D / 16;                 // MFMA k-steps over head_dim
+  constexpr int KS = D / 16;                 // bf16 MFMA k-steps over head_dim
+  constexpr int KS8 = D / 64;                // fp8 MFMA k-steps over head_dim
   constexpr int DT = D / 32;                 // 32-row tiles of O^T
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;              // rows one wave-wide 16-byte load covers
-  constexpr int NI = BN * CPR / (64 * NW);   // loads per lane per stage (per tensor)
+  constexpr int CPR = D / 8;                 // 16-byte chunks per bf16 row
+  constexpr int RPI = 64 / CPR;              // bf16 rows one wave-wide 16-byte load covers
+  constexpr int NI = BN * CPR / (64 * NW);   // bf16 loads per lane per stage (per tensor)
+  constexpr int CPR8 = D / 16;               // 16-byte chunks per e4m3 row
+  constexpr int RPI8 = 64 / CPR8;
+  constexpr int NI8 = BN * CPR8 / (64 * NW);
+  static_assert(!FP8 || (NI8 >= 1 && CPR8 == 8), "fp8 path is laid out for head_dim 128");
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * D];
 
@@ -120,14 +138,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int nst = kw.stages();
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const size_t rs = (size_t)g.H * D;  // row stride of [*, H, D] tensors
+  const size_t rs = (size_t)g.H * D;  // row stride (elements) of [*, H, D] tensors
 
   int qtok = t0 + wave * 32 + l32;
   const bool qok = qtok < t1;
   qtok = qok ? qtok : t1 - 1;
+  // Q^T operands: bf16 (all bf16 stages, and the fp8 path's text stages) and e4m3
   bf16x8 qreg[KS];
-  {
-    const __bf16* qp = a.q + (size_t)qtok * rs + h * D + half * 8;
+  i32x8 q8[FP8 ? KS8 : 1];
+  if constexpr (FP8) {
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (size_t)qtok * rs + h * D;
+#pragma unroll
+    for (int s = 0; s < KS8; ++s) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * half);
+      const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * half + 16);
+      q8[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    // bf16 operand: channels 16 s + 8 half + 0..7, converted exactly from e4m3
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint2 w = *reinterpret_cast<const uint2*>(qp + 16 * s + 8 * half);
+      const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+      const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+      const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+      const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+      qreg[s] = bf16x8{(__bf16)f0[0], (__bf16)f0[1], (__bf16)f1[0], (__bf16)f1[1],
+                       (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
+    }
+  } else {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)qtok * rs + h * D + half * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(qp + 16 * s);
   }
@@ -137,28 +176,51 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    lcol[i] = ((lane % CPR) ^ swz<D>(lrow[i])) * 8 + h * D;
+    lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
   }
   auto issue = [&](int j, int buf) {
     bool text;
     int start, valid;
     kw.stage_at(j, text, start, valid);
-    const __bf16* kb = text ? a.tk : a.k;
+    if (FP8 && !text) {
+      // e4m3 keys: rows of D bytes, CPR8 chunks
+      const uint8_t* kb = static_cast<const uint8_t*>(a.k);
+      uint8_t* kd = reinterpret_cast<uint8_t*>(Ks[buf]);
+#pragma unroll
+      for (int i = 0; i < NI8; ++i) {
+        const int r = (wave * NI8 + i) * RPI8 + lane / CPR8;
+        const int row = start + imin(r, valid - 1);
+        const size_t o = (size_t)row * rs + h * D + ((lane % CPR8) ^ swz<CPR8>(r)) * 16;
+        load_lds16(kb + o, kd + (wave * NI8 + i) * RPI8 * D);
+      }
+    } else {
+      const __bf16* kb = text ? a.tk : static_cast<const __bf16*>(a.k);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = start + imin(lrow[i], valid - 1);  // rows past the segment: masked later
+        load_lds16(kb + (size_t)row * rs + lcol[i], &Ks[buf][(wave * NI + i) * RPI * D]);
+      }
+    }
     const __bf16* vb = text ? a.tv : a.v;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = start + imin(lrow[i], valid - 1);  // rows past the segment: masked later
-      const size_t o = (size_t)row * rs + lcol[i];
-      load_lds16(kb + o, &Ks[buf][(wave * NI + i) * RPI * D]);
-      load_lds16(vb + o, &Vs[buf][(wave * NI + i) * RPI * D]);
+      const int row = start + imin(lrow[i], valid - 1);
+      load_lds16(vb + (size_t)row * rs + lcol[i], &Vs[buf][(wave * NI + i) * RPI * D]);
     }
   };
 
-  // LDS read offsets (elements), the same for every sub-tile (the swizzle depends on the
-  // low 4 bits of the row only, so sub-tile and row-tile offsets are plain additions)
+  // LDS read offsets (elements / bytes), the same for every sub-tile (the swizzle depends
+  // on the low 4 bits of the row only, so sub-tile and row-tile offsets are plain additions)
   int krd[KS];
 #pragma unroll
-  for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<D>(l32)) * 8);
+  for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
+  int krd8[FP8 ? 2 * KS8 : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int k = 0; k < KS8; ++k)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) krd8[2 * k + e] = l32 * D + (((4 * k + 2 * half + e) ^ swz<CPR8>(l32)) * 16);
+  }
   const int grp16 = lane >> 4, i16 = lane & 15;
   int vrd[DT][2];
 #pragma unroll
@@ -169,41 +231,53 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       // the transposing read hands lane j of the group channel d0 + j of keys K0..K0+3
       const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
       const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
-      vrd[dt][c] = row * D + (((d >> 3) ^ swz<D>(row)) * 8) + (d & 7);
+      vrd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
     }
 
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = 0.0f;
   float m = -INFINITY, l = 0.0f;
-  const float c2 = a.scale_log2;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int j = 0; j < nst; ++j) {
+  // One 128-key stage: two 64-key sub-tiles of scores, softmax update and P V.
+  // VIDEO8 selects the e4m3 score path (fp8 inputs, video keys).
+  auto stage = [&](int j, auto video8) {
+    constexpr bool VIDEO8 = decltype(video8)::value;
     const int buf = j & 1;
     bool text;
     int start, svalid;
     kw.stage_at(j, text, start, svalid);
+    const float c2 = VIDEO8 ? a.c2_video : a.c2_text;
     if (j + 1 < nst) issue(j + 1, buf ^ 1);
 
     for (int sub = 0; sub < BN / BC; ++sub) {
       const int valid = svalid - sub * BC;  // valid keys of this sub-tile (>= BC when full)
       if (valid <= 0) break;
-      const __bf16* K = Ks[buf] + sub * BC * D;
       const __bf16* V = Vs[buf] + sub * BC * D;
 
       f32x16 s[2];
       s[0] = 0.0f;
       s[1] = 0.0f;
+      if constexpr (VIDEO8) {
+        const uint8_t* K8 = reinterpret_cast<const uint8_t*>(Ks[buf]) + sub * BC * D;
 #pragma unroll
-      for (int k = 0; k < KS; ++k)
+        for (int k = 0; k < KS8; ++k)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[k]), qreg[k], s[rt]);
+          for (int rt = 0; rt < 2; ++rt) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(K8 + 32 * rt * D + krd8[2 * k]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(K8 + 32 * rt * D + krd8[2 * k + 1]);
+            const i32x8 ka = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            s[rt] = mfma32x32x64_fp8(ka, q8[k], s[rt]);
+          }
+      } else {
+        const __bf16* K = Ks[buf] + sub * BC * D;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[k]), qreg[k], s[rt]);
+      }
       if (valid < BC) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -255,10 +329,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     // the next stage has landed in every wave, and every wave is done with this one
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-  }
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // text stages first (bf16 keys), then the video stages
+  int j = 0;
+  for (; j < kw.n0; ++j) stage(j, std::integral_constant<bool, false>{});
+  for (; j < nst; ++j) stage(j, std::integral_constant<bool, FP8>{});
 
   l = pair_sum(l);
-  const float inv = 1.0f / l;
+  const float inv = a.out_scale / l;
   if (!qok) return;
   const size_t orow = (size_t)qtok * rs + h * D;
   __bf16* arow = a.acat + (size_t)qtok * 2 * rs + h * D;
@@ -286,11 +368,59 @@ hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles * a.geo.H), block(512);
   if (a.geo.d == 128)
-    hipLaunchKernelGGL(softmax_bf16_kernel<128>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_kernel<128, false>), grid, block, 0, stream, a);
   else if (a.geo.d == 64)
-    hipLaunchKernelGGL(softmax_bf16_kernel<64>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_kernel<64, false>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_fp8(const SoftmaxArgs& a, hipStream_t stream) {
+  const int tiles = count_tiles(a.geo, 256);
+  if (tiles == 0) return hipSuccess;
+  if (a.geo.d != 128) return hipErrorInvalidValue;
+  dim3 grid(tiles * a.geo.H), block(512);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_kernel<128, true>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---- fp8 value staging ---------------------------------------------------------------
+// Video value codes -> bf16 (exact: every e4m3 value is a bf16 value); text values -> bf16
+// of value / v_scale, so one accumulator serves both and the output is scaled by v_scale.
+__global__ __launch_bounds__(256) void dequant_values_kernel(DequantArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i < a.n_video) {
+    const uint2 w = *reinterpret_cast<const uint2*>(a.v8 + i);
+    const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    uint4 out;
+    out.x = pack_bf16x2(f0[0], f0[1]);
+    out.y = pack_bf16x2(f1[0], f1[1]);
+    out.z = pack_bf16x2(f2[0], f2[1]);
+    out.w = pack_bf16x2(f3[0], f3[1]);
+    *reinterpret_cast<uint4*>(a.vout + i) = out;
+  } else {
+    const int64_t t = i - a.n_video;
+    if (t >= a.n_text) return;
+    const uint4 w = *reinterpret_cast<const uint4*>(a.tv + t);
+    uint4 out;
+    out.x = pack_bf16x2(bf16_to_f32(w.x & 0xffff) * a.inv_v_scale, bf16_to_f32(w.x >> 16) * a.inv_v_scale);
+    out.y = pack_bf16x2(bf16_to_f32(w.y & 0xffff) * a.inv_v_scale, bf16_to_f32(w.y >> 16) * a.inv_v_scale);
+    out.z = pack_bf16x2(bf16_to_f32(w.z & 0xffff) * a.inv_v_scale, bf16_to_f32(w.z >> 16) * a.inv_v_scale);
+    out.w = pack_bf16x2(bf16_to_f32(w.w & 0xffff) * a.inv_v_scale, bf16_to_f32(w.w >> 16) * a.inv_v_scale);
+    *reinterpret_cast<uint4*>(a.tvout + t) = out;
+  }
+}
+
+hipError_t launch_dequant_values(const DequantArgs& a, hipStream_t stream) {
+  // both element counts are multiples of head_dim (>= 64), hence of 8
+  const int64_t units = (a.n_video + a.n_text) / 8;
+  if (units == 0) return hipSuccess;
+  dim3 grid((unsigned)((units + 255) / 256)), block(256);
+  hipLaunchKernelGGL(dequant_values_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
