@@ -171,4 +171,49 @@ __device__ inline float bf16_to_f32(uint16_t bits) {
   return __builtin_bit_cast(float, (uint32_t)bits << 16);
 }
 
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Value of the lane pair (l, l ^ 32): v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, so with both holding x they end up
+// holding x and the partner's x.  The compiler does not look inside the asm, so the asm
+// carries the wait states a VALU write before, and a read after, the swap need.
+__device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_swap(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_swap(x, a, b);
+  return a + b;
+}
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row, for rows of 16 chunks
+// (bf16, head_dim 128) and rows of 8 chunks (bf16 head_dim 64, or e4m3 head_dim 128).
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return ((row & 2) << 1) | ((row >> 2) & 3);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
+  return __builtin_bit_cast(
+      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p)));
+}
+
+// Four v_permlane32_swap at once: for each e, lanes 32-63 of x[e] and lanes 0-31 of y[e]
+// trade places (x[e] keeps its lanes 0-31, y[e] its lanes 32-63).
+__device__ __forceinline__ void permlane32_swap4(float (&x)[4], float (&y)[4]) {
+  asm volatile(
+      "s_nop 2\n\tv_permlane32_swap_b32 %0, %4\n\tv_permlane32_swap_b32 %1, %5\n\t"
+      "v_permlane32_swap_b32 %2, %6\n\tv_permlane32_swap_b32 %3, %7\n\ts_nop 2"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
+}
+
 }  // namespace vdn

@@ -131,16 +131,20 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 
 // ---- state read: u = q.S_fwd + q.S_bwd, RMSNorm, gate --------------------------------
 //
-// One workgroup = 128 query tokens of one query group and one head.  The group's two
-// states are summed in float32 (the identity feature map makes q.S_fwd + q.S_bwd equal
-// to q.(S_fwd + S_bwd); only rounding differs), split into bf16 hi + lo parts and
-// stored transposed in LDS, so u^T = S^T q^T runs as two bf16 MFMA passes with float32
-// accumulation (about 16 mantissa bits of the state kept).  Lanes own one token each.
+// One workgroup = up to 512 query tokens of one query group and one head; each of the 4
+// waves walks 32-token sub-tiles.  The group's two states are summed in float32 (the
+// identity feature map makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding
+// differs), split into bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled
+// 16-byte chunks) in LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes
+// with float32 accumulation (about 16 mantissa bits of the state kept); the S^T operand is
+// gathered with the transposing LDS read.  A lane owns one token, so RMSNorm needs one
+// lane-pair sum; a lane-pair swap then gives each lane 8 contiguous channels, so gate
+// loads and output stores are 16 bytes wide.
 template <int D>
 __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
-  constexpr int BM = 128, PAD = D + 8, KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 Shi[D * PAD];
-  __shared__ __attribute__((aligned(16))) __bf16 Slo[D * PAD];
+  constexpr int BM = 512, KS = D / 16, DT = D / 32, CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) __bf16 Shi[D * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Slo[D * D];
   const Geo g = a.geo;
   const int h = blockIdx.y;
   int grp, t0, t1;
@@ -150,87 +154,117 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
   const size_t rs = (size_t)g.H * D;
   const size_t hs = (size_t)h * D * D;
 
-  // S_sum^T into LDS: unit = rows (i, i+1) x columns j..j+3
+  // S_sum = S_fwd + S_bwd (anchors: text/2 + text/2) into LDS as bf16 hi + lo
   {
     const float* ta = a.Stext + hs;
     const float* fa = chunk >= 0 ? a.Sfwd + (size_t)chunk * g.H * D * D + hs : ta;
     const float* ba = chunk >= 0 ? a.Sbwd + (size_t)chunk * g.H * D * D + hs : ta;
-    const float wf = chunk >= 0 ? 1.0f : 0.5f;  // anchor rows: text/2 + text/2
-    for (int u = tid; u < D * D / 8; u += 256) {
-      const int i = 2 * (u / (D / 4)), j = 4 * (u % (D / 4));
-      const float4 f0 = *reinterpret_cast<const float4*>(fa + i * D + j);
-      const float4 f1 = *reinterpret_cast<const float4*>(fa + (i + 1) * D + j);
-      const float4 b0 = *reinterpret_cast<const float4*>(ba + i * D + j);
-      const float4 b1 = *reinterpret_cast<const float4*>(ba + (i + 1) * D + j);
-      const float s0[4] = {wf * f0.x + wf * b0.x, wf * f0.y + wf * b0.y, wf * f0.z + wf * b0.z, wf * f0.w + wf * b0.w};
-      const float s1[4] = {wf * f1.x + wf * b1.x, wf * f1.y + wf * b1.y, wf * f1.z + wf * b1.z, wf * f1.w + wf * b1.w};
+    const float wf = chunk >= 0 ? 1.0f : 0.5f;
+    for (int u = tid; u < D * D / 4; u += 256) {
+      const int i = u / (D / 4), j = 4 * (u % (D / 4));
+      const float4 f = *reinterpret_cast<const float4*>(fa + i * D + j);
+      const float4 b = *reinterpret_cast<const float4*>(ba + i * D + j);
+      const float sv[4] = {wf * f.x + wf * b.x, wf * f.y + wf * b.y, wf * f.z + wf * b.z, wf * f.w + wf * b.w};
+      float hv[4], lv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const __bf16 h0 = (__bf16)s0[e], h1 = (__bf16)s1[e];
-        const float l0 = s0[e] - (float)h0, l1 = s1[e] - (float)h1;
-        bf16x2 hv = {h0, h1};
-        *reinterpret_cast<uint32_t*>(&Shi[(j + e) * PAD + i]) = __builtin_bit_cast(uint32_t, hv);
-        *reinterpret_cast<uint32_t*>(&Slo[(j + e) * PAD + i]) = pack_bf16x2(l0, l1);
+        hv[e] = (float)(__bf16)sv[e];
+        lv[e] = sv[e] - hv[e];
       }
+      const int off = i * D + (((j >> 3) ^ swz<CPR>(i)) * 8) + (j & 7);
+      *reinterpret_cast<uint2*>(&Shi[off]) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      *reinterpret_cast<uint2*>(&Slo[off]) = make_uint2(pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3]));
     }
   }
   __syncthreads();
 
-  int tok = t0 + wave * 32 + l32;
-  const bool ok = tok < t1;
-  tok = ok ? tok : t1 - 1;
-  bf16x8 qreg[KS];
-  const size_t qrow = (size_t)tok * rs + h * D;
+  // S^T operand via the transposing read: 16-lane group grp16 reads d_in rows K0..K0+3 and
+  // d_out columns D0..D0+15; lane j of the group gets column D0 + j of rows K0..K0+3
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int srd[DT][2];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 8 * (grp16 >> 1) + 4 * c + (i16 >> 2);
+      const int col = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      srd[dt][c] = row * D + (((col >> 3) ^ swz<CPR>(row)) * 8) + (col & 7);
+    }
+  const float* wrow = a.w + h * D;
 
-  f32x16 u[DT];
+  for (int st = wave; st * 32 < t1 - t0; st += 4) {
+    int tok = t0 + st * 32 + l32;
+    const bool ok = tok < t1;
+    tok = ok ? tok : t1 - 1;
+    const size_t qrow = (size_t)tok * rs + h * D;
+    bf16x8 qreg[KS];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    u[dt] = 0.0f;
-    const __bf16* hp = &Shi[(32 * dt + l32) * PAD + 8 * half];
-    const __bf16* lp = &Slo[(32 * dt + l32) * PAD + 8 * half];
+    for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+
+    f32x16 u[DT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u[dt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(lp + 16 * ks), qreg[ks], u[dt]);
-      u[dt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(hp + 16 * ks), qreg[ks], u[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+      u[dt] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        // rows 16 ks + 8 half + 4 c + e of S are d_in slots 8 half + 4 c + e of this k-step
+        const int base = 16 * ks * D;
+        const bf16x4 l0 = lds_read_tr(Slo + base + srd[dt][0]), l1 = lds_read_tr(Slo + base + srd[dt][1]);
+        const bf16x4 h0 = lds_read_tr(Shi + base + srd[dt][0]), h1 = lds_read_tr(Shi + base + srd[dt][1]);
+        const bf16x8 lo = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        const bf16x8 hi = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        u[dt] = mfma32x32x16(lo, qreg[ks], u[dt]);
+        u[dt] = mfma32x32x16(hi, qreg[ks], u[dt]);
+      }
     }
+    // lane holds channels 32 dt + 8 i + 4 half + e of token `tok`
+    float ss = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss += u[dt][r] * u[dt][r];
+    const float rinv = rsqrtf(pair_sum(ss) / D + a.eps);
+    __bf16* arow = a.acat + (size_t)tok * 2 * rs + rs + h * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        // after the swap: lanes 0-31 hold channels c0 .. c0+7 with c0 = 32 dt + 16 ip,
+        // lanes 32-63 hold c0 + 8 .. c0 + 15
+        float x[4], y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = u[dt][4 * (2 * ip) + e];
+          y[e] = u[dt][4 * (2 * ip + 1) + e];
+        }
+        permlane32_swap4(x, y);
+        const int c0 = 32 * dt + 16 * ip + 8 * half;
+        const float uv[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        const uint4 graw = *reinterpret_cast<const uint4*>(a.gl + qrow + c0);
+        const float4 w0 = *reinterpret_cast<const float4*>(wrow + c0);
+        const float4 w1 = *reinterpret_cast<const float4*>(wrow + c0 + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float gv = bf16_to_f32((e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffff));
+          r[e] = sigmoid(gv) * (uv[e] * rinv * wv[e]);
+        }
+        if (ok) {
+          *reinterpret_cast<uint4*>(arow + c0) = make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]),
+                                                             pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7]));
+          if (a.u_dbg) {
+            *reinterpret_cast<float4*>(a.u_dbg + qrow + c0) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+            *reinterpret_cast<float4*>(a.u_dbg + qrow + c0 + 4) = make_float4(uv[4], uv[5], uv[6], uv[7]);
+          }
+        }
+      }
   }
-  // lane holds channels 32 dt + 8 i + 4 half + e of token `tok`
-  float ss = 0.0f;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ss += u[dt][r] * u[dt][r];
-  ss += __shfl_xor(ss, 32);
-  const float rinv = rsqrtf(ss / D + a.eps);
-  if (!ok) return;
-  __bf16* arow = a.acat + (size_t)tok * 2 * rs + rs + h * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 32 * dt + 8 * i + 4 * half;
-      const float4 w4 = *reinterpret_cast<const float4*>(a.w + h * D + d0);
-      const uint2 graw = *reinterpret_cast<const uint2*>(a.gl + qrow + d0);
-      const float gv[4] = {bf16_to_f32(graw.x & 0xffff), bf16_to_f32(graw.x >> 16),
-                           bf16_to_f32(graw.y & 0xffff), bf16_to_f32(graw.y >> 16)};
-      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-      float r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = sigmoid(gv[e]) * (u[dt][4 * i + e] * rinv * wv[e]);
-      uint2 ov;
-      ov.x = pack_bf16x2(r[0], r[1]);
-      ov.y = pack_bf16x2(r[2], r[3]);
-      *reinterpret_cast<uint2*>(arow + d0) = ov;
-      if (a.u_dbg)
-        *reinterpret_cast<float4*>(a.u_dbg + qrow + d0) =
-            make_float4(u[dt][4 * i], u[dt][4 * i + 1], u[dt][4 * i + 2], u[dt][4 * i + 3]);
-    }
 }
 
 hipError_t launch_readout_bf16(const ReadoutArgs<__bf16>& a, hipStream_t stream) {
-  const int tiles = count_tiles(a.geo, 128);
+  const int tiles = count_tiles(a.geo, 512);
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.geo.H), block(256);
   if (a.geo.d == 128)

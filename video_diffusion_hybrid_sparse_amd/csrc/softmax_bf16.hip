@@ -37,42 +37,8 @@
 
 namespace vdn {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Value of the lane pair (l, l ^ 32): v_permlane32_swap exchanges the upper half of its
-// first operand with the lower half of its second, so with both holding x they end up
-// holding x and the partner's x.  The compiler does not look inside the asm, so the asm
-// carries the wait states a VALU write before, and a read after, the swap need.
-__device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
-  a = x;
-  b = x;
-  asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float pair_max(float x) {
-  float a, b;
-  pair_swap(x, a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  float a, b;
-  pair_swap(x, a, b);
-  return a + b;
-}
-
-// XOR swizzle of the 16-byte chunk index inside an LDS row, for rows of 16 chunks
-// (bf16, head_dim 128) and rows of 8 chunks (bf16 head_dim 64, or e4m3 head_dim 128).
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-  else return ((row & 2) << 1) | ((row >> 2) & 3);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
-  return __builtin_bit_cast(
-      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p)));
-}
 
 __device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
@@ -341,25 +307,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   l = pair_sum(l);
   const float inv = a.out_scale / l;
-  if (!qok) return;
   const size_t orow = (size_t)qtok * rs + h * D;
   __bf16* arow = a.acat + (size_t)qtok * 2 * rs + h * D;
+  // lane holds channels 32 dt + 8 i + 4 half + e; a lane-pair swap gives each lane 8
+  // contiguous channels so the gate loads and output stores are 16 bytes wide
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 32 * dt + 8 * i + 4 * half;
-      const uint2 graw = *reinterpret_cast<const uint2*>(a.gs + orow + d0);
-      float ov[4], gv[4];
-      gv[0] = bf16_to_f32(graw.x & 0xffff); gv[1] = bf16_to_f32(graw.x >> 16);
-      gv[2] = bf16_to_f32(graw.y & 0xffff); gv[3] = bf16_to_f32(graw.y >> 16);
+    for (int ip = 0; ip < 2; ++ip) {
+      float x[4], y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = o[dt][4 * i + e] * inv;
-      uint2 outv;
-      outv.x = pack_bf16x2(sigmoid(gv[0]) * ov[0], sigmoid(gv[1]) * ov[1]);
-      outv.y = pack_bf16x2(sigmoid(gv[2]) * ov[2], sigmoid(gv[3]) * ov[3]);
-      *reinterpret_cast<uint2*>(arow + d0) = outv;
-      if (a.o_dbg) *reinterpret_cast<float4*>(a.o_dbg + orow + d0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+      for (int e = 0; e < 4; ++e) {
+        x[e] = o[dt][4 * (2 * ip) + e] * inv;
+        y[e] = o[dt][4 * (2 * ip + 1) + e] * inv;
+      }
+      permlane32_swap4(x, y);
+      const int c0 = 32 * dt + 16 * ip + 8 * half;
+      const float ov[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+      const uint4 graw = *reinterpret_cast<const uint4*>(a.gs + orow + c0);
+      const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        r[e] = sigmoid(bf16_to_f32((e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffff))) * ov[e];
+      if (qok) {
+        *reinterpret_cast<uint4*>(arow + c0) = make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]),
+                                                           pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7]));
+        if (a.o_dbg) {
+          *reinterpret_cast<float4*>(a.o_dbg + orow + c0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+          *reinterpret_cast<float4*>(a.o_dbg + orow + c0 + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
+        }
+      }
     }
 }
 
