@@ -28,16 +28,27 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const float4 half = make_float4(0.5f * t.x, 0.5f * t.y, 0.5f * t.z, 0.5f * t.w);
   const int64_t n4 = a.n4;
 
+  // Chunk sums.  The frames of a chunk are loaded together (up to 8 per chunk in one
+  // unrolled, predicated group) so every lane keeps several 16-byte loads in flight.
   float4 cs[MAXC];
 #pragma unroll
   for (int j = 0; j < MAXC; ++j) {
     cs[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (j < g.nC) {
       const int f0 = j * g.C, f1 = imin(g.F, f0 + g.C);
-      for (int f = f0; f < f1; ++f) {
-        if (is_anchor(g, f)) continue;
-        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(&S[f * n4 + e]));
-        cs[j].x += x[0]; cs[j].y += x[1]; cs[j].z += x[2]; cs[j].w += x[3];
+      for (int fb = f0; fb < f1; fb += 8) {
+        f32x4 x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int f = fb + k;
+          x[k] = (f < f1 && !is_anchor(g, f))
+                     ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(&S[f * n4 + e]))
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          cs[j].x += x[k][0]; cs[j].y += x[k][1]; cs[j].z += x[k][2]; cs[j].w += x[k][3];
+        }
       }
     }
   }
