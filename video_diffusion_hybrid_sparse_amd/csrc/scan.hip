@@ -79,9 +79,86 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
 }
 
+// Same result with four times the threads.  A workgroup owns 64 float4 columns of the
+// state; its four waves split the chunks (wave w takes chunks w, w + 4, ...), sum each
+// chunk's frames into LDS, and after one barrier every thread writes the forward and
+// backward states of its own chunks from the chunk sums (same summation order as above,
+// so the results are bitwise equal).  Frame loads go through a buffer resource: loads of
+// frames that do not count (anchors, slots past the chunk or past the last frame) get an
+// offset beyond the resource's size, which the hardware answers with zeros without a
+// memory access, so the CP loads of a chunk are issued together without branches.
+// Requires CP >= chunk_frames, nC <= 4 * CPW and per-frame states spanning < 2^31 bytes.
+template <int CPW, int CP>
+__global__ __launch_bounds__(256) void scan_lds_kernel(ScanArgs a) {
+  __shared__ f32x4 csum[4 * CPW][64];
+  const Geo g = a.geo;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t n4 = a.n4;
+  const int64_t e = (int64_t)blockIdx.x * 64 + lane;
+  const bool live = e < n4;
+  const uint32_t bytes = (uint32_t)(g.F * n4 * 16);
+  // raw buffer: base, stride 0, size in bytes, 32-bit data format word
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.S), 0, (int)bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int j = w + 4 * i;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < CP; ++k) {
+      const int f = j * g.C + k;
+      const bool counts = live && j < g.nC && k < g.C && f < g.F && !is_anchor(g, f);
+      const uint32_t off = counts ? (uint32_t)((f * n4 + e) * 16) : 0x80000000u;
+      acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+    csum[j][lane] = acc;
+  }
+  __syncthreads();
+  if (!live) return;
+  const f32x4 half = __builtin_bit_cast(f32x4, reinterpret_cast<const float4*>(a.Stext)[e]) * 0.5f;
+  f32x4* Sf = reinterpret_cast<f32x4*>(a.Sfwd);
+  f32x4* Sb = reinterpret_cast<f32x4*>(a.Sbwd);
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = w + 4 * i;
+    if (c < g.nC) {
+      f32x4 pre = {0.f, 0.f, 0.f, 0.f};
+      const int pf = fwd_prefix_chunk(g, c);  // chunks 0..pf end before the window
+      for (int j = 0; j <= pf; ++j) pre += csum[j][lane];
+      Sf[c * n4 + e] = half + pre;
+      f32x4 suf = {0.f, 0.f, 0.f, 0.f};
+      const int bf = bwd_prefix_chunk(g, c);  // chunks after bf start after the window
+      for (int j = g.nC - 1; j > bf; --j) suf += csum[j][lane];
+      Sb[c * n4 + e] = half + suf;
+    }
+  }
+}
+
+template <int CPW>
+static hipError_t launch_scan_lds(const ScanArgs& a, int C, hipStream_t stream) {
+  dim3 grid((unsigned)((a.n4 + 63) / 64)), block(256);
+  switch (C) {
+    case 1: hipLaunchKernelGGL(HIP_KERNEL_NAME(scan_lds_kernel<CPW, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(HIP_KERNEL_NAME(scan_lds_kernel<CPW, 2>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(HIP_KERNEL_NAME(scan_lds_kernel<CPW, 3>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(HIP_KERNEL_NAME(scan_lds_kernel<CPW, 4>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL(HIP_KERNEL_NAME(scan_lds_kernel<CPW, 5>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(HIP_KERNEL_NAME(scan_lds_kernel<CPW, 8>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
-  const int nC = a.geo.nC;
+  const int nC = a.geo.nC, C = a.geo.C;
   dim3 grid((unsigned)((a.n4 + 255) / 256)), block(256);
+  if ((double)a.geo.F * (double)a.n4 * 16.0 < 2147483648.0 && C <= 8) {
+    if (nC <= 4) return launch_scan_lds<1>(a, C, stream);
+    if (nC <= 8) return launch_scan_lds<2>(a, C, stream);
+    if (nC <= 12) return launch_scan_lds<3>(a, C, stream);
+    if (nC <= 16) return launch_scan_lds<4>(a, C, stream);
+    if (nC <= 24) return launch_scan_lds<6>(a, C, stream);
+    if (nC <= 32) return launch_scan_lds<8>(a, C, stream);
+  }
   if (nC <= 4)
     hipLaunchKernelGGL(scan_kernel<4>, grid, block, 0, stream, a);
   else if (nC <= 8)
