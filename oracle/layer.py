@@ -14,6 +14,21 @@ Sources, all in the VDN-MiniMax-H3 article (modelscope.csdn.net):
 
 Array layouts: q, k, v, gates [N, H, d] with token n in frame n // T; text_k, text_v
 [L, H, d]; w_rms [H, d]; w_s, w_l [D, H*d] (output rows, input columns); x [N, D].
+
+Linear variant 1 (delta rule).  The article's summary (section "解决的问题") says the
+long-range branch is a delta linear attention whose state matrix is updated over time,
+and the model card names the model Video DeltaNet; neither gives the rule.  The reading
+taken here is the DeltaNet delta rule applied once per frame:
+
+* feature map phi(x) = x / sqrt(sum x^2 + EPS_PHI) on keys and queries;
+* frame update S <- S + (beta / T) Khat^T (V - Khat S) over the frame's T tokens, all
+  with the state from before the frame (beta in (0, 1] a per-layer step size);
+* the text block is the same update applied to a zero state with L tokens; both
+  recurrences start from half of it;
+* the forward recurrence takes the non-anchor frames in increasing order, the backward
+  recurrence in decreasing order; a query reads the forward state after the frames
+  before its window and the backward state after the frames behind it (the same frame
+  sets as the additive variant), and u = phi(q).S_fwd + phi(q).S_bwd.
 """
 from __future__ import annotations
 
@@ -131,6 +146,81 @@ def linear_branch(q, k, v, text_k, text_v, frames: int, chunk_frames: int,
     return linear_read(q, fwd, bwd, frames, rows)
 
 
+EPS_PHI = 1e-6
+
+
+def phi(x) -> np.ndarray:
+    """Delta-rule feature map: x / sqrt(sum over head_dim of x^2 + EPS_PHI)."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + EPS_PHI)
+
+
+def delta_update(S, k_blk, v_blk, beta: float) -> np.ndarray:
+    """One block update of the delta rule for one head.
+
+    S [d, d]; k_blk, v_blk [n, d] (raw keys and values of the block's n tokens):
+    S + (beta / n) Khat^T (V - Khat S) with Khat = phi(k_blk) and S held fixed over
+    the block.
+    """
+    S, v_blk = _f64(S), _f64(v_blk)
+    n = k_blk.shape[0]
+    if n == 0:
+        return S.copy()
+    kh = phi(k_blk)
+    return S + (beta / n) * (kh.T @ (v_blk - kh @ S))
+
+
+def delta_text_state(text_k, text_v, beta: float) -> np.ndarray:
+    """Tx [H, d, d]: the delta update of a zero state with the text tokens."""
+    text_k, text_v = _f64(text_k), _f64(text_v)
+    L, H, d = text_k.shape
+    return np.stack([delta_update(np.zeros((d, d)), text_k[:, h], text_v[:, h], beta)
+                     for h in range(H)])
+
+
+def delta_run(init, k, v, order, frames: int, beta: float) -> list:
+    """States of one recurrence: element i is the [H, d, d] state after the first i
+    frames of ``order`` (element 0 is ``init``)."""
+    k, v = _f64(k), _f64(v)
+    N, H, d = k.shape
+    T = N // frames
+    out = [_f64(init).copy()]
+    for g in order:
+        prev = out[-1]
+        out.append(np.stack([delta_update(prev[h], k[g * T:(g + 1) * T, h], v[g * T:(g + 1) * T, h], beta)
+                             for h in range(H)]))
+    return out
+
+
+def delta_side_states(k, v, text_k, text_v, frames: int, chunk_frames: int,
+                      neighbor_chunks: int = 1, beta: float = 0.5):
+    """(S_fwd, S_bwd, Tx) of the delta variant; S_fwd/S_bwd [F, H, d, d] aligned to
+    every query frame, Tx [H, d, d] the text state (both recurrences start at Tx/2)."""
+    Tx = delta_text_state(text_k, text_v, beta)
+    init = 0.5 * Tx
+    inner = [g for g in range(frames) if not sets.is_anchor(g, frames)]
+    fwd_run = delta_run(init, k, v, inner, frames, beta)
+    bwd_run = delta_run(init, k, v, inner[::-1], frames, beta)
+    H, d = Tx.shape[0], Tx.shape[1]
+    fwd = np.zeros((frames, H, d, d))
+    bwd = np.zeros((frames, H, d, d))
+    for f in range(frames):
+        fw = sets.forward_frames(f, frames, chunk_frames, neighbor_chunks)
+        bw = sets.backward_frames(f, frames, chunk_frames, neighbor_chunks)
+        # each set is a prefix of its recurrence's frame order
+        assert sorted(fw) == inner[:len(fw)] and sorted(bw) == sorted(inner[::-1][:len(bw)]), f
+        fwd[f] = fwd_run[len(fw)]
+        bwd[f] = bwd_run[len(bw)]
+    return fwd, bwd, Tx
+
+
+def delta_linear_branch(q, k, v, text_k, text_v, frames: int, chunk_frames: int,
+                        neighbor_chunks: int = 1, beta: float = 0.5, rows=None) -> np.ndarray:
+    """u = phi(q).S_fwd + phi(q).S_bwd with the delta-rule states."""
+    fwd, bwd, _ = delta_side_states(k, v, text_k, text_v, frames, chunk_frames, neighbor_chunks, beta)
+    return linear_read(phi(q), fwd, bwd, frames, rows)
+
+
 def rms_norm(u, w, eps: float = 1e-6) -> np.ndarray:
     """u / sqrt(mean over head_dim of u^2 + eps), times the weight of (head, channel)."""
     u, w = _f64(u), _f64(w)
@@ -151,17 +241,24 @@ def project(a_s, a_l, w_s, w_l, x) -> np.ndarray:
 
 def layer(q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, frames: int,
           chunk_frames: int, neighbor_chunks: int = 1, eps: float = 1e-6,
-          scale: float | None = None, q_lin=None, k_lin=None, v_lin=None) -> dict:
+          scale: float | None = None, q_lin=None, k_lin=None, v_lin=None,
+          linear_variant: int = 0, beta: float = 0.5) -> dict:
     """Full layer.  Returns codes, o_soft, u, a_s, a_l, out.
 
     q_lin/k_lin/v_lin, when given, feed the linear branch instead of q/k/v (the
     softmax branch may see a lower-precision copy of the same activations).
+    linear_variant 0: additive states; 1: delta rule with step size ``beta``.
     """
     ql = q if q_lin is None else q_lin
     kl = k if k_lin is None else k_lin
     vl = v if v_lin is None else v_lin
     o_soft = softmax_branch(q, k, v, text_k, text_v, frames, chunk_frames, neighbor_chunks, scale)
-    u = linear_branch(ql, kl, vl, text_k, text_v, frames, chunk_frames, neighbor_chunks)
+    if linear_variant == 0:
+        u = linear_branch(ql, kl, vl, text_k, text_v, frames, chunk_frames, neighbor_chunks)
+    elif linear_variant == 1:
+        u = delta_linear_branch(ql, kl, vl, text_k, text_v, frames, chunk_frames, neighbor_chunks, beta)
+    else:
+        raise ValueError(f"linear_variant {linear_variant}")
     a_s = sigmoid(g_s) * o_soft
     a_l = sigmoid(g_l) * rms_norm(u, w_rms, eps)
     out = project(a_s, a_l, w_s, w_l, x)
