@@ -22,6 +22,18 @@
  * elementwise over [token, head, channel] and act before the projections; RMSNorm is
  * over head_dim with a per-(head, channel) float32 weight; no projection bias.
  *
+ * Linear variant 1 (delta rule).  The article's summary (section "解决的问题") calls the
+ * long-range branch a delta linear attention whose state matrix is updated over time,
+ * without giving the update.  Variant 1 reads it as the DeltaNet rule applied once per
+ * frame: phi(x) = x / sqrt(|x|^2 + 1e-6) on keys and queries;
+ * S <- S + (delta_beta / T) Khat^T (V - Khat S) per frame with S fixed over the frame's
+ * T tokens; the text block is the same update of a zero state (L tokens) and both
+ * recurrences start from half of it; the forward recurrence takes the non-anchor frames
+ * in increasing order, the backward one in decreasing order; a query reads the forward
+ * state after the frames before its window and the backward state after the frames
+ * behind it (the variant-0 frame sets), u = phi(q).S_fwd + phi(q).S_bwd; RMSNorm, gate
+ * and projection as in variant 0.
+ *
  * Conventions for every entry point:
  *   - All tensors are dense, row-major, 16-byte aligned device pointers owned by the
  *     caller.  The library allocates no tensor memory; scratch space comes from the
@@ -76,17 +88,22 @@ typedef struct {
   int32_t act_dtype;        /* vdn_dtype (F32 or BF16) of text_kv, gates, w_out,
                                residual, out and the linear branch's q, k, v */
   float q_scale, k_scale, v_scale; /* per-tensor dequantisation scales (> 0); FP8 only */
-  int32_t linear_variant;   /* 0 = additive state, identity feature map (the only one) */
+  int32_t linear_variant;   /* 0 = additive state, identity feature map;
+                               1 = frame-wise delta rule (act_dtype BF16, head_dim 64/128) */
+  float delta_beta;         /* variant 1: step size in (0, 1]; ignored by variant 0 */
 } vdn_hybrid_cfg;
 
 /* Byte offsets of the intermediate tensors inside the workspace.  They are exported so
  * that tests can read the per-step results of one vdn_hybrid_attn_fwd call. */
 typedef struct {
   size_t frame_states;  /* float32 [F, H, d, d]: k^T v summed over each frame's tokens;
-                           anchor frames hold zeros */
-  size_t text_state;    /* float32 [H, d, d]: k^T v summed over the text tokens */
-  size_t fwd_states;    /* float32 [nC, H, d, d]: text/2 + frames before chunk c's window */
-  size_t bwd_states;    /* float32 [nC, H, d, d]: text/2 + frames after chunk c's window */
+                           anchor frames hold zeros (variant 0; unused by variant 1) */
+  size_t text_state;    /* float32 [H, d, d]: k^T v summed over the text tokens (variant 1:
+                           the delta update of a zero state with the text) */
+  size_t fwd_states;    /* float32 [nC, H, d, d]: text/2 + frames before chunk c's window
+                           (variant 1: the forward recurrence's state there) */
+  size_t bwd_states;    /* float32 [nC, H, d, d]: text/2 + frames after chunk c's window
+                           (variant 1: the backward recurrence's state there) */
   size_t branch_out;    /* act_dtype [N, 2*H*d]: row n = gated softmax output of token n
                            (heads concatenated) followed by its gated linear output */
   size_t value_stage;   /* FP8 only, bf16 [N + L, H, d]: the value codes converted to bf16,
@@ -128,7 +145,8 @@ vdn_status vdn_hybrid_attn_workspace_layout(const vdn_hybrid_cfg* cfg,
  *
  * Steps, all enqueued on `stream`: per-frame and text state build; forward/backward
  * state scan; linear read + RMSNorm + gate; block-sparse softmax + gate; one GEMM for both
- * projections with the residual added.
+ * projections with the residual added.  Variant 1 replaces build and scan by the two
+ * delta recurrences (one launch).
  */
 vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                const void* text_kv, const void* gates,
@@ -149,7 +167,8 @@ vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_h
 /* Per-step timing.  While enabled, vdn_hybrid_attn_fwd records HIP events on its stream
  * around each step.  vdn_profile_read waits for the recorded events and writes the summed
  * milliseconds of each step into ms[0..n_steps) (0 build, 1 scan, 2 linear read,
- * 3 softmax, 4 projection) and the number of recorded calls into *calls; it also clears
+ * 3 softmax, 4 projection; variant 1 records its recurrences as step 0 and an empty
+ * step 1) and the number of recorded calls into *calls; it also clears
  * the record.  At most 4096 calls are recorded between reads (VDN_ERR_INVALID_ARG after). */
 #define VDN_PROFILE_STEPS 5
 vdn_status vdn_profile_enable(int on);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(binding.Cfg) == 16 * 4
+    assert ctypes.sizeof(binding.Cfg) == 17 * 4
     assert ctypes.sizeof(binding.WorkspaceLayout) == 9 * ctypes.sizeof(ctypes.c_size_t)
 
 
@@ -67,12 +67,26 @@ BAD = [
     (dict(neighbor_chunks=0), INVALID, "neighbor_chunks"),
     (dict(rms_eps=0.0), INVALID, "rms_eps"),
     (dict(softmax_scale=-1.0), INVALID, "softmax_scale"),
-    (dict(linear_variant=1), UNSUPPORTED, "linear_variant"),
+    (dict(linear_variant=2), UNSUPPORTED, "linear_variant"),
+    (dict(linear_variant=1, delta_beta=0.0), INVALID, "delta_beta"),
+    (dict(linear_variant=1, delta_beta=1.5), INVALID, "delta_beta"),
+    (dict(linear_variant=1, delta_beta=float("nan")), INVALID, "delta_beta"),
     (dict(head_dim=96), UNSUPPORTED, "head_dim"),
     (dict(head_dim=32), UNSUPPORTED, "head_dim"),  # bf16 path
     (dict(act_dtype=binding.F32), UNSUPPORTED, "dtype"),
     (dict(frames=5 * 33), UNSUPPORTED, "chunks"),
 ]
+
+
+def test_delta_variant_needs_bf16_activations():
+    cfg = binding.make_cfg(shapes.TOY)  # f32
+    cfg.linear_variant, cfg.delta_beta = 1, 0.5
+    with pytest.raises(binding.VdnError) as e:
+        binding.workspace_layout(cfg)
+    assert e.value.status == UNSUPPORTED and "linear_variant 1" in binding.last_error()
+    cfg = binding.make_cfg(shapes.MID)
+    cfg.linear_variant, cfg.delta_beta = 1, 1.0
+    assert binding.workspace_bytes(cfg) == binding.workspace_bytes(binding.make_cfg(shapes.MID))
 
 
 @pytest.mark.parametrize("change,status,word", BAD, ids=[b[2] + str(i) for i, b in enumerate(BAD)])

@@ -38,7 +38,7 @@ class Cfg(ctypes.Structure):
                 ("chunk_frames", ctypes.c_int32), ("neighbor_chunks", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("qkv_dtype", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float), ("linear_variant", ctypes.c_int32)]
+                ("v_scale", ctypes.c_float), ("linear_variant", ctypes.c_int32), ("delta_beta", ctypes.c_float)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -88,7 +88,7 @@ def make_cfg(shape: LayerShape, q_scale: float = 1.0, k_scale: float = 1.0, v_sc
              softmax_scale: float = 0.0) -> Cfg:
     return Cfg(shape.frames, shape.tokens_per_frame, shape.heads, shape.head_dim, shape.text_len, shape.dmodel,
                shape.chunk_frames, shape.neighbor_chunks, softmax_scale, shape.rms_eps, _DT[shape.qkv_dtype],
-               _DT[shape.act_dtype], q_scale, k_scale, v_scale, 0)
+               _DT[shape.act_dtype], q_scale, k_scale, v_scale, shape.linear_variant, shape.delta_beta)
 
 
 def workspace_bytes(cfg: Cfg) -> int:

@@ -49,8 +49,14 @@ vdn_status check_cfg(const vdn_hybrid_cfg* c) {
   if (!(c->rms_eps > 0.0f) || !isfinite(c->rms_eps)) return fail(VDN_ERR_INVALID_ARG, "rms_eps must be > 0");
   if (!(c->softmax_scale >= 0.0f) || !isfinite(c->softmax_scale))
     return fail(VDN_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (c->linear_variant != 0) return fail(VDN_ERR_UNSUPPORTED, "linear_variant %d is not built", c->linear_variant);
+  if (c->linear_variant != 0 && c->linear_variant != 1)
+    return fail(VDN_ERR_UNSUPPORTED, "linear_variant %d is not built", c->linear_variant);
   const int qd = c->qkv_dtype, ad = c->act_dtype;
+  if (c->linear_variant == 1) {
+    if (!(c->delta_beta > 0.0f && c->delta_beta <= 1.0f))
+      return fail(VDN_ERR_INVALID_ARG, "delta_beta must lie in (0, 1] for linear_variant 1");
+    if (ad != VDN_BF16) return fail(VDN_ERR_UNSUPPORTED, "linear_variant 1 needs act_dtype BF16");
+  }
   const bool f32 = qd == VDN_F32 && ad == VDN_F32;
   const bool bf16 = qd == VDN_BF16 && ad == VDN_BF16;
   const bool fp8 = qd == VDN_FP8_E4M3 && ad == VDN_BF16;
@@ -255,27 +261,36 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
   auto mark = [&](int i) { if (ev) hipEventRecord(ev[i], stream); };
 
   hipError_t e = hipSuccess;
+  const bool delta = cfg->linear_variant == 1;
   mark(0);
-  if (bf16) {
-    BuildArgs<__bf16> ba{(const __bf16*)kl, (const __bf16*)vl, (const __bf16*)tk, (const __bf16*)tv, S, St, g};
-    e = launch_build_bf16(ba, stream);
+  if (delta) {
+    DeltaArgs da{(const __bf16*)kl, (const __bf16*)vl, (const __bf16*)tk, (const __bf16*)tv, St, Sf, Sb, g,
+                 cfg->delta_beta};
+    e = launch_delta_bf16(da, stream);
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "delta recurrence launch: %s", hipGetErrorString(e));
+    mark(1);
   } else {
-    BuildArgs<float> ba{(const float*)kl, (const float*)vl, (const float*)tk, (const float*)tv, S, St, g};
-    e = launch_build_f32(ba, stream);
+    if (bf16) {
+      BuildArgs<__bf16> ba{(const __bf16*)kl, (const __bf16*)vl, (const __bf16*)tk, (const __bf16*)tv, S, St, g};
+      e = launch_build_bf16(ba, stream);
+    } else {
+      BuildArgs<float> ba{(const float*)kl, (const float*)vl, (const float*)tk, (const float*)tv, S, St, g};
+      e = launch_build_f32(ba, stream);
+    }
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "state build launch: %s", hipGetErrorString(e));
+    mark(1);
+    ScanArgs sa{S, St, Sf, Sb, g, (int64_t)(g.H * (size_t)g.d * g.d / 4)};
+    e = launch_scan(sa, stream);
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   }
-  if (e != hipSuccess) return fail(VDN_ERR_HIP, "state build launch: %s", hipGetErrorString(e));
-  mark(1);
-  ScanArgs sa{S, St, Sf, Sb, g, (int64_t)(g.H * (size_t)g.d * g.d / 4)};
-  e = launch_scan(sa, stream);
-  if (e != hipSuccess) return fail(VDN_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   mark(2);
   if (bf16) {
     ReadoutArgs<__bf16> ra{(const __bf16*)ql, Sf, Sb, St, (const __bf16*)gl, rms_weight, (__bf16*)acat, u_lin_dbg, g,
-                           cfg->rms_eps};
+                           cfg->rms_eps, delta ? 1 : 0};
     e = launch_readout_bf16(ra, stream);
   } else {
     ReadoutArgs<float> ra{(const float*)ql, Sf, Sb, St, (const float*)gl, rms_weight, (float*)acat, u_lin_dbg, g,
-                          cfg->rms_eps};
+                          cfg->rms_eps, 0};
     e = launch_readout_f32(ra, stream);
   }
   if (e != hipSuccess) return fail(VDN_ERR_HIP, "linear read launch: %s", hipGetErrorString(e));

@@ -86,6 +86,24 @@ struct ReadoutArgs {
   float* u_dbg;        // nullable [N,H,d]
   Geo geo;
   float eps;
+  int phi_q;           // 1: the query is L2-normalised first (delta-rule variant)
+};
+
+// Epsilon of the delta-rule feature map phi(x) = x / sqrt(|x|^2 + eps).
+constexpr float kEpsPhi = 1e-6f;
+
+// Delta-rule recurrences (linear variant 1): writes the text state and the forward and
+// backward states at every chunk's window edges.
+struct DeltaArgs {
+  const __bf16* k;   // [N,H,d] linear-branch keys
+  const __bf16* v;   // [N,H,d]
+  const __bf16* tk;  // [L,H,d]
+  const __bf16* tv;
+  float* Stext;      // [H,d,d]
+  float* Sfwd;       // [nC,H,d,d]
+  float* Sbwd;       // [nC,H,d,d]
+  Geo geo;
+  float beta;
 };
 
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);
@@ -97,6 +115,7 @@ hipError_t launch_build_f32(const BuildArgs<float>& a, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_readout_bf16(const ReadoutArgs<__bf16>& a, hipStream_t stream);
 hipError_t launch_readout_f32(const ReadoutArgs<float>& a, hipStream_t stream);
+hipError_t launch_delta_bf16(const DeltaArgs& a, hipStream_t stream);
 hipError_t launch_membership(const Geo& g, int8_t* codes_dev, hipStream_t stream);
 
 // Largest chunk count the scan kernel keeps in registers.

@@ -201,6 +201,18 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
 #pragma unroll
     for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
 
+    // delta-rule variant: u = phi(q).S with phi(q) = q / sqrt(|q|^2 + eps); the lane and
+    // its partner (lane +- 32) hold the two halves of token `tok`'s channels
+    float qscale = 1.0f;
+    if (a.phi_q) {
+      float qq = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qq += (float)qreg[s][e] * (float)qreg[s][e];
+      qscale = 1.0f / sqrtf(pair_sum(qq) + kEpsPhi);
+    }
+
     f32x16 u[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -216,6 +228,10 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
         u[dt] = mfma32x32x16(lo, qreg[ks], u[dt]);
         u[dt] = mfma32x32x16(hi, qreg[ks], u[dt]);
       }
+    }
+    if (a.phi_q) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) u[dt] *= qscale;
     }
     // lane holds channels 32 dt + 8 i + 4 half + e of token `tok`
     float ss = 0.0f;

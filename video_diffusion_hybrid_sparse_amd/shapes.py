@@ -29,6 +29,8 @@ class LayerShape:
     input_scale: float = 1.0  # q/k/v/text draws are multiplied by this before rounding
     seed: int = 0
     rms_eps: float = 1e-6
+    linear_variant: int = 0  # 0 additive states, 1 frame-wise delta rule
+    delta_beta: float = 0.5  # delta-rule step size (variant 1)
 
     @property
     def tokens(self) -> int:
