@@ -9,11 +9,16 @@ Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole layer; per-st
 kernel times come from HIP events the library records on its stream during the timed
 steps.  The CPU baseline times the fp64 oracle on a bounded sample of the same layer.
 
+With --linear-variant 1 the linear branch is the frame-wise delta rule (step size
+--delta-beta) instead of the additive states; the line then describes that layer.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--linear-variant 0|1] [--delta-beta B]
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -93,6 +98,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--linear-variant", type=int, default=0, choices=(0, 1))
+    ap.add_argument("--delta-beta", type=float, default=0.5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the layer is not sharded across GPUs (asked for --gpus {args.gpus})",
@@ -104,6 +111,8 @@ def main() -> int:
     from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth, workload
 
     shape = shapes.P768
+    if args.linear_variant == 1:
+        shape = dataclasses.replace(shape, name=f"{shape.name}_delta", linear_variant=1, delta_beta=args.delta_beta)
     log("bench: generating inputs", shape.name)
     inp = synth.make_inputs(shape)
     dl = runner.upload(inp)
@@ -146,9 +155,10 @@ def main() -> int:
         "config": {"workload": shape.name, "frames": shape.frames, "tokens_per_frame": shape.tokens_per_frame,
                    "heads": shape.heads, "head_dim": shape.head_dim, "text_len": shape.text_len,
                    "chunk_frames": shape.chunk_frames, "model_dim": shape.dmodel,
+                   "linear_variant": shape.linear_variant,
                    "layer_tflop": round(fl["total"] / 1e12, 3)},
         "pct_mfma_peak": round(100 * fl["total"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "softmax_bf16_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "softmax_kernel<128, false>", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": softmax_traffic()},
         "steps_ms": {k: round(v, 4) for k, v in per.items()},
@@ -156,11 +166,12 @@ def main() -> int:
             "softmax_tflops": round(achieved, 1),
             "projection_tflops": round(fl["projection"] / (per["projection"] * 1e-3) / 1e12, 1),
             "state_build_gbs": round(by["state_build"] / (per["state_build"] * 1e-3) / 1e9, 1),
-            "state_scan_gbs": round(by["state_scan"] / (per["state_scan"] * 1e-3) / 1e9, 1),
+            "state_build_tflops": round(fl["state_build"] / (per["state_build"] * 1e-3) / 1e12, 2),
+            "state_scan_gbs": round(by["state_scan"] / max(per["state_scan"], 1e-6) / 1e6, 1),
             "linear_read_gbs": round(by["linear_read"] / (per["linear_read"] * 1e-3) / 1e9, 1),
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and shape.linear_variant == 0:
         log("bench: cpu baseline (oracle on a sample)")
         res["cpu_baseline"] = cpu_baseline(shape, inp)
     print(json.dumps(res), flush=True)

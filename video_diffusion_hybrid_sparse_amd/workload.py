@@ -5,7 +5,10 @@ Counts what the method must do, not what a kernel happens to do:
   per head; exp/max are not counted;
 * state build: 2 T d^2 per non-anchor frame and head, plus 2 L d^2 per head for text;
 * linear read: 2 d^2 per query token and head (one read of the summed state);
-* projections: 2 N (2 H d) D.
+* projections: 2 N (2 H d) D;
+* delta-rule variant (linear_variant 1), in place of build and scan: per direction,
+  4 d^2 per frame token and head (Khat S and Khat^T R) and 2 d^2 per text token and head
+  (the text block starts from a zero state); keys and values are read once per direction.
 Key-set sizes follow the layer's geometry (chunk windows clipped at the clip ends, two
 anchor frames that read everything, all text tokens), counted here independently.
 """
@@ -37,8 +40,12 @@ def pairs_per_head(s: LayerShape) -> int:
 
 def flops(s: LayerShape) -> dict:
     H, d, T, L, N, D, F = s.heads, s.head_dim, s.tokens_per_frame, s.text_len, s.tokens, s.dmodel, s.frames
+    if s.linear_variant == 1:
+        build = 2 * (4 * d * d * H * T * (F - 2) + 2 * d * d * H * L)
+    else:
+        build = 2 * d * d * H * (T * (F - 2) + L)
     f = dict(softmax=4 * d * H * pairs_per_head(s),
-             state_build=2 * d * d * H * (T * (F - 2) + L),
+             state_build=build,
              state_scan=0,
              linear_read=2 * d * d * H * N,
              projection=2 * N * 2 * H * d * D)
@@ -52,9 +59,15 @@ def bytes_moved(s: LayerShape) -> dict:
     a = 4 if s.act_dtype == "f32" else 2
     qb = {"f32": 4, "bf16": 2, "fp8": 1}[s.qkv_dtype]
     st = H * d * d * 4
+    if s.linear_variant == 1:
+        build = 2 * 2 * ((F - 2) * T + L) * H * d * a + 2 * nC * st + st
+        scan = 0
+    else:
+        build = 2 * ((F - 2) * T + L) * H * d * a + (F + 1) * st
+        scan = (F - 2) * st + st + 2 * nC * st
     return dict(
-        state_build=2 * ((F - 2) * T + L) * H * d * a + (F + 1) * st,
-        state_scan=(F - 2) * st + st + 2 * nC * st,
+        state_build=build,
+        state_scan=scan,
         linear_read=3 * N * H * d * a + 2 * nC * st + st,
         softmax=3 * N * H * d * qb + 2 * L * H * d * a + 2 * N * H * d * a,
         projection=(N * 2 * H * d + D * 2 * H * d + 2 * N * D) * a,
