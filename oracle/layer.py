@@ -264,3 +264,124 @@ def layer(q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, frames: int,
     out = project(a_s, a_l, w_s, w_l, x)
     return dict(codes=sets.code_matrix(frames, chunk_frames, neighbor_chunks),
                 o_soft=o_soft, u=u, a_s=a_s, a_l=a_l, out=out)
+
+
+# ---- backward (gradient of sum(out * dout) with respect to every input) ---------------
+
+def softmax_branch_backward(q, k, v, text_k, text_v, d_o, frames: int, chunk_frames: int,
+                            neighbor_chunks: int = 1, scale: float | None = None):
+    """Gradients of sum(o_soft * d_o) for the softmax branch: (dq, dk, dv, dtext_k, dtext_v).
+
+    Per query n and head h, with keys K (text then the frames of its key set), P = softmax
+    (scale q K^T) and o = P V: dV_j += P_j d_o, dP_j = d_o . v_j,
+    dS_j = P_j (dP_j - sum_i P_i dP_i), dq += scale sum_j dS_j k_j, dK_j += scale dS_j q.
+    """
+    q, k, v, text_k, text_v, d_o = map(_f64, (q, k, v, text_k, text_v, d_o))
+    N, H, d = q.shape
+    L = text_k.shape[0]
+    T = N // frames
+    scale = d ** -0.5 if scale is None else scale
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dtk, dtv = np.zeros_like(text_k), np.zeros_like(text_v)
+    for f in range(frames):
+        rows = np.arange(f * T, (f + 1) * T)
+        idx = frame_tokens(sets.softmax_frames(f, frames, chunk_frames, neighbor_chunks), T)
+        keys = np.concatenate([text_k, k[idx]], axis=0)
+        vals = np.concatenate([text_v, v[idx]], axis=0)
+        for h in range(H):
+            s = scale * (q[rows, h] @ keys[:, h].T)
+            s -= s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            dov = d_o[rows, h]
+            dvals = p.T @ dov
+            dp = dov @ vals[:, h].T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[rows, h] += scale * (ds @ keys[:, h])
+            dkeys = scale * (ds.T @ q[rows, h])
+            dtk[:, h] += dkeys[:L]
+            dtv[:, h] += dvals[:L]
+            np.add.at(dk[:, h], idx, dkeys[L:])
+            np.add.at(dv[:, h], idx, dvals[L:])
+    return dq, dk, dv, dtk, dtv
+
+
+def linear_branch_backward(q, k, v, text_k, text_v, du, frames: int, chunk_frames: int,
+                           neighbor_chunks: int = 1):
+    """Gradients of sum(u * du) for the additive linear branch: (dq, dk, dv, dtext_k, dtext_v).
+
+    u_n = q_n (S_fwd[f] + S_bwd[f]); S_fwd[f] = Tx/2 + sum_{Fw(f)} S_g, S_bwd[f] = Tx/2 +
+    sum_{Bw(f)} S_g; S_g = sum_t k_t^T v_t, Tx = sum_l tk_l^T tv_l.
+    """
+    q, k, v, text_k, text_v, du = map(_f64, (q, k, v, text_k, text_v, du))
+    N, H, d = q.shape
+    T = N // frames
+    S = frame_states(k, v, frames)
+    Tx = text_state(text_k, text_v)
+    fwd, bwd = side_states(S, Tx, frames, chunk_frames, neighbor_chunks)
+    dq = np.zeros_like(q)
+    dS = np.zeros_like(S)
+    dTx = np.zeros_like(Tx)
+    for f in range(frames):
+        rows = np.arange(f * T, (f + 1) * T)
+        for h in range(H):
+            dq[rows, h] = du[rows, h] @ (fwd[f, h] + bwd[f, h]).T
+            dside = q[rows, h].T @ du[rows, h]  # gradient of both side states of frame f
+            dTx[h] += dside                     # Tx/2 in each of the two
+            for g in sets.forward_frames(f, frames, chunk_frames, neighbor_chunks):
+                dS[g, h] += dside
+            for g in sets.backward_frames(f, frames, chunk_frames, neighbor_chunks):
+                dS[g, h] += dside
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    for g in range(frames):
+        rows = np.arange(g * T, (g + 1) * T)
+        if sets.is_anchor(g, frames):
+            continue
+        for h in range(H):
+            dk[rows, h] = v[rows, h] @ dS[g, h].T
+            dv[rows, h] = k[rows, h] @ dS[g, h]
+    dtk, dtv = np.zeros_like(text_k), np.zeros_like(text_v)
+    for h in range(H):
+        dtk[:, h] = text_v[:, h] @ dTx[h].T
+        dtv[:, h] = text_k[:, h] @ dTx[h]
+    return dq, dk, dv, dtk, dtv
+
+
+def layer_backward(q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, dout, frames: int,
+                   chunk_frames: int, neighbor_chunks: int = 1, eps: float = 1e-6,
+                   scale: float | None = None) -> dict:
+    """Gradients of sum(out * dout) for the layer (additive linear branch, shared q/k/v).
+
+    Returns dq, dk, dv, dtext_k, dtext_v, dg_s, dg_l, dw_rms, dw_s, dw_l, dx, and the
+    intermediate d_o (gradient of o_soft) and du (gradient of u).
+    """
+    q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, dout = map(
+        _f64, (q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, dout))
+    N, H, d = q.shape
+    o_soft = softmax_branch(q, k, v, text_k, text_v, frames, chunk_frames, neighbor_chunks, scale)
+    u = linear_branch(q, k, v, text_k, text_v, frames, chunk_frames, neighbor_chunks)
+    ss, sl = sigmoid(g_s), sigmoid(g_l)
+    rho = 1.0 / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    rhat = u * rho
+    a_s = ss * o_soft
+    a_l = sl * rhat * w_rms
+    # out = x + a_s W_s^T + a_l W_l^T
+    da_s = (dout @ w_s).reshape(N, H, d)
+    da_l = (dout @ w_l).reshape(N, H, d)
+    dw_s = dout.T @ a_s.reshape(N, H * d)
+    dw_l = dout.T @ a_l.reshape(N, H * d)
+    # gates
+    d_o = da_s * ss
+    dg_s = da_s * o_soft * ss * (1.0 - ss)
+    dr = da_l * sl
+    dg_l = da_l * rhat * w_rms * sl * (1.0 - sl)
+    # RMSNorm: r = rhat w, rhat = u rho
+    dw_rms = np.sum(dr * rhat, axis=0)
+    drhat = dr * w_rms
+    du = rho * (drhat - rhat * np.mean(drhat * rhat, axis=-1, keepdims=True))
+    sq, sk, sv, stk, stv = softmax_branch_backward(q, k, v, text_k, text_v, d_o, frames, chunk_frames,
+                                                   neighbor_chunks, scale)
+    lq, lk, lv, ltk, ltv = linear_branch_backward(q, k, v, text_k, text_v, du, frames, chunk_frames,
+                                                  neighbor_chunks)
+    return dict(dq=sq + lq, dk=sk + lk, dv=sv + lv, dtext_k=stk + ltk, dtext_v=stv + ltv, dg_s=dg_s,
+                dg_l=dg_l, dw_rms=dw_rms, dw_s=dw_s, dw_l=dw_l, dx=dout.copy(), d_o=d_o, du=du)
