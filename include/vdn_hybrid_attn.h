@@ -156,6 +156,33 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                float* o_soft_dbg, float* u_lin_dbg,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace of one vdn_hybrid_attn_bwd call, or 0 if cfg is invalid or the backward is not
+ * built for it (then vdn_last_error() says why). */
+size_t vdn_hybrid_attn_bwd_workspace_bytes(const vdn_hybrid_cfg* cfg);
+
+/*
+ * Backward pass of the layer: gradients of sum(out * dout) with respect to every input
+ * (the article's layer as in vdn_hybrid_attn_fwd; built for linear_variant 0 with
+ * qkv_dtype = act_dtype = BF16 and head_dim 64 or 128, else VDN_ERR_UNSUPPORTED).
+ *
+ *   q .. w_out   the forward's inputs, same layouts (q, k, v feed both branches; no
+ *                qkv_lin).  The forward is recomputed inside; its residual is not needed.
+ *   dout         [N, D] bf16: gradient of out.  The residual's gradient is dout itself.
+ *   dqkv         [3, N, H, d] float32: dq, dk, dv (written).
+ *   dtext_kv     [2, L, H, d] float32: gradients of the text keys, values (NULL if L == 0).
+ *   dgates       [2, N, H, d] float32: gradients of the softmax and linear gate logits.
+ *   drms_weight  [H, d] float32.
+ *   dw_out       [D, 2*H*d] float32: gradient of w_out (W_s columns then W_l columns).
+ *   workspace    device memory of at least vdn_hybrid_attn_bwd_workspace_bytes(cfg) bytes.
+ * All outputs are overwritten; argument checks and errors as for vdn_hybrid_attn_fwd.
+ * The result is deterministic (no atomics).
+ */
+vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, const void* text_kv,
+                               const void* gates, const float* rms_weight, const void* w_out,
+                               const void* dout, const vdn_hybrid_cfg* cfg, float* dqkv,
+                               float* dtext_kv, float* dgates, float* drms_weight, float* dw_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Membership export: runs, on the current device, the same index functions the kernels
  * use and writes codes_host[f * F + g] (host memory, F*F bytes) = how query frame f reads

@@ -115,6 +115,42 @@ void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
   L->total = off;
 }
 
+// Backward workspace: the forward's layout, then the recomputed forward tensors and the
+// backward's intermediates.
+struct BwdLayout {
+  vdn_workspace_layout fwd;
+  size_t o, u, lse, delta, dacat, dO, du, G, dS, dTx, dw_part, total;
+};
+
+vdn_status check_bwd_cfg(const vdn_hybrid_cfg* c) {
+  vdn_status s = check_cfg(c);
+  if (s != VDN_OK) return s;
+  if (c->linear_variant != 0) return fail(VDN_ERR_UNSUPPORTED, "the backward is built for linear_variant 0 only");
+  if (c->qkv_dtype != VDN_BF16 || c->act_dtype != VDN_BF16)
+    return fail(VDN_ERR_UNSUPPORTED, "the backward is built for bf16 q/k/v and activations only");
+  return VDN_OK;
+}
+
+void bwd_layout_of(const vdn_hybrid_cfg* c, BwdLayout* B) {
+  layout_of(c, &B->fwd);
+  const size_t H = c->heads, d = c->head_dim, N = (size_t)c->frames * c->tokens_per_frame;
+  const size_t nC = (c->frames + c->chunk_frames - 1) / c->chunk_frames, ng = nC + 2;
+  const size_t st = H * d * d * 4, nhd = N * H * d;
+  size_t off = B->fwd.total;
+  B->o = off; off = align_up(off + nhd * 4);
+  B->u = off; off = align_up(off + nhd * 4);
+  B->lse = off; off = align_up(off + N * H * 4);
+  B->delta = off; off = align_up(off + N * H * 4);
+  B->dacat = off; off = align_up(off + 2 * nhd * 4);
+  B->dO = off; off = align_up(off + nhd * 2);
+  B->du = off; off = align_up(off + nhd * 2);
+  B->G = off; off = align_up(off + ng * st);
+  B->dS = off; off = align_up(off + nC * st);
+  B->dTx = off; off = align_up(off + st);
+  B->dw_part = off; off = align_up(off + ((N + 63) / 64) * H * d * 4);
+  B->total = off;
+}
+
 // ---- profiling ----------------------------------------------------------------------
 constexpr int kProfSlots = 4096;
 struct Prof {
@@ -176,6 +212,126 @@ vdn_status vdn_profile_read(double* ms, int n_steps, int64_t* calls) {
   }
   if (calls) *calls = used;
   g_prof.used = 0;
+  return VDN_OK;
+}
+
+size_t vdn_hybrid_attn_bwd_workspace_bytes(const vdn_hybrid_cfg* cfg) {
+  if (check_bwd_cfg(cfg) != VDN_OK) return 0;
+  BwdLayout B;
+  bwd_layout_of(cfg, &B);
+  return B.total;
+}
+
+vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
+                               const float* rms_weight, const void* w_out, const void* dout,
+                               const vdn_hybrid_cfg* cfg, float* dqkv, float* dtext_kv, float* dgates,
+                               float* drms_weight, float* dw_out, void* workspace, size_t workspace_bytes,
+                               void* stream_ptr) {
+  vdn_status s = check_bwd_cfg(cfg);
+  if (s != VDN_OK) return s;
+  const struct { const void* p; const char* name; } req[] = {
+      {q, "q"}, {k, "k"}, {v, "v"}, {gates, "gates"}, {rms_weight, "rms_weight"}, {w_out, "w_out"},
+      {dout, "dout"}, {dqkv, "dqkv"}, {dgates, "dgates"}, {drms_weight, "drms_weight"}, {dw_out, "dw_out"},
+      {workspace, "workspace"}};
+  for (const auto& r : req) {
+    if (!r.p) return fail(VDN_ERR_INVALID_ARG, "%s is NULL", r.name);
+    if (!aligned16(r.p)) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", r.name);
+  }
+  if (cfg->text_len > 0) {
+    if (!text_kv || !dtext_kv) return fail(VDN_ERR_INVALID_ARG, "text_kv and dtext_kv are required when text_len > 0");
+    if (!aligned16(text_kv) || !aligned16(dtext_kv))
+      return fail(VDN_ERR_INVALID_ARG, "text_kv / dtext_kv are not 16-byte aligned");
+  }
+  BwdLayout B;
+  bwd_layout_of(cfg, &B);
+  if (workspace_bytes < B.total)
+    return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, B.total);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  const Geo g = make_geo(cfg);
+  const size_t N = (size_t)g.F * g.T, row = (size_t)g.H * g.d, nhd = N * row;
+  char* ws = static_cast<char*>(workspace);
+  const vdn_workspace_layout& L = B.fwd;
+  float* S = reinterpret_cast<float*>(ws + L.frame_states);
+  float* St = reinterpret_cast<float*>(ws + L.text_state);
+  float* Sf = reinterpret_cast<float*>(ws + L.fwd_states);
+  float* Sb = reinterpret_cast<float*>(ws + L.bwd_states);
+  __bf16* acat = reinterpret_cast<__bf16*>(ws + L.branch_out);
+  float* O = reinterpret_cast<float*>(ws + B.o);
+  float* U = reinterpret_cast<float*>(ws + B.u);
+  float* lse = reinterpret_cast<float*>(ws + B.lse);
+  float* delta = reinterpret_cast<float*>(ws + B.delta);
+  float* dacat = reinterpret_cast<float*>(ws + B.dacat);
+  __bf16* dO = reinterpret_cast<__bf16*>(ws + B.dO);
+  __bf16* du = reinterpret_cast<__bf16*>(ws + B.du);
+  float* G = reinterpret_cast<float*>(ws + B.G);
+  float* dS = reinterpret_cast<float*>(ws + B.dS);
+  float* dTx = reinterpret_cast<float*>(ws + B.dTx);
+  float* dw_part = reinterpret_cast<float*>(ws + B.dw_part);
+  const __bf16* qb = static_cast<const __bf16*>(q);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  const __bf16* vb = static_cast<const __bf16*>(v);
+  const __bf16* tk = text_kv ? static_cast<const __bf16*>(text_kv) : qb;  // L == 0: never read
+  const __bf16* tv = text_kv ? tk + (size_t)g.L * row : qb;
+  const __bf16* gs = static_cast<const __bf16*>(gates);
+  const __bf16* gl = gs + nhd;
+  float* dq = dqkv;
+  float* dk = dqkv + nhd;
+  float* dv = dqkv + 2 * nhd;
+  float* dtk = dtext_kv;
+  float* dtv = dtext_kv ? dtext_kv + (size_t)g.L * row : nullptr;
+  const float scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / sqrtf((float)g.d);
+  const float c2 = scale * 1.4426950408889634f;
+  hipError_t e;
+#define VDN_LAUNCH(what, expr) \
+  if ((e = (expr)) != hipSuccess) return fail(VDN_ERR_HIP, what " launch: %s", hipGetErrorString(e));
+
+  // forward recompute: states, linear read (u), softmax (o and its log-sum-exp)
+  BuildArgs<__bf16> ba{kb, vb, tk, tv, S, St, g};
+  VDN_LAUNCH("state build", launch_build_bf16(ba, stream));
+  ScanArgs sa{S, St, Sf, Sb, g, (int64_t)(g.H * (size_t)g.d * g.d / 4)};
+  VDN_LAUNCH("scan", launch_scan(sa, stream));
+  ReadoutArgs<__bf16> ra{qb, Sf, Sb, St, gl, rms_weight, acat, U, g, cfg->rms_eps, 0};
+  VDN_LAUNCH("linear read", launch_readout_bf16(ra, stream));
+  SoftmaxArgs sm{q, k, vb, tk, tv, gs, acat, O, g, c2, c2, 1.0f, lse};
+  VDN_LAUNCH("softmax", launch_softmax_bf16(sm, stream));
+
+  // d[a_s | a_l] = dout W (row-major N x 2Hd) and dW = dout^T [a_s | a_l] (D x 2Hd)
+  const char* gerr = nullptr;
+  const int64_t K2 = (int64_t)(2 * row), Dm = cfg->model_dim;
+  if (gemm_bf16_f32out(false, false, K2, (int64_t)N, Dm, w_out, K2, dout, Dm, dacat, K2, ws + L.gemm_ws,
+                       L.gemm_ws_bytes, stream, &gerr) != 0)
+    return fail(VDN_ERR_HIP, "backward GEMM (branch outputs): %s", gerr);
+  if (gemm_bf16_f32out(false, true, K2, Dm, (int64_t)N, acat, K2, dout, Dm, dw_out, K2, ws + L.gemm_ws,
+                       L.gemm_ws_bytes, stream, &gerr) != 0)
+    return fail(VDN_ERR_HIP, "backward GEMM (weights): %s", gerr);
+
+  // gates, RMSNorm
+  EpiBwdArgs ea{dacat, gs, gl, O, U, rms_weight, dO, du, dgates, dgates + nhd, delta, dw_part, drms_weight, g,
+                cfg->rms_eps};
+  VDN_LAUNCH("epilogue backward", launch_epi_bwd(ea, stream));
+  // softmax branch: dq, dk, dv, text (stored)
+  SoftmaxBwdArgs sb{qb, kb, vb, tk, tv, dO, lse, delta, dq, dk, dv, dtk, dtv, g, c2, scale};
+  VDN_LAUNCH("softmax backward", launch_softmax_bwd(sb, stream));
+  // linear branch (accumulated)
+  BuildArgs<__bf16> ga{qb, du, tk, tv, G, nullptr, g, 1};
+  VDN_LAUNCH("group state gradients", launch_build_bf16(ga, stream));
+  VDN_LAUNCH("state gradient mix", launch_lin_mix(G, dS, dTx, g, stream));
+  TokenStateArgs<__bf16> t_dq{du, Sf, Sb, St, dq, g, 0};
+  VDN_LAUNCH("linear dq", launch_token_state(t_dq, true, stream));
+  TokenStateArgs<__bf16> t_dk{vb, dS, nullptr, nullptr, dk, g, 0};
+  VDN_LAUNCH("linear dk", launch_token_state(t_dk, true, stream));
+  TokenStateArgs<__bf16> t_dv{kb, dS, nullptr, nullptr, dv, g, 0};
+  VDN_LAUNCH("linear dv", launch_token_state(t_dv, false, stream));
+  if (g.L > 0) {
+    TokenStateArgs<__bf16> t_tk{tv, dTx, nullptr, nullptr, dtk, g, 1};
+    VDN_LAUNCH("linear text dk", launch_token_state(t_tk, true, stream));
+    TokenStateArgs<__bf16> t_tv{tk, dTx, nullptr, nullptr, dtv, g, 1};
+    VDN_LAUNCH("linear text dv", launch_token_state(t_tv, false, stream));
+  }
+#undef VDN_LAUNCH
   return VDN_OK;
 }
 
@@ -304,11 +460,11 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
     e = launch_dequant_values(da, stream);
     if (e != hipSuccess) return fail(VDN_ERR_HIP, "value staging launch: %s", hipGetErrorString(e));
     SoftmaxArgs sm{q, k, vst, (const __bf16*)tk, tvst, (const __bf16*)gs, (__bf16*)acat, o_soft_dbg, g,
-                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale};
+                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale, nullptr};
     e = launch_softmax_fp8(sm, stream);
   } else if (bf16) {
     SoftmaxArgs sm{q, k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv, (const __bf16*)gs, (__bf16*)acat,
-                   o_soft_dbg, g, c2, c2, 1.0f};
+                   o_soft_dbg, g, c2, c2, 1.0f, nullptr};
     e = launch_softmax_bf16(sm, stream);
   } else {
     SoftmaxF32Args sm{(const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,

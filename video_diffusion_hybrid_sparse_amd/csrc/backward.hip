@@ -1,0 +1,621 @@
+// Backward pass of the hybrid attention layer (additive linear branch), bf16 inputs.
+//
+// Gradient of sum(out * dout) with respect to q, k, v, the text keys and values, both
+// gate logits, the RMSNorm weight and the output projection, for the layer of the
+// VDN-MiniMax-H3 article (modelscope.csdn.net), sections "局部精确计算，远程线性记忆" and
+// "独立门控，融合两条注意力分支".  The forward is recomputed first (softmax output and its
+// log-sum-exp, the linear read u, the gated branch outputs); then, in stream order:
+//   1. d[a_s | a_l] = dout W and dW = dout^T [a_s | a_l]      (library GEMMs);
+//   2. epilogue backward per (token, head): dO, Delta = dO . O, dg_s, dg_l, du and the
+//      RMSNorm weight gradient (per-block partial sums, reduced in a second kernel);
+//   3. softmax backward, block-sparse as the forward: dQ per query tile walking its key
+//      segments, dK/dV per key tile walking the queries that read it (the mirror image
+//      of the key sets: a chunk's key segments are the queries of its frames' keys);
+//   4. linear backward: dq += du (S_fwd + S_bwd)^T; per query group the state gradient
+//      sum q^T du; each chunk's frame-state gradient is the sum of the group gradients of
+//      the chunks whose window excludes it, the text state's the sum of all of them;
+//      dk += v dS^T, dv += k dS per token.
+#include "kernels.h"
+
+namespace vdn {
+
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ float sig(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace
+
+// ---- 2. epilogue backward -----------------------------------------------------------
+// One workgroup = 64 tokens of one head; 8 groups of 32 lanes, one token at a time per
+// group, D/32 channels per lane.
+template <int D>
+__global__ __launch_bounds__(256) void epi_bwd_kernel(EpiBwdArgs a) {
+  constexpr int CPL = D / 32;
+  __shared__ float red[8][D];
+  const Geo g = a.geo;
+  const int h = blockIdx.y, blk = blockIdx.x;
+  const int tid = threadIdx.x, grp = tid >> 5, l = tid & 31;
+  const int N = g.F * g.T;
+  const size_t rs = (size_t)g.H * D, hd = rs;
+  float w[CPL], dwp[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    w[e] = a.w[h * D + l * CPL + e];
+    dwp[e] = 0.0f;
+  }
+  for (int t = blk * 64 + grp; t < imin(N, blk * 64 + 64); t += 8) {
+    const size_t o = (size_t)t * rs + h * D + l * CPL;
+    const float* das = a.dacat + (size_t)t * 2 * hd + h * D + l * CPL;
+    const float* dal = das + hd;
+    float dO[CPL], O[CPL], rh[CPL], dr[CPL], gl[CPL];
+    float delta = 0.0f, uu = 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const float gs = (float)a.gs[o + e], ss = sig(gs);
+      O[e] = a.o[o + e];
+      dO[e] = das[e] * ss;
+      a.dgs[o + e] = das[e] * O[e] * ss * (1.0f - ss);
+      delta += dO[e] * O[e];
+      rh[e] = a.u[o + e];
+      uu += rh[e] * rh[e];
+      gl[e] = (float)a.gl[o + e];
+    }
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) {
+      delta += __shfl_xor(delta, m, 32);
+      uu += __shfl_xor(uu, m, 32);
+    }
+    const float rho = 1.0f / sqrtf(uu / D + a.eps);
+    float sdr = 0.0f;  // sum over channels of (dr w) rhat
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      rh[e] *= rho;
+      const float sl = sig(gl[e]);
+      dr[e] = dal[e] * sl;
+      a.dgl[o + e] = dal[e] * rh[e] * w[e] * sl * (1.0f - sl);
+      dwp[e] += dr[e] * rh[e];
+      sdr += dr[e] * w[e] * rh[e];
+    }
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) sdr += __shfl_xor(sdr, m, 32);
+    const float mean = sdr / D;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      a.du[o + e] = (__bf16)(rho * (dr[e] * w[e] - rh[e] * mean));
+      a.dO[o + e] = (__bf16)dO[e];
+    }
+    if (l == 0) a.delta[(size_t)t * g.H + h] = delta;
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) red[grp][l * CPL + e] = dwp[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s += red[r][tid];
+    a.dw_part[((size_t)blk * g.H + h) * D + tid] = s;
+  }
+}
+
+// RMSNorm weight gradient: sum of the per-block partials, in block order.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* part, float* dw, int nblk, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int b = 0; b < nblk; ++b) s += part[(size_t)b * n + i];
+  dw[i] = s;
+}
+
+// ---- 4. linear backward helpers -------------------------------------------------------
+// Frame-state gradient of each chunk and the text-state gradient from the per-group
+// state gradients G[grp] (grp 0, 1 the anchors, 2 + c chunk c):
+//   dS[c] = sum over chunks c' with |c' - c| > R of G[2 + c']  (frames of chunk c are in
+//           the forward or backward set of exactly those chunks' queries);
+//   dTx   = sum over all groups of G[grp]  (each side holds text/2; both sides are read).
+__global__ __launch_bounds__(256) void lin_mix_kernel(const float* G, float* dS, float* dTx, Geo g, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int ng = n_groups(g);
+  float t = 0.0f;
+  for (int grp = 0; grp < ng; ++grp) t += G[(size_t)grp * n + i];
+  dTx[i] = t;
+  for (int c = 0; c < g.nC; ++c) {
+    float s = 0.0f;
+    for (int c2 = 0; c2 < g.nC; ++c2)
+      if (c2 - c > g.R || c - c2 > g.R) s += G[(size_t)(2 + c2) * n + i];
+    dS[(size_t)c * n + i] = s;
+  }
+}
+
+// y[n] += x[n] . M (TRANS = 0) or x[n] . M^T (TRANS = 1) for the tokens of one query group
+// (or the text) and one head, M a d x d float32 matrix of that group (m0 + m1 when m1 is
+// given).  One workgroup = 32 tokens; thread = one output channel (tid % D) for a slice
+// of the tokens (tid / D); M in LDS (transposed for TRANS), the tokens' x in LDS.
+template <int D, bool TRANS, typename X>
+__global__ __launch_bounds__(256) void token_state_kernel(TokenStateArgs<X> a) {
+  constexpr int TT = 32, TPT = TT * D / 256;  // tokens per thread
+  __shared__ float M[D * D];
+  __shared__ float xs[TT][D + 4];
+  const Geo g = a.geo;
+  const int grp = blockIdx.x, h = blockIdx.y, tile = blockIdx.z, tid = threadIdx.x;
+  const int o = tid % D, th = tid / D;
+  int t0, t1;
+  if (a.text) {
+    t0 = 0;
+    t1 = g.L;
+  } else {
+    int f0, f1;
+    group_frames(g, grp, f0, f1);
+    t0 = f0 * g.T;
+    t1 = f1 * g.T;
+  }
+  const int tb = t0 + tile * TT;
+  if (tb >= t1) return;
+  // the group's matrix: text -> m0[0]; anchor groups -> m_anchor (skipped when absent);
+  // chunk groups -> m0 (+ m1) of the group's chunk
+  const bool anchor = !a.text && grp < 2;
+  if (anchor && !a.m_anchor) return;
+  const float* m0 = anchor ? a.m_anchor : a.m0;
+  const float* m1 = anchor ? nullptr : a.m1;
+  const int mi = (a.text || anchor) ? 0 : group_chunk(grp);
+  const size_t mo = ((size_t)mi * g.H + h) * D * D;
+  for (int e = tid; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;
+    float v = m0[mo + e];
+    if (m1) v += m1[mo + e];
+    if (TRANS) M[j * D + i] = v;  // M^T: y[o] = sum_m x[m] M[o][m]
+    else M[e] = v;
+  }
+  const size_t rs = (size_t)g.H * D;
+  for (int e = tid; e < TT * D; e += 256) {
+    const int t = e / D, c = e % D;
+    xs[t][c] = tb + t < t1 ? (float)a.x[(size_t)(tb + t) * rs + h * D + c] : 0.0f;
+  }
+  __syncthreads();
+  float acc[TPT];
+#pragma unroll
+  for (int t = 0; t < TPT; ++t) acc[t] = 0.0f;
+#pragma unroll 2
+  for (int m = 0; m < D; m += 4) {
+    const float w0 = M[(m + 0) * D + o], w1 = M[(m + 1) * D + o], w2 = M[(m + 2) * D + o], w3 = M[(m + 3) * D + o];
+#pragma unroll
+    for (int t = 0; t < TPT; ++t) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[th * TPT + t][m]);
+      acc[t] += xv.x * w0 + xv.y * w1 + xv.z * w2 + xv.w * w3;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TPT; ++t) {
+    const int tok = tb + th * TPT + t;
+    if (tok < t1) {
+      float* y = a.y + (size_t)tok * rs + h * D + o;
+      *y += acc[t];
+    }
+  }
+}
+
+// ---- 3a. softmax backward, dQ -----------------------------------------------------------
+// Query tiles as in the forward (256 queries of one group and head, 8 waves x 32).  Per
+// 64-key sub-tile: S^T = K Q^T and dP^T = V dO^T (K and V rows are MFMA A operands);
+// P^T = exp2(S^T c2 - lse), dS^T = P^T (dP^T - Delta) (the query is lane-local);
+// dQ^T += K^T dS^T with K^T gathered by the transposing LDS read.  dq = scale dQ.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bwd_dq_kernel(SoftmaxBwdArgs a) {
+  constexpr int BM = 256, NW = 8, BN = 64;
+  constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
+  constexpr int NI = BN * CPR / (64 * NW);
+  static_assert(NI >= 1, "stage size");
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * D];
+  const Geo g = a.geo;
+  const int per_head = count_tiles(g, BM);
+  const int total = per_head * g.H;
+  const int hid = blockIdx.x, xcd = hid & 7;
+  const int lid = xcd * (total >> 3) + imin(xcd, total & 7) + (hid >> 3);
+  const int h = lid / per_head;
+  int grp, t0, t1;
+  if (!locate_tile(g, lid - h * per_head, BM, grp, t0, t1)) return;
+  const KeySegs sg = group_keys(g, grp);
+  const int n0 = (g.L + BN - 1) / BN, n1 = (sg.l0 + BN - 1) / BN, n2 = (sg.l1 + BN - 1) / BN, n3 = (sg.l2 + BN - 1) / BN;
+  const int nst = n0 + n1 + n2 + n3;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const size_t rs = (size_t)g.H * D;
+
+  int qtok = t0 + wave * 32 + l32;
+  const bool qok = qtok < t1;
+  qtok = qok ? qtok : t1 - 1;
+  bf16x8 qreg[KS], doreg[KS];
+  {
+    const __bf16* qp = a.q + (size_t)qtok * rs + h * D + half * 8;
+    const __bf16* dp = a.dO + (size_t)qtok * rs + h * D + half * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qreg[s] = load_bf16x8(qp + 16 * s);
+      doreg[s] = load_bf16x8(dp + 16 * s);
+    }
+  }
+  const float lse = a.lse[(size_t)qtok * g.H + h];
+  const float delta = a.delta[(size_t)qtok * g.H + h];
+  const intptr_t tk_off = reinterpret_cast<intptr_t>(a.tk) - reinterpret_cast<intptr_t>(a.k);
+  const intptr_t tv_off = reinterpret_cast<intptr_t>(a.tv) - reinterpret_cast<intptr_t>(a.v);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  int lrow[NI], lcol[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    lrow[i] = (wave * NI + i) * RPI + lane / CPR;
+    lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
+  }
+  auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
+    int len, base;
+    if (j < n0) { base = 0; len = g.L; }
+    else if ((j -= n0) < n1) { base = sg.s0; len = sg.l0; }
+    else if ((j -= n1) < n2) { base = sg.s1; len = sg.l1; }
+    else { j -= n2; base = sg.s2; len = sg.l2; }
+    start = base + BN * j;
+    valid = len - BN * j;
+  };
+  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+    int start, valid;
+    stage_at(j, start, valid);
+    const bool text = j < n0;
+    const __bf16* kb = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.k) + (text ? tk_off : 0));
+    const __bf16* vb = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.v) + (text ? tv_off : 0));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const size_t row = (size_t)(start + imin(lrow[i], valid - 1));
+      load_lds16(kb + row * rs + lcol[i], &Ks[buf][(wave * NI + i) * RPI * D]);
+      load_lds16(vb + row * rs + lcol[i], &Vs[buf][(wave * NI + i) * RPI * D]);
+    }
+  };
+  int krd[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int trd[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
+      const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
+    }
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) dq[i] = 0.0f;
+  const float c2 = a.c2;
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nst; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nst) issue(j + 1, buf ^ 1);
+    int start, valid;
+    stage_at(j, start, valid);
+    const __bf16* K = Ks[buf];
+    const __bf16* V = Vs[buf];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      s[rt] = 0.0f;
+      dp[rt] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[k]), qreg[k], s[rt]);
+        dp[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(V + 32 * rt * D + krd[k]), doreg[k], dp[rt]);
+      }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int key = rt * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
+          const float p = key < valid ? __builtin_amdgcn_exp2f(s[rt][r + e] * c2 - lse) : 0.0f;
+          ds2[e] = p * (dp[rt][r + e] - delta);
+        }
+        uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
+        const uint32_t pk = pack_bf16x2(ds2[0], ds2[1]);
+        const int e = (r & 7) >> 1;
+        if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
+        pb[2 * rt + (r >> 3)] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+    for (int G = 0; G < 4; ++G)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x4 lo = lds_read_tr(K + 16 * G * D + trd[dt][0]);
+        const bf16x4 hi = lds_read_tr(K + 16 * G * D + trd[dt][1]);
+        const bf16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dq[dt] = mfma32x32x16(ka, pb[G], dq[dt]);
+      }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (qok) {
+    float* out = a.dq + (size_t)qtok * rs + h * D;
+    // lane holds channels 32 dt + 8 i + 4 half + e of its query
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(out + 32 * dt + 8 * i + 4 * half) =
+            make_float4(a.scale * dq[dt][4 * i], a.scale * dq[dt][4 * i + 1], a.scale * dq[dt][4 * i + 2],
+                        a.scale * dq[dt][4 * i + 3]);
+  }
+}
+
+// ---- 3b. softmax backward, dK and dV ----------------------------------------------------
+// One workgroup = 128 keys of one frame (or of the text) and one head, 4 waves x 32 keys.
+// The queries that read a video key frame are the key segments of its chunk's group
+// (anchor frames and text: every query).  Per 64-query sub-tile: S = Q K^T and
+// dP = dO V^T (Q and dO rows are MFMA A operands, the key is lane-local);
+// P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and dK^T += Q^T dS with dO^T
+// and Q^T gathered by the transposing LDS read.  dk = scale dK.
+template <int D>
+__global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a) {
+  constexpr int NW = 4, BK = 128, BQ = 64;
+  constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
+  constexpr int NI = BQ * CPR / (64 * NW);
+  static_assert(NI >= 1, "stage size");
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Os[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ], Dl[2][BQ];
+  const Geo g = a.geo;
+  // key tiles of one head: text tiles, then the tiles of frames 0 .. F-1; anchors' and
+  // text tiles first (they see every query)
+  const int ntt = (g.L + BK - 1) / BK, tpf = (g.T + BK - 1) / BK;
+  const int per_head = ntt + g.F * tpf;
+  const int h = blockIdx.x / per_head;
+  int kt = blockIdx.x - h * per_head;
+  bool text;
+  int kframe = -1, kstart, kvalid;
+  {
+    // order: anchor 0's tiles, anchor F-1's tiles, text tiles, then frames 1 .. F-2
+    if (kt < tpf) { text = false; kframe = 0; kstart = kt * BK; }
+    else if ((kt -= tpf) < tpf) { text = false; kframe = g.F - 1; kstart = (g.F - 1) * g.T + kt * BK; }
+    else if ((kt -= tpf) < ntt) { text = true; kstart = kt * BK; }
+    else { kt -= ntt; text = false; kframe = 1 + kt / tpf; kstart = kframe * g.T + (kt % tpf) * BK; }
+    const int end = text ? g.L : (kframe + 1) * g.T;
+    kvalid = end - kstart;
+  }
+  const KeySegs qs = group_keys(g, (text || kframe == 0 || kframe == g.F - 1) ? 0 : 2 + kframe / g.C);
+  const int n1 = (qs.l0 + BQ - 1) / BQ, n2 = (qs.l1 + BQ - 1) / BQ, n3 = (qs.l2 + BQ - 1) / BQ;
+  const int nst = n1 + n2 + n3;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const size_t rs = (size_t)g.H * D;
+
+  int ktok = kstart + wave * 32 + l32;
+  const bool kok = wave * 32 + l32 < kvalid;
+  ktok = kok ? ktok : kstart + kvalid - 1;
+  const __bf16* kbase = text ? a.tk : a.k;
+  const __bf16* vbase = text ? a.tv : a.v;
+  bf16x8 kreg[KS], vreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kreg[s] = load_bf16x8(kbase + (size_t)ktok * rs + h * D + half * 8 + 16 * s);
+    vreg[s] = load_bf16x8(vbase + (size_t)ktok * rs + h * D + half * 8 + 16 * s);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  int lrow[NI], lcol[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    lrow[i] = (wave * NI + i) * RPI + lane / CPR;
+    lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
+  }
+  auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
+    int len, base;
+    if (j < n1) { base = qs.s0; len = qs.l0; }
+    else if ((j -= n1) < n2) { base = qs.s1; len = qs.l1; }
+    else { j -= n2; base = qs.s2; len = qs.l2; }
+    start = base + BQ * j;
+    valid = len - BQ * j;
+  };
+  // per-query lse and Delta of the next sub-tile: loaded into registers before its
+  // HBM -> LDS copies (so waiting for them does not wait for the copies), written to LDS
+  // at the end of the current sub-tile
+  float lse_next = 0.0f, delta_next = 0.0f;
+  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+    int start, valid;
+    stage_at(j, start, valid);
+    if (tid < BQ) {
+      const int row = start + imin(tid, valid - 1);
+      lse_next = a.lse[(size_t)row * g.H + h];
+      delta_next = a.delta[(size_t)row * g.H + h];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const size_t row = (size_t)(start + imin(lrow[i], valid - 1));
+      load_lds16(a.q + row * rs + lcol[i], &Qs[buf][(wave * NI + i) * RPI * D]);
+      load_lds16(a.dO + row * rs + lcol[i], &Os[buf][(wave * NI + i) * RPI * D]);
+    }
+  };
+  auto put_stats = [&](int buf) __attribute__((always_inline)) {
+    if (tid < BQ) {
+      Ls[buf][tid] = lse_next;
+      Dl[buf][tid] = delta_next;
+    }
+  };
+  int qrd[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) qrd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int trd[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
+      const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
+    }
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) {
+    dk[i] = 0.0f;
+    dv[i] = 0.0f;
+  }
+  const float c2 = a.c2;
+
+  if (nst > 0) {
+    issue(0, 0);
+    put_stats(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nst; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nst) issue(j + 1, buf ^ 1);
+    int start, valid;
+    stage_at(j, start, valid);
+    const __bf16* Q = Qs[buf];
+    const __bf16* O = Os[buf];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      s[rt] = 0.0f;
+      dp[rt] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Q + 32 * rt * D + qrd[k]), kreg[k], s[rt]);
+        dp[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(O + 32 * rt * D + qrd[k]), vreg[k], dp[rt]);
+      }
+    // accumulator row = query 32 rt + 8 (r/4) + 4 half + r%4 of the sub-tile
+    bf16x8 pb[4], sb[4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int q0 = rt * 32 + 8 * r4 + 4 * half;
+        const float4 lv = *reinterpret_cast<const float4*>(&Ls[buf][q0]);
+        const float4 dv4 = *reinterpret_cast<const float4*>(&Dl[buf][q0]);
+        const float lq[4] = {lv.x, lv.y, lv.z, lv.w}, dq4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          p[e] = q0 + e < valid ? __builtin_amdgcn_exp2f(s[rt][r] * c2 - lq[e]) : 0.0f;
+          ds[e] = p[e] * (dp[rt][r] - dq4[e]);
+        }
+        uint4 wp = __builtin_bit_cast(uint4, pb[2 * rt + (r4 >> 1)]);
+        uint4 ws = __builtin_bit_cast(uint4, sb[2 * rt + (r4 >> 1)]);
+        if (r4 & 1) {
+          wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
+          ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
+        } else {
+          wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
+          ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
+        }
+        pb[2 * rt + (r4 >> 1)] = __builtin_bit_cast(bf16x8, wp);
+        sb[2 * rt + (r4 >> 1)] = __builtin_bit_cast(bf16x8, ws);
+      }
+#pragma unroll
+    for (int G = 0; G < 4; ++G)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x4 olo = lds_read_tr(O + 16 * G * D + trd[dt][0]);
+        const bf16x4 ohi = lds_read_tr(O + 16 * G * D + trd[dt][1]);
+        const bf16x8 oa = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
+        dv[dt] = mfma32x32x16(oa, pb[G], dv[dt]);
+        const bf16x4 qlo = lds_read_tr(Q + 16 * G * D + trd[dt][0]);
+        const bf16x4 qhi = lds_read_tr(Q + 16 * G * D + trd[dt][1]);
+        const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+        dk[dt] = mfma32x32x16(qa, sb[G], dk[dt]);
+      }
+    if (j + 1 < nst) put_stats(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (kok) {
+    float* ko = (text ? a.dtk : a.dk) + (size_t)ktok * rs + h * D;
+    float* vo = (text ? a.dtv : a.dv) + (size_t)ktok * rs + h * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 32 * dt + 8 * i + 4 * half;
+        *reinterpret_cast<float4*>(ko + c) = make_float4(a.scale * dk[dt][4 * i], a.scale * dk[dt][4 * i + 1],
+                                                         a.scale * dk[dt][4 * i + 2], a.scale * dk[dt][4 * i + 3]);
+        *reinterpret_cast<float4*>(vo + c) = make_float4(dv[dt][4 * i], dv[dt][4 * i + 1], dv[dt][4 * i + 2],
+                                                         dv[dt][4 * i + 3]);
+      }
+  }
+}
+
+// ---- launchers ------------------------------------------------------------------------
+hipError_t launch_epi_bwd(const EpiBwdArgs& a, hipStream_t stream) {
+  const int N = a.geo.F * a.geo.T, nblk = (N + 63) / 64;
+  dim3 grid(nblk, a.geo.H), block(256);
+  if (a.geo.d == 128) hipLaunchKernelGGL(epi_bwd_kernel<128>, grid, block, 0, stream, a);
+  else if (a.geo.d == 64) hipLaunchKernelGGL(epi_bwd_kernel<64>, grid, block, 0, stream, a);
+  else return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = a.geo.H * a.geo.d;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a.dw_part, a.dw, nblk, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_lin_mix(const float* G, float* dS, float* dTx, const Geo& g, hipStream_t stream) {
+  const int64_t n = (int64_t)g.H * g.d * g.d;
+  hipLaunchKernelGGL(lin_mix_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, G, dS, dTx, g, n);
+  return hipGetLastError();
+}
+
+template <typename X>
+hipError_t launch_token_state(const TokenStateArgs<X>& a, bool trans, hipStream_t stream) {
+  const Geo& g = a.geo;
+  const int ngrp = a.text ? 1 : n_groups(g);
+  int maxtok = a.text ? g.L : g.C * g.T;
+  if (!a.text) maxtok = imax(maxtok, g.T);
+  const int tiles = (maxtok + 31) / 32;
+  if (tiles == 0) return hipSuccess;
+  dim3 grid(ngrp, g.H, tiles), block(256);
+#define VDN_TS(DD, TR) hipLaunchKernelGGL(HIP_KERNEL_NAME(token_state_kernel<DD, TR, X>), grid, block, 0, stream, a)
+  if (g.d == 128) { if (trans) VDN_TS(128, true); else VDN_TS(128, false); }
+  else if (g.d == 64) { if (trans) VDN_TS(64, true); else VDN_TS(64, false); }
+  else return hipErrorInvalidValue;
+#undef VDN_TS
+  return hipGetLastError();
+}
+template hipError_t launch_token_state<__bf16>(const TokenStateArgs<__bf16>&, bool, hipStream_t);
+
+hipError_t launch_softmax_bwd(const SoftmaxBwdArgs& a, hipStream_t stream) {
+  const Geo& g = a.geo;
+  const int tiles = count_tiles(g, 256);
+  if (tiles > 0) {
+    dim3 grid(tiles * g.H), block(512);
+    if (g.d == 128) hipLaunchKernelGGL(softmax_bwd_dq_kernel<128>, grid, block, 0, stream, a);
+    else if (g.d == 64) hipLaunchKernelGGL(softmax_bwd_dq_kernel<64>, grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int per_head = (g.L + 127) / 128 + g.F * ((g.T + 127) / 128);
+  dim3 grid2(per_head * g.H), block2(256);
+  if (g.d == 128) hipLaunchKernelGGL(softmax_bwd_dkdv_kernel<128>, grid2, block2, 0, stream, a);
+  else hipLaunchKernelGGL(softmax_bwd_dkdv_kernel<64>, grid2, block2, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace vdn

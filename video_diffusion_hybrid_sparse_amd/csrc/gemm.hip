@@ -28,6 +28,18 @@ struct Plan {
 std::mutex g_mu;
 std::map<int, hipblasLtHandle_t> g_handles;
 std::map<std::tuple<int, int, int64_t, int64_t, int64_t, size_t>, Plan> g_plans;
+std::map<std::tuple<int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, size_t>, Plan> g_gplans;
+
+int get_handle(int dev, hipblasLtHandle_t* handle, const char** err) {
+  auto hit = g_handles.find(dev);
+  if (hit != g_handles.end()) {
+    *handle = hit->second;
+    return 0;
+  }
+  if (hipblasLtCreate(handle) != HIPBLAS_STATUS_SUCCESS) { *err = "hipblasLtCreate failed"; return -1; }
+  g_handles[dev] = *handle;
+  return 0;
+}
 
 }  // namespace
 
@@ -83,6 +95,52 @@ int projection_gemm(bool bf16, int64_t n_tokens, int64_t d_model, int64_t k2, co
   const float alpha = 1.0f, beta = 1.0f;
   hipblasStatus_t st = hipblasLtMatmul(handle, p.desc, &alpha, w_cat, p.la, a_cat, p.lb, &beta, residual,
                                        p.lc, out, p.lc, &p.algo, ws, p.ws, stream);
+  if (st != HIPBLAS_STATUS_SUCCESS) { *err = "hipblasLtMatmul failed"; return -1; }
+  return 0;
+}
+
+int gemm_bf16_f32out(bool trans_a, bool trans_b, int64_t m, int64_t n, int64_t k, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, float* D, int64_t ldd, void* ws, size_t ws_bytes,
+                     hipStream_t stream, const char** err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { *err = "hipGetDevice failed"; return -1; }
+  std::lock_guard<std::mutex> lock(g_mu);
+  hipblasLtHandle_t handle;
+  if (get_handle(dev, &handle, err) != 0) return -1;
+  const auto key = std::make_tuple(dev, trans_a ? 1 : 0, trans_b ? 1 : 0, m, n, k, lda, ldb, ldd, ws_bytes);
+  auto pit = g_gplans.find(key);
+  if (pit == g_gplans.end()) {
+    Plan p;
+    if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) {
+      *err = "hipblasLtMatmulDescCreate failed";
+      return -1;
+    }
+    int32_t opa = trans_a ? HIPBLAS_OP_T : HIPBLAS_OP_N, opb = trans_b ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+    hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof(opa));
+    hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof(opb));
+    hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, trans_a ? k : m, trans_a ? m : k, lda);
+    hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, trans_b ? n : k, trans_b ? k : n, ldb);
+    hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_32F, m, n, ldd);
+    hipblasLtMatmulPreference_t pref;
+    hipblasLtMatmulPreferenceCreate(&pref);
+    uint64_t wsz = ws_bytes;
+    hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz, sizeof(wsz));
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int nres = 0;
+    hipblasStatus_t st = hipblasLtMatmulAlgoGetHeuristic(handle, p.desc, p.la, p.lb, p.lc, p.lc, pref, 1, res, &nres);
+    hipblasLtMatmulPreferenceDestroy(pref);
+    if (st != HIPBLAS_STATUS_SUCCESS || nres < 1) {
+      *err = "hipBLASLt found no algorithm for a backward GEMM";
+      return -1;
+    }
+    p.algo = res[0].algo;
+    p.ws = res[0].workspaceSize;
+    pit = g_gplans.emplace(key, p).first;
+  }
+  const Plan& p = pit->second;
+  const float alpha = 1.0f, beta = 0.0f;
+  hipblasStatus_t st = hipblasLtMatmul(handle, p.desc, &alpha, A, p.la, B, p.lb, &beta, D, p.lc, D, p.lc, &p.algo,
+                                       ws, p.ws, stream);
   if (st != HIPBLAS_STATUS_SUCCESS) { *err = "hipblasLtMatmul failed"; return -1; }
   return 0;
 }

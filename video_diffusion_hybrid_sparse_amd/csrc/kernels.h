@@ -23,6 +23,8 @@ struct SoftmaxArgs {
   Geo geo;
   float c2_text, c2_video;
   float out_scale;
+  float* lse;    // nullable [N,H]: m + log2(l), the log2-domain log-sum-exp of each query's
+                 // scaled scores (the backward rebuilds P = exp2(s * c2 - lse))
 };
 
 // fp8 value staging: vout[n] = bf16(code value of v8[n]) for the video values and
@@ -58,9 +60,10 @@ struct BuildArgs {
   const T* v;
   const T* tk;  // [L,H,d]
   const T* tv;
-  float* S;      // [F,H,d,d]
+  float* S;      // [F,H,d,d]; by_group: [n_groups,H,d,d]
   float* Stext;  // [H,d,d]
   Geo geo;
+  int by_group = 0;  // 1: S[grp] = sum over the tokens of query group grp of k^T v (no text)
 };
 
 // Forward/backward state scan over chunks.
@@ -105,6 +108,63 @@ struct DeltaArgs {
   Geo geo;
   float beta;
 };
+
+// ---- backward -----------------------------------------------------------------------
+// Gate and RMSNorm backward per (token, head).
+struct EpiBwdArgs {
+  const float* dacat;  // [N, 2*H*d]: gradient of [a_s | a_l]
+  const __bf16* gs;    // [N,H,d] gate logits
+  const __bf16* gl;
+  const float* o;      // [N,H,d] softmax output (before its gate)
+  const float* u;      // [N,H,d] linear read (before RMSNorm)
+  const float* w;      // [H,d] RMSNorm weight
+  __bf16* dO;          // [N,H,d] gradient of o
+  __bf16* du;          // [N,H,d] gradient of u
+  float* dgs;          // [N,H,d]
+  float* dgl;
+  float* delta;        // [N,H]: dO . o per token and head
+  float* dw_part;      // [ceil(N/64),H,d] per-block partial sums of the weight gradient
+  float* dw;           // [H,d]
+  Geo geo;
+  float eps;
+};
+
+// y[n] += x[n] . M or x[n] . M^T per token of each query group (or of the text).
+template <typename X>
+struct TokenStateArgs {
+  const X* x;              // [tokens,H,d]
+  const float* m0;         // [nC,H,d,d] indexed by the group's chunk (text: [H,d,d])
+  const float* m1;         // nullable, same layout, added to m0
+  const float* m_anchor;   // nullable [H,d,d]: matrix of the anchor groups (skipped if NULL)
+  float* y;                // [tokens,H,d], accumulated
+  Geo geo;
+  int text;                // 1: the text tokens, m0 [H,d,d]
+};
+
+// Softmax backward: dq (stored), dk, dv, dtext_k, dtext_v (stored).
+struct SoftmaxBwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* tk;
+  const __bf16* tv;
+  const __bf16* dO;    // [N,H,d]
+  const float* lse;    // [N,H] log2-domain log-sum-exp
+  const float* delta;  // [N,H]
+  float* dq;           // [N,H,d]
+  float* dk;
+  float* dv;
+  float* dtk;          // [L,H,d]
+  float* dtv;
+  Geo geo;
+  float c2, scale;     // scale * log2(e), scale
+};
+
+hipError_t launch_epi_bwd(const EpiBwdArgs& a, hipStream_t stream);
+hipError_t launch_lin_mix(const float* G, float* dS, float* dTx, const Geo& g, hipStream_t stream);
+template <typename X>
+hipError_t launch_token_state(const TokenStateArgs<X>& a, bool trans, hipStream_t stream);
+hipError_t launch_softmax_bwd(const SoftmaxBwdArgs& a, hipStream_t stream);
 
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream);
 hipError_t launch_softmax_fp8(const SoftmaxArgs& a, hipStream_t stream);

@@ -31,7 +31,14 @@ __global__ __launch_bounds__(256) void build_bf16_kernel(BuildArgs<__bf16> a) {
 
   const __bf16 *kb, *vb;
   int ntok;
-  if (fr < g.F) {
+  if (a.by_group) {
+    int f0, f1;
+    group_frames(g, fr, f0, f1);
+    kb = a.k + (size_t)f0 * g.T * rs + h * D;
+    vb = a.v + (size_t)f0 * g.T * rs + h * D;
+    ntok = (f1 - f0) * g.T;
+    out = a.S + ((size_t)fr * g.H + h) * D * D;
+  } else if (fr < g.F) {
     kb = a.k + (size_t)fr * g.T * rs + h * D;
     vb = a.v + (size_t)fr * g.T * rs + h * D;
     ntok = is_anchor(g, fr) ? 0 : g.T;  // anchors are in neither linear state
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(256) void build_bf16_kernel(BuildArgs<__bf16> a) {
 }
 
 hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
-  dim3 grid(a.geo.F + 1, a.geo.H), block(256);
+  dim3 grid(a.by_group ? n_groups(a.geo) : a.geo.F + 1, a.geo.H), block(256);
   if (a.geo.d == 128)
     hipLaunchKernelGGL(build_bf16_kernel<128>, grid, block, 0, stream, a);
   else if (a.geo.d == 64)

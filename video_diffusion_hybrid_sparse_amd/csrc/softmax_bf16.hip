@@ -306,6 +306,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   for (; j < nst; ++j) stage(j, std::integral_constant<bool, FP8>{});
 
   l = pair_sum(l);
+  if (a.lse && qok && half == 0) a.lse[(size_t)qtok * g.H + h] = m + __log2f(l);
   const float inv = a.out_scale / l;
   const size_t orow = (size_t)qtok * rs + h * D;
   __bf16* arow = a.acat + (size_t)qtok * 2 * rs + h * D;

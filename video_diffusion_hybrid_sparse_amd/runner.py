@@ -43,6 +43,27 @@ class DeviceLayer:
                                 o_soft_dbg=self.o_soft_dbg, u_lin_dbg=self.u_lin_dbg, workspace=self.workspace,
                                 stream=stream)
 
+    def backward(self, dout: torch.Tensor, stream=None) -> dict:
+        """Layer backward for the upstream gradient dout [N, D]; returns float32 gradients
+        (dq, dk, dv, dtext_k, dtext_v, dg_s, dg_l, dw_rms, dw_s, dw_l)."""
+        c = self.cfg
+        N, H, d, L, D = c.frames * c.tokens_per_frame, c.heads, c.head_dim, c.text_len, c.model_dim
+        dev = self.q.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        dqkv = torch.empty(3, N, H, d, **f32)
+        dtext = torch.empty(2, L, H, d, **f32)
+        dgates = torch.empty(2, N, H, d, **f32)
+        dw = torch.empty(H, d, **f32)
+        dwo = torch.empty(D, 2 * H * d, **f32)
+        if "bwd_ws" not in self.extra:
+            self.extra["bwd_ws"] = torch.empty(binding.bwd_workspace_bytes(c), dtype=torch.uint8, device=dev)
+        binding.hybrid_attn_bwd(self.q, self.k, self.v, self.text_kv, self.gates, self.rms_weight, self.w_out,
+                                dout.contiguous(), c, dqkv, dtext if L > 0 else None, dgates, dw, dwo,
+                                workspace=self.extra["bwd_ws"], stream=stream)
+        hd = H * d
+        return dict(dq=dqkv[0], dk=dqkv[1], dv=dqkv[2], dtext_k=dtext[0], dtext_v=dtext[1], dg_s=dgates[0],
+                    dg_l=dgates[1], dw_rms=dw, dw_s=dwo[:, :hd], dw_l=dwo[:, hd:])
+
     def workspace_tensors(self) -> dict:
         """Views into the workspace (valid after run): frame_states [F,H,d,d],
         text_state [H,d,d], fwd_states/bwd_states [nC,H,d,d] float32 and

@@ -7,7 +7,7 @@ HIP library) can take their inputs from here.
 Recipe (stated once so a reader can regenerate any tensor):
 
 * Each tensor has a fixed index: q 0, k 1, v 2, text_k 3, text_v 4, g_s 5, g_l 6,
-  w_rms 7, w_s 8, w_l 9, x 10.
+  w_rms 7, w_s 8, w_l 9, x 10, and the upstream gradient of backward tests dout 11.
 * Its flat element range is cut into 2**22-element chunks; chunk j is drawn as float32
   standard normals from ``numpy.random.PCG64(SeedSequence([seed, index, j]))``.  The
   result does not depend on the number of threads used.
@@ -157,6 +157,13 @@ def make_inputs(shape: LayerShape, seed: Optional[int] = None) -> LayerInputs:
         g_s=_round(g_s, act), g_l=_round(g_l, act),
         w_rms=torch.from_numpy(w_rms.astype(np.float32)),
         w_s=_round(ws, act), w_l=_round(wl, act), x=_round(x, act), **kw)
+
+
+def upstream_grad(shape: LayerShape, seed: Optional[int] = None) -> torch.Tensor:
+    """Seeded upstream gradient dout [N, D] for backward tests: N(0,1) with tensor index 11,
+    rounded to the activation dtype."""
+    seed = shape.seed if seed is None else seed
+    return _round(_normal(seed, 11, shape.tokens * shape.dmodel).reshape(shape.tokens, shape.dmodel), shape.act_dtype)
 
 
 def membership_probe_inputs(shape: LayerShape) -> LayerInputs:
