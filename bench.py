@@ -100,6 +100,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--linear-variant", type=int, default=0, choices=(0, 1))
     ap.add_argument("--delta-beta", type=float, default=0.5)
+    ap.add_argument("--backward", action="store_true", help="time the layer backward instead of the forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the layer is not sharded across GPUs (asked for --gpus {args.gpus})",
@@ -117,6 +118,8 @@ def main() -> int:
     inp = synth.make_inputs(shape)
     dl = runner.upload(inp)
     torch.cuda.synchronize()
+    if args.backward:
+        return bench_backward(args, shape, inp, dl)
     log("bench: warmup", args.warmup)
     for _ in range(args.warmup):
         dl.run()
@@ -175,6 +178,37 @@ def main() -> int:
         log("bench: cpu baseline (oracle on a sample)")
         res["cpu_baseline"] = cpu_baseline(shape, inp)
     print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_backward(args, shape, inp, dl) -> int:
+    """Times vdn_hybrid_attn_bwd (which recomputes the forward it needs) at the same shape."""
+    import torch
+
+    from video_diffusion_hybrid_sparse_amd import synth, workload
+
+    if shape.linear_variant != 0:
+        print("the backward is built for linear variant 0", file=sys.stderr)
+        return 2
+    dout = synth.upstream_grad(shape).cuda()
+    for _ in range(args.warmup):
+        dl.backward(dout)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dl.backward(dout)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fl = workload.backward_flops(shape)
+    print(json.dumps({
+        "metric": "hybrid-attn layer backward ms + TFLOP/s at 768p 60-frame shape, 1 GPU",
+        "value": round(fl["total"] / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations, gate logits and upstream gradient, 768p layer shape",
+        "config": {"workload": shape.name + "_backward", "layer_backward_tflop": round(fl["total"] / 1e12, 3),
+                   "includes": "forward recompute (not counted in the FLOPs)"},
+    }), flush=True)
     return 0
 
 

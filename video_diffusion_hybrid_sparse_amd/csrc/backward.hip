@@ -135,17 +135,19 @@ __global__ __launch_bounds__(256) void lin_mix_kernel(const float* G, float* dS,
 }
 
 // y[n] += x[n] . M (TRANS = 0) or x[n] . M^T (TRANS = 1) for the tokens of one query group
-// (or the text) and one head, M a d x d float32 matrix of that group (m0 + m1 when m1 is
-// given).  One workgroup = 32 tokens; thread = one output channel (tid % D) for a slice
-// of the tokens (tid / D); M in LDS (transposed for TRANS), the tokens' x in LDS.
+// (or of the text) and one head, M a d x d float32 matrix of that group (m0 + m1 when m1 is
+// given), on MFMA like the forward's linear read: M is split into bf16 hi + lo parts,
+// stored row-major with XOR-swizzled 16-byte chunks in LDS, and y^T = A x^T runs as two
+// bf16 passes with float32 accumulation; A = M (TRANS: 16-byte row reads) or A = M^T
+// (transposing LDS read).  One workgroup = up to 512 tokens, 4 waves x 32-token
+// sub-tiles; the token is lane-local, y is accumulated in float32.
 template <int D, bool TRANS, typename X>
 __global__ __launch_bounds__(256) void token_state_kernel(TokenStateArgs<X> a) {
-  constexpr int TT = 32, TPT = TT * D / 256;  // tokens per thread
-  __shared__ float M[D * D];
-  __shared__ float xs[TT][D + 4];
+  constexpr int BM = 512, KS = D / 16, DT = D / 32, CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) __bf16 Mhi[D * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Mlo[D * D];
   const Geo g = a.geo;
-  const int grp = blockIdx.x, h = blockIdx.y, tile = blockIdx.z, tid = threadIdx.x;
-  const int o = tid % D, th = tid / D;
+  const int grp = blockIdx.x, h = blockIdx.y, tile = blockIdx.z;
   int t0, t1;
   if (a.text) {
     t0 = 0;
@@ -156,9 +158,10 @@ __global__ __launch_bounds__(256) void token_state_kernel(TokenStateArgs<X> a) {
     t0 = f0 * g.T;
     t1 = f1 * g.T;
   }
-  const int tb = t0 + tile * TT;
+  const int tb = t0 + tile * BM;
   if (tb >= t1) return;
-  // the group's matrix: text -> m0[0]; anchor groups -> m_anchor (skipped when absent);
+  const int te = imin(t1, tb + BM);
+  // the group's matrix: text -> m0; anchor groups -> m_anchor (skipped when absent);
   // chunk groups -> m0 (+ m1) of the group's chunk
   const bool anchor = !a.text && grp < 2;
   if (anchor && !a.m_anchor) return;
@@ -166,37 +169,87 @@ __global__ __launch_bounds__(256) void token_state_kernel(TokenStateArgs<X> a) {
   const float* m1 = anchor ? nullptr : a.m1;
   const int mi = (a.text || anchor) ? 0 : group_chunk(grp);
   const size_t mo = ((size_t)mi * g.H + h) * D * D;
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    float v = m0[mo + e];
-    if (m1) v += m1[mo + e];
-    if (TRANS) M[j * D + i] = v;  // M^T: y[o] = sum_m x[m] M[o][m]
-    else M[e] = v;
-  }
-  const size_t rs = (size_t)g.H * D;
-  for (int e = tid; e < TT * D; e += 256) {
-    const int t = e / D, c = e % D;
-    xs[t][c] = tb + t < t1 ? (float)a.x[(size_t)(tb + t) * rs + h * D + c] : 0.0f;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  for (int u = tid; u < D * D / 4; u += 256) {
+    const int i = u / (D / 4), j = 4 * (u % (D / 4));
+    float4 x = *reinterpret_cast<const float4*>(m0 + mo + i * D + j);
+    if (m1) {
+      const float4 y = *reinterpret_cast<const float4*>(m1 + mo + i * D + j);
+      x = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    }
+    const float sv[4] = {x.x, x.y, x.z, x.w};
+    float hv[4], lv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hv[e] = (float)(__bf16)sv[e];
+      lv[e] = sv[e] - hv[e];
+    }
+    const int off = i * D + (((j >> 3) ^ swz<CPR>(i)) * 8) + (j & 7);
+    *reinterpret_cast<uint2*>(&Mhi[off]) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+    *reinterpret_cast<uint2*>(&Mlo[off]) = make_uint2(pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3]));
   }
   __syncthreads();
-  float acc[TPT];
+
+  // A operand offsets for k-step 0 (channels m = 8 half .. +7 of the contraction):
+  //  TRANS:  A = M, row o = 32 dt + l32, 16-byte row read;
+  //  !TRANS: A = M^T, transposing read; 16-lane group grp16 reads rows m = 8 (grp16 >> 1)
+  //          + 4 c .. +3 and columns o = 32 dt + 16 (grp16 & 1) + 4 (i16 & 3) .. +3.
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int aoff[DT][2];
 #pragma unroll
-  for (int t = 0; t < TPT; ++t) acc[t] = 0.0f;
-#pragma unroll 2
-  for (int m = 0; m < D; m += 4) {
-    const float w0 = M[(m + 0) * D + o], w1 = M[(m + 1) * D + o], w2 = M[(m + 2) * D + o], w3 = M[(m + 3) * D + o];
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int t = 0; t < TPT; ++t) {
-      const float4 xv = *reinterpret_cast<const float4*>(&xs[th * TPT + t][m]);
-      acc[t] += xv.x * w0 + xv.y * w1 + xv.z * w2 + xv.w * w3;
+    for (int c = 0; c < 2; ++c) {
+      if (TRANS) {
+        aoff[dt][c] = (32 * dt + l32) * D;  // + chunk per k-step
+      } else {
+        const int row = 8 * (grp16 >> 1) + 4 * c + (i16 >> 2);
+        const int col = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+        aoff[dt][c] = row * D + (((col >> 3) ^ swz<CPR>(row)) * 8) + (col & 7);
+      }
     }
-  }
+  const size_t rs = (size_t)g.H * D;
+  for (int st = wave; tb + st * 32 < te; st += 4) {
+    int tok = tb + st * 32 + l32;
+    const bool ok = tok < te;
+    tok = ok ? tok : te - 1;
+    bf16x8 xr[KS];
 #pragma unroll
-  for (int t = 0; t < TPT; ++t) {
-    const int tok = tb + th * TPT + t;
-    if (tok < t1) {
-      float* y = a.y + (size_t)tok * rs + h * D + o;
-      *y += acc[t];
+    for (int s = 0; s < KS; ++s) xr[s] = load_bf16x8(a.x + (size_t)tok * rs + h * D + half * 8 + 16 * s);
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      acc[dt] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 ahi, alo;
+        if (TRANS) {
+          const int off = aoff[dt][0] + (((2 * ks + half) ^ swz<CPR>(l32)) * 8);
+          ahi = *reinterpret_cast<const bf16x8*>(&Mhi[off]);
+          alo = *reinterpret_cast<const bf16x8*>(&Mlo[off]);
+        } else {
+          const int base = 16 * ks * D;
+          const bf16x4 h0 = lds_read_tr(Mhi + base + aoff[dt][0]), h1 = lds_read_tr(Mhi + base + aoff[dt][1]);
+          const bf16x4 l0 = lds_read_tr(Mlo + base + aoff[dt][0]), l1 = lds_read_tr(Mlo + base + aoff[dt][1]);
+          ahi = bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          alo = bf16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        }
+        acc[dt] = mfma32x32x16(alo, xr[ks], acc[dt]);
+        acc[dt] = mfma32x32x16(ahi, xr[ks], acc[dt]);
+      }
+    }
+    if (ok) {
+      // lane holds outputs o = 32 dt + 8 i + 4 half + e of its token
+      float* y = a.y + (size_t)tok * rs + h * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float4* p = reinterpret_cast<float4*>(y + 32 * dt + 8 * i + 4 * half);
+          const float4 cur = *p;
+          *p = make_float4(cur.x + acc[dt][4 * i], cur.y + acc[dt][4 * i + 1], cur.z + acc[dt][4 * i + 2],
+                           cur.w + acc[dt][4 * i + 3]);
+        }
     }
   }
 }
@@ -588,7 +641,7 @@ hipError_t launch_token_state(const TokenStateArgs<X>& a, bool trans, hipStream_
   const int ngrp = a.text ? 1 : n_groups(g);
   int maxtok = a.text ? g.L : g.C * g.T;
   if (!a.text) maxtok = imax(maxtok, g.T);
-  const int tiles = (maxtok + 31) / 32;
+  const int tiles = (maxtok + 511) / 512;
   if (tiles == 0) return hipSuccess;
   dim3 grid(ngrp, g.H, tiles), block(256);
 #define VDN_TS(DD, TR) hipLaunchKernelGGL(HIP_KERNEL_NAME(token_state_kernel<DD, TR, X>), grid, block, 0, stream, a)

@@ -53,6 +53,20 @@ def flops(s: LayerShape) -> dict:
     return f
 
 
+def backward_flops(s: LayerShape) -> dict:
+    """Algorithmic FLOPs of the layer backward (the forward it recomputes is not counted):
+    softmax 8 d per (query, key) pair and head (dV = P^T dO, dP = dO V^T, dQ = dS K,
+    dK = dS^T Q); projections 2 x 2 N (2 H d) D (input and weight gradients); linear
+    branch 2 d^2 per query token and head for dq and for the state gradients, and
+    2 x 2 d^2 per key token and head for dk and dv."""
+    H, d, T, L, N, D, F = s.heads, s.head_dim, s.tokens_per_frame, s.text_len, s.tokens, s.dmodel, s.frames
+    f = dict(softmax=8 * d * H * pairs_per_head(s),
+             projection=2 * 2 * N * 2 * H * d * D,
+             linear=2 * 2 * d * d * H * N + 2 * 2 * d * d * H * (T * (F - 2) + L))
+    f["total"] = sum(f.values())
+    return f
+
+
 def bytes_moved(s: LayerShape) -> dict:
     """Algorithmic HBM bytes per step (each input read once, each output written once)."""
     H, d, T, L, N, D, F, nC = s.heads, s.head_dim, s.tokens_per_frame, s.text_len, s.tokens, s.dmodel, s.frames, s.n_chunks
