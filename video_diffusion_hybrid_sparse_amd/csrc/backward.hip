@@ -414,20 +414,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 }
 
 // ---- 3b. softmax backward, dK and dV ----------------------------------------------------
-// One workgroup = 128 keys of one frame (or of the text) and one head, 4 waves x 32 keys.
-// The queries that read a video key frame are the key segments of its chunk's group
-// (anchor frames and text: every query).  Per 64-query sub-tile: S = Q K^T and
+// One workgroup = 256 keys of one frame (or of the text) and one head, 8 waves x 32 keys
+// (two waves per SIMD).  The queries that read a video key frame are the key segments of
+// its chunk's group (anchor frames and text: every query).  Queries arrive in 64-query
+// stages (HBM -> LDS, double-buffered), computed as two 32-query halves so that the score
+// tiles of one half fit beside the key-side registers.  Per half: S = Q K^T and
 // dP = dO V^T (Q and dO rows are MFMA A operands, the key is lane-local);
 // P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and dK^T += Q^T dS with dO^T
-// and Q^T gathered by the transposing LDS read.  dk = scale dK.
-template <int D>
-__global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a) {
-  constexpr int NW = 4, BK = 128, BQ = 64;
+// and Q^T gathered by the transposing LDS read.  dk = scale dK.  The two gradients are
+// separate passes (PASS 0: dV from S; PASS 1: dK from S and dP, the tile's values in LDS
+// as the B operand of dP): one set of accumulators per pass fits two waves per SIMD.
+template <int D, int PASS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a) {
+  constexpr int NW = 8, BK = 256, BQ = 64;
   constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
   constexpr int NI = BQ * CPR / (64 * NW);
   static_assert(NI >= 1, "stage size");
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) __bf16 Os[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[BK * D];  // the tile's values (B operand of dP)
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ], Dl[2][BQ];
   const Geo g = a.geo;
   // key tiles of one head: text tiles, then the tiles of frames 0 .. F-1; anchors' and
@@ -458,13 +463,21 @@ __global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a)
   ktok = kok ? ktok : kstart + kvalid - 1;
   const __bf16* kbase = text ? a.tk : a.k;
   const __bf16* vbase = text ? a.tv : a.v;
-  bf16x8 kreg[KS], vreg[KS];
+  bf16x8 kreg[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    kreg[s] = load_bf16x8(kbase + (size_t)ktok * rs + h * D + half * 8 + 16 * s);
-    vreg[s] = load_bf16x8(vbase + (size_t)ktok * rs + h * D + half * 8 + 16 * s);
-  }
+  for (int s = 0; s < KS; ++s) kreg[s] = load_bf16x8(kbase + (size_t)ktok * rs + h * D + half * 8 + 16 * s);
   __builtin_amdgcn_s_waitcnt(0);
+  // value rows of the tile into LDS (XOR-swizzled 16-byte chunks; rows past the tile are
+  // copies of its last row)
+  if constexpr (PASS == 1) {
+    constexpr int NIV = BK * CPR / (64 * NW);
+#pragma unroll
+    for (int i = 0; i < NIV; ++i) {
+      const int q = i * 64 * NW + tid, r = q / CPR, c = q % CPR;
+      const size_t row = (size_t)(kstart + imin(r, kvalid - 1));
+      load_lds16(vbase + row * rs + h * D + (c ^ swz<CPR>(r)) * 8, &Vt[(i * 64 * NW + wave * 64) * 8]);
+    }
+  }
 
   int lrow[NI], lcol[NI];
 #pragma unroll
@@ -519,12 +532,9 @@ __global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a)
       trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
     }
 
-  f32x16 dk[DT], dv[DT];
+  f32x16 acc[DT];  // PASS 0: dV^T, PASS 1: dK^T
 #pragma unroll
-  for (int i = 0; i < DT; ++i) {
-    dk[i] = 0.0f;
-    dv[i] = 0.0f;
-  }
+  for (int i = 0; i < DT; ++i) acc[i] = 0.0f;
   const float c2 = a.c2;
 
   if (nst > 0) {
@@ -538,25 +548,20 @@ __global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a)
     if (j + 1 < nst) issue(j + 1, buf ^ 1);
     int start, valid;
     stage_at(j, start, valid);
-    const __bf16* Q = Qs[buf];
-    const __bf16* O = Os[buf];
-    f32x16 s[2], dp[2];
+    for (int rt = 0; rt < 2; ++rt) {  // 32-query halves of the stage
+    if (rt * 32 >= valid) break;
+    const __bf16* Q = Qs[buf] + 32 * rt * D;
+    const __bf16* O = Os[buf] + 32 * rt * D;
+    f32x16 s = 0.0f, dp = 0.0f;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      s[rt] = 0.0f;
-      dp[rt] = 0.0f;
+    for (int k = 0; k < KS; ++k) {
+      s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Q + qrd[k]), kreg[k], s);
+      if constexpr (PASS == 1)
+        dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(O + qrd[k]),
+                          *reinterpret_cast<const bf16x8*>(&Vt[wave * 32 * D + qrd[k]]), dp);
     }
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Q + 32 * rt * D + qrd[k]), kreg[k], s[rt]);
-        dp[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(O + 32 * rt * D + qrd[k]), vreg[k], dp[rt]);
-      }
-    // accumulator row = query 32 rt + 8 (r/4) + 4 half + r%4 of the sub-tile
-    bf16x8 pb[4], sb[4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    // accumulator row = query 32 rt + 8 (r/4) + 4 half + r%4 of the stage
+    bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int q0 = rt * 32 + 8 * r4 + 4 * half;
@@ -567,11 +572,11 @@ __global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          p[e] = q0 + e < valid ? __builtin_amdgcn_exp2f(s[rt][r] * c2 - lq[e]) : 0.0f;
-          ds[e] = p[e] * (dp[rt][r] - dq4[e]);
+          p[e] = q0 + e < valid ? __builtin_amdgcn_exp2f(s[r] * c2 - lq[e]) : 0.0f;
+          ds[e] = p[e] * (dp[r] - dq4[e]);
         }
-        uint4 wp = __builtin_bit_cast(uint4, pb[2 * rt + (r4 >> 1)]);
-        uint4 ws = __builtin_bit_cast(uint4, sb[2 * rt + (r4 >> 1)]);
+        uint4 wp = __builtin_bit_cast(uint4, pb[r4 >> 1]);
+        uint4 ws = __builtin_bit_cast(uint4, sb[r4 >> 1]);
         if (r4 & 1) {
           wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
           ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
@@ -579,39 +584,34 @@ __global__ __launch_bounds__(256) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a)
           wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
           ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
         }
-        pb[2 * rt + (r4 >> 1)] = __builtin_bit_cast(bf16x8, wp);
-        sb[2 * rt + (r4 >> 1)] = __builtin_bit_cast(bf16x8, ws);
+        pb[r4 >> 1] = __builtin_bit_cast(bf16x8, wp);
+        sb[r4 >> 1] = __builtin_bit_cast(bf16x8, ws);
       }
 #pragma unroll
-    for (int G = 0; G < 4; ++G)
+    for (int G = 0; G < 2; ++G)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 olo = lds_read_tr(O + 16 * G * D + trd[dt][0]);
-        const bf16x4 ohi = lds_read_tr(O + 16 * G * D + trd[dt][1]);
-        const bf16x8 oa = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
-        dv[dt] = mfma32x32x16(oa, pb[G], dv[dt]);
-        const bf16x4 qlo = lds_read_tr(Q + 16 * G * D + trd[dt][0]);
-        const bf16x4 qhi = lds_read_tr(Q + 16 * G * D + trd[dt][1]);
-        const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-        dk[dt] = mfma32x32x16(qa, sb[G], dk[dt]);
+        const __bf16* X = PASS == 0 ? O : Q;  // dV^T += dO^T P ; dK^T += Q^T dS
+        const bf16x4 lo = lds_read_tr(X + 16 * G * D + trd[dt][0]);
+        const bf16x4 hi = lds_read_tr(X + 16 * G * D + trd[dt][1]);
+        const bf16x8 xa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = mfma32x32x16(xa, PASS == 0 ? pb[G] : sb[G], acc[dt]);
       }
+    }
     if (j + 1 < nst) put_stats(buf ^ 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   if (kok) {
-    float* ko = (text ? a.dtk : a.dk) + (size_t)ktok * rs + h * D;
-    float* vo = (text ? a.dtv : a.dv) + (size_t)ktok * rs + h * D;
+    float* dst = PASS == 0 ? (text ? a.dtv : a.dv) : (text ? a.dtk : a.dk);
+    dst += (size_t)ktok * rs + h * D;
+    const float f = PASS == 0 ? 1.0f : a.scale;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 32 * dt + 8 * i + 4 * half;
-        *reinterpret_cast<float4*>(ko + c) = make_float4(a.scale * dk[dt][4 * i], a.scale * dk[dt][4 * i + 1],
-                                                         a.scale * dk[dt][4 * i + 2], a.scale * dk[dt][4 * i + 3]);
-        *reinterpret_cast<float4*>(vo + c) = make_float4(dv[dt][4 * i], dv[dt][4 * i + 1], dv[dt][4 * i + 2],
-                                                         dv[dt][4 * i + 3]);
-      }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * i + 4 * half) =
+            make_float4(f * acc[dt][4 * i], f * acc[dt][4 * i + 1], f * acc[dt][4 * i + 2], f * acc[dt][4 * i + 3]);
   }
 }
 
@@ -664,10 +664,15 @@ hipError_t launch_softmax_bwd(const SoftmaxBwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int per_head = (g.L + 127) / 128 + g.F * ((g.T + 127) / 128);
-  dim3 grid2(per_head * g.H), block2(256);
-  if (g.d == 128) hipLaunchKernelGGL(softmax_bwd_dkdv_kernel<128>, grid2, block2, 0, stream, a);
-  else hipLaunchKernelGGL(softmax_bwd_dkdv_kernel<64>, grid2, block2, 0, stream, a);
+  const int per_head = (g.L + 255) / 256 + g.F * ((g.T + 255) / 256);
+  dim3 grid2(per_head * g.H), block2(512);
+  if (g.d == 128) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<128, 0>), grid2, block2, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<128, 1>), grid2, block2, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<64, 0>), grid2, block2, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<64, 1>), grid2, block2, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
