@@ -154,3 +154,45 @@ def test_binding_checks_shapes_before_calling():
     q = torch.zeros(3, 1, 32)
     with pytest.raises(ValueError):
         binding.hybrid_attn_fwd(q, q, q, None, None, None, None, None, None, cfg)
+
+
+def test_bwd_unsupported_configs():
+    for shape, change in ((shapes.TOY, {}), (shapes.LONG, {}), (shapes.MID, dict(linear_variant=1, delta_beta=0.5))):
+        cfg = binding.make_cfg(shape)
+        for k, v in change.items():
+            setattr(cfg, k, v)
+        assert binding.lib().vdn_hybrid_attn_bwd_workspace_bytes(ctypes.byref(cfg)) == 0
+        assert "backward" in binding.last_error()
+    cfg = binding.make_cfg(shapes.MID)
+    assert binding.bwd_workspace_bytes(cfg) > binding.workspace_bytes(cfg)
+
+
+def _bwd(cfg, ptrs, ws_bytes):
+    return binding.lib().vdn_hybrid_attn_bwd(*ptrs[:8], ctypes.byref(cfg), *ptrs[8:], ws_bytes, None)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check: fake pointers must never reach a GPU")
+def test_bwd_argument_checks_launch_nothing():
+    cfg = binding.make_cfg(shapes.MID)
+    need = binding.bwd_workspace_bytes(cfg)
+    # q k v text_kv gates rms_weight w_out dout | dqkv dtext_kv dgates drms_weight dw_out workspace
+    good = [0x10000 * (i + 1) for i in range(14)]
+    assert _bwd(cfg, good, need) == NO_DEVICE
+    required = [0, 1, 2, 4, 5, 6, 7, 8, 10, 11, 12, 13]
+    for i in required:
+        bad = list(good)
+        bad[i] = None
+        assert _bwd(cfg, bad, need) == INVALID, i
+        assert "NULL" in binding.last_error()
+        bad[i] = good[i] + 4
+        assert _bwd(cfg, bad, need) == INVALID, i
+        assert "aligned" in binding.last_error()
+    for i in (3, 9):  # text_kv, dtext_kv with text_len > 0
+        bad = list(good)
+        bad[i] = None
+        assert _bwd(cfg, bad, need) == INVALID, i
+    assert _bwd(cfg, good, need - 1) == WORKSPACE
+    cfg.text_len = 0
+    bad = list(good)
+    bad[3] = bad[9] = None
+    assert _bwd(cfg, bad, binding.bwd_workspace_bytes(cfg)) == NO_DEVICE
