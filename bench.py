@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
-PMC_TRAFFIC = {"source_sha256_16": "bd7ac06167ec7857", "bytes": 12.968e9}
+PMC_TRAFFIC = {"source_sha256_16": "74fa942776c6cc68", "bytes": 13.105e9}
 SOFTMAX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/softmax_bf16.hip",
                    "video_diffusion_hybrid_sparse_amd/csrc/common.h",
                    "video_diffusion_hybrid_sparse_amd/csrc/kernels.h")
