@@ -35,4 +35,4 @@ Parity pins: every function here is pinned by a CPU test (tests/test_oracle_*.py
 something other than itself — the article's frame-7 example, hand-derived set tables,
 library attention and RMSNorm routines, brute-force loops and closed-form invariants.
 """
-from . import layer, sets  # noqa: F401
+from . import layer, mxfp8, sets  # noqa: F401
