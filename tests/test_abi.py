@@ -10,14 +10,17 @@ import torch
 
 from video_diffusion_hybrid_sparse_amd import binding, shapes
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vdn_hybrid_attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, NO_DEVICE = range(6)
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vdn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(vdn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_exports():
@@ -196,3 +199,47 @@ def test_bwd_argument_checks_launch_nothing():
     bad = list(good)
     bad[3] = bad[9] = None
     assert _bwd(cfg, bad, binding.bwd_workspace_bytes(cfg)) == NO_DEVICE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check: fake pointers must never reach a GPU")
+def test_mxfp8_argument_checks_launch_nothing():
+    L = binding.lib()
+    x, codes, scales = 0x10000, 0x20000, 0x30000
+    assert L.vdn_mxfp8_quantize(x, 64, 256, codes, scales, None) == NO_DEVICE
+    assert L.vdn_mxfp8_quantize(x, 64, 96, codes, scales, None) == INVALID  # cols % 128
+    assert L.vdn_mxfp8_quantize(x, -1, 256, codes, scales, None) == INVALID
+    assert L.vdn_mxfp8_quantize(x + 8, 64, 256, codes, scales, None) == INVALID
+    assert "aligned" in binding.last_error()
+    assert L.vdn_mxfp8_quantize(x, 64, 256, codes, scales + 2, None) == INVALID
+    assert L.vdn_mxfp8_quantize(None, 64, 256, codes, scales, None) == INVALID
+    assert L.vdn_mxfp8_quantize(x, 1 << 30, 1 << 13, codes, scales, None) == INVALID  # rows * cols >= 2^42
+    b, a = 0x40000, 0x50000
+    assert L.vdn_mxfp8_quantize_lora(x, b, a, 16, 0.5, 64, 256, codes, scales, None) == NO_DEVICE
+    assert L.vdn_mxfp8_quantize_lora(x, b, a, 0, 0.5, 64, 256, codes, scales, None) == INVALID
+    assert L.vdn_mxfp8_quantize_lora(x, None, a, 16, 0.5, 64, 256, codes, scales, None) == INVALID
+    assert L.vdn_mxfp8_quantize_lora(x, b, a + 8, 16, 0.5, 64, 256, codes, scales, None) == INVALID
+    assert L.vdn_mxfp8_quantize_lora(x, b, a, 16, float("inf"), 64, 256, codes, scales, None) == INVALID
+
+    outs = (ctypes.c_void_p * 5)(*[0x100000 * (i + 1) for i in range(5)])
+    ac, as_, wc, ws = 0x10000, 0x20000, 0x30000, 0x40000
+
+    def lin(m=300, n=640, k=512, n_out=5, o=outs, bias=None, **ptrs):
+        p = dict(ac=ac, as_=as_, wc=wc, ws=ws)
+        p.update(ptrs)
+        return L.vdn_mxfp8_linear(p["ac"], p["as_"], p["wc"], p["ws"], bias, m, n, k, n_out, o, None)
+
+    assert lin() == NO_DEVICE
+    assert lin(bias=0x50000) == NO_DEVICE
+    assert lin(bias=0x50002) == INVALID
+    assert lin(k=384) == UNSUPPORTED  # k % 256
+    assert lin(n=600) == UNSUPPORTED  # n / n_out = 120 is not a multiple of 32
+    assert lin(n_out=9) == INVALID
+    assert lin(n_out=0) == INVALID
+    assert lin(m=(1 << 24) - 1, k=1 << 8) == NO_DEVICE
+    assert lin(m=1 << 24, k=1 << 8) == UNSUPPORTED  # m * k = 2^32
+    assert lin(ac=None) == INVALID
+    assert lin(wc=wc + 4) == INVALID
+    assert lin(ws=ws + 1) == INVALID
+    bad = (ctypes.c_void_p * 5)(*[0x100000 * (i + 1) for i in range(4)], None)
+    assert lin(o=bad) == INVALID
+    assert "outs[4]" in binding.last_error()

@@ -24,7 +24,8 @@ PROFILE_STEPS = ("state_build", "state_scan", "linear_read", "softmax", "project
 
 EXPORTS = ("vdn_hybrid_attn_workspace_bytes", "vdn_hybrid_attn_workspace_layout", "vdn_hybrid_attn_fwd",
            "vdn_hybrid_attn_bwd_workspace_bytes", "vdn_hybrid_attn_bwd",
-           "vdn_hybrid_attn_membership", "vdn_profile_enable", "vdn_profile_read", "vdn_last_error")
+           "vdn_hybrid_attn_membership", "vdn_profile_enable", "vdn_profile_read", "vdn_last_error",
+           "vdn_mxfp8_quantize", "vdn_mxfp8_quantize_lora", "vdn_mxfp8_linear")
 
 
 class VdnError(RuntimeError):
@@ -75,6 +76,13 @@ def lib() -> ctypes.CDLL:
         L.vdn_profile_enable.restype = i32
         L.vdn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(ctypes.c_int64)]
         L.vdn_profile_read.restype = i32
+        i64, f32 = ctypes.c_int64, ctypes.c_float
+        L.vdn_mxfp8_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.vdn_mxfp8_quantize.restype = i32
+        L.vdn_mxfp8_quantize_lora.argtypes = [vp, vp, vp, ctypes.c_int32, f32, i64, i64, vp, vp, vp]
+        L.vdn_mxfp8_quantize_lora.restype = i32
+        L.vdn_mxfp8_linear.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, ctypes.POINTER(vp), vp]
+        L.vdn_mxfp8_linear.restype = i32
         L.vdn_last_error.argtypes = []
         L.vdn_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -224,3 +232,49 @@ def hybrid_attn_bwd(q, k, v, text_kv, gates, rms_weight, w_out, dout, cfg: Cfg, 
         _ptr(dqkv, "dqkv"), _ptr(dtext_kv, "dtext_kv") if L > 0 else None, _ptr(dgates, "dgates"),
         _ptr(drms_weight, "drms_weight"), _ptr(dw_out, "dw_out"), _ptr(workspace, "workspace"), workspace.numel(),
         handle))
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def mxfp8_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, lora_b=None, lora_a=None,
+                   lora_scale: float = 0.0, stream=None) -> None:
+    """Enqueue MXFP8 quantisation of the rows of bf16 x [rows, cols] into uint8 codes
+    [rows, cols] and uint8 E8M0 scales [rows, cols // 32]; with lora_b [rows, r] and
+    lora_a [r, cols] (bf16) the merged x + lora_scale * lora_b @ lora_a is quantised."""
+    rows, cols = x.shape
+    _expect(x, "x", (rows, cols), (torch.bfloat16,))
+    _expect(codes, "codes", (rows, cols), (torch.uint8, torch.float8_e4m3fn))
+    _expect(scales, "scales", (rows, cols // 32), (torch.uint8,))
+    h = _stream_handle(stream, x.device)
+    if lora_b is None:
+        _check(lib().vdn_mxfp8_quantize(_ptr(x, "x"), rows, cols, _ptr(codes, "codes"), _ptr(scales, "scales"), h))
+        return
+    rank = lora_b.shape[1]
+    _expect(lora_b, "lora_b", (rows, rank), (torch.bfloat16,))
+    _expect(lora_a, "lora_a", (rank, cols), (torch.bfloat16,))
+    _check(lib().vdn_mxfp8_quantize_lora(_ptr(x, "w"), _ptr(lora_b, "lora_b"), _ptr(lora_a, "lora_a"), rank,
+                                         float(lora_scale), rows, cols, _ptr(codes, "codes"),
+                                         _ptr(scales, "scales"), h))
+
+
+def mxfp8_linear(a_codes, a_scales, w_codes, w_scales, outs: list, bias=None, stream=None) -> None:
+    """Enqueue the MXFP8 product: outs[o] [m, n / len(outs)] (bf16) = dequant(a) @
+    dequant(w)[o * c:(o + 1) * c].T + bias[o * c:(o + 1) * c] with c = n / len(outs)."""
+    m, k = a_codes.shape
+    n = w_codes.shape[0]
+    n_out = len(outs)
+    _expect(a_codes, "a_codes", (m, k), (torch.uint8, torch.float8_e4m3fn))
+    _expect(a_scales, "a_scales", (m, k // 32), (torch.uint8,))
+    _expect(w_codes, "w_codes", (n, k), (torch.uint8, torch.float8_e4m3fn))
+    _expect(w_scales, "w_scales", (n, k // 32), (torch.uint8,))
+    _expect(bias, "bias", (n,), (torch.float32,))
+    for i, o in enumerate(outs):
+        _expect(o, f"outs[{i}]", (m, n // n_out), (torch.bfloat16,))
+    arr = (ctypes.c_void_p * n_out)(*[_ptr(o, f"outs[{i}]") for i, o in enumerate(outs)])
+    _check(lib().vdn_mxfp8_linear(_ptr(a_codes, "a_codes"), _ptr(a_scales, "a_scales"), _ptr(w_codes, "w_codes"),
+                                  _ptr(w_scales, "w_scales"), _ptr(bias, "bias"), m, n, k, n_out, arr,
+                                  _stream_handle(stream, a_codes.device)))

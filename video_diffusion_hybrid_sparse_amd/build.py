@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvdn_hybrid_attn.so")
-SOURCES = ["api.hip", "gemm.hip", "softmax_bf16.hip", "linear_bf16.hip", "scan.hip", "delta_bf16.hip", "backward.hip", "fp32_path.hip"]
+SOURCES = ["api.hip", "gemm.hip", "softmax_bf16.hip", "linear_bf16.hip", "scan.hip", "delta_bf16.hip", "backward.hip", "fp32_path.hip", "mxfp8.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"

@@ -11,7 +11,9 @@
 
 #include "gemm.h"
 #include "kernels.h"
+#include "mxfp8.h"
 #include "vdn_hybrid_attn.h"
+#include "vdn_mxfp8.h"
 
 using namespace vdn;
 
@@ -478,6 +480,96 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
                       ws + L.gemm_ws, L.gemm_ws_bytes, stream, &gerr) != 0)
     return fail(VDN_ERR_HIP, "projection: %s", gerr);
   mark(5);
+  return VDN_OK;
+}
+
+// ---- MXFP8 input-side projections ---------------------------------------------------
+
+static vdn_status check_mx_quant(const void* x, int64_t rows, int64_t cols, const uint8_t* codes,
+                                 const uint8_t* scales) {
+  if (rows > 0 && (!x || !codes || !scales))
+    return fail(VDN_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!aligned16(x) || !aligned16(codes)) return fail(VDN_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  if (((uintptr_t)scales & 3u) != 0) return fail(VDN_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+  if (rows < 0 || cols <= 0 || cols % 128 != 0)
+    return fail(VDN_ERR_INVALID_ARG, "need rows >= 0 and cols a positive multiple of 128 (got %lld x %lld)",
+                (long long)rows, (long long)cols);
+  if (rows > 0 && rows > (INT64_C(1) << 42) / cols)
+    return fail(VDN_ERR_INVALID_ARG, "rows * cols must stay below 2^42");
+  return VDN_OK;
+}
+
+static vdn_status check_device() {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+  return VDN_OK;
+}
+
+vdn_status vdn_mxfp8_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+  vdn_status s = check_mx_quant(x, rows, cols, codes, scales);
+  if (s == VDN_OK) s = check_device();
+  if (s != VDN_OK) return s;
+  MxQuantArgs a{static_cast<const __bf16*>(x), nullptr, nullptr, codes, scales, rows, cols, 0, 0.0f};
+  const hipError_t e = launch_mx_quant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "mxfp8 quantiser launch: %s", hipGetErrorString(e));
+  return VDN_OK;
+}
+
+vdn_status vdn_mxfp8_quantize_lora(const void* w, const void* lora_b, const void* lora_a, int32_t rank,
+                                   float lora_scale, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                   void* stream) {
+  vdn_status s = check_mx_quant(w, rows, cols, codes, scales);
+  if (s != VDN_OK) return s;
+  if (rows > 0 && (!lora_b || !lora_a)) return fail(VDN_ERR_INVALID_ARG, "lora_b and lora_a must be non-NULL");
+  if (!aligned16(lora_a) || ((uintptr_t)lora_b & 1u))
+    return fail(VDN_ERR_INVALID_ARG, "lora_a must be 16-byte aligned and lora_b 2-byte aligned");
+  if (rank < 1 || rank > 4096) return fail(VDN_ERR_INVALID_ARG, "rank must lie in [1, 4096] (got %d)", rank);
+  if (!isfinite(lora_scale)) return fail(VDN_ERR_INVALID_ARG, "lora_scale must be finite");
+  s = check_device();
+  if (s != VDN_OK) return s;
+  MxQuantArgs a{static_cast<const __bf16*>(w), static_cast<const __bf16*>(lora_b), static_cast<const __bf16*>(lora_a),
+                codes, scales, rows, cols, rank, lora_scale};
+  const hipError_t e = launch_mx_quant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "mxfp8 quantiser launch: %s", hipGetErrorString(e));
+  return VDN_OK;
+}
+
+vdn_status vdn_mxfp8_linear(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const float* bias, int64_t m, int64_t n, int64_t k, int32_t n_out,
+                            void* const* outs, void* stream) {
+  if (m > 0 && (!a_codes || !a_scales || !w_codes || !w_scales || !outs))
+    return fail(VDN_ERR_INVALID_ARG, "codes, scales and outs must be non-NULL");
+  if (!aligned16(a_codes) || !aligned16(w_codes)) return fail(VDN_ERR_INVALID_ARG, "codes must be 16-byte aligned");
+  if (((uintptr_t)a_scales & 3u) || ((uintptr_t)w_scales & 3u) || ((uintptr_t)bias & 3u))
+    return fail(VDN_ERR_INVALID_ARG, "scales and bias must be 4-byte aligned");
+  if (m < 0 || n <= 0 || k <= 0) return fail(VDN_ERR_INVALID_ARG, "need m >= 0, n > 0, k > 0");
+  if (k % 256 != 0) return fail(VDN_ERR_UNSUPPORTED, "k must be a multiple of 256 (got %lld)", (long long)k);
+  if (n_out < 1 || n_out > kMxMaxOut)
+    return fail(VDN_ERR_INVALID_ARG, "n_out must lie in [1, %d] (got %d)", kMxMaxOut, n_out);
+  if (n % n_out != 0 || (n / n_out) % 32 != 0)
+    return fail(VDN_ERR_UNSUPPORTED, "n / n_out must be a multiple of 32 (n %lld, n_out %d)", (long long)n, n_out);
+  if (m * k >= (INT64_C(1) << 32) || n * k >= (INT64_C(1) << 32))
+    return fail(VDN_ERR_UNSUPPORTED, "m * k and n * k must stay below 2^32");
+  MxGemmArgs g{};
+  for (int i = 0; i < n_out && m > 0; ++i) {
+    if (!outs[i] || ((uintptr_t)outs[i] & 1u))
+      return fail(VDN_ERR_INVALID_ARG, "outs[%d] must be non-NULL and 2-byte aligned", i);
+    g.out[i] = static_cast<__bf16*>(outs[i]);
+  }
+  const vdn_status s = check_device();
+  if (s != VDN_OK) return s;
+  g.a = a_codes;
+  g.as = a_scales;
+  g.b = w_codes;
+  g.bs = w_scales;
+  g.bias = bias;
+  g.m = (int)m;
+  g.n = (int)n;
+  g.k = (int)k;
+  g.cols_per_out = (int)(n / n_out);
+  const hipError_t e = launch_mx_gemm(g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "mxfp8 GEMM launch: %s", hipGetErrorString(e));
   return VDN_OK;
 }
 

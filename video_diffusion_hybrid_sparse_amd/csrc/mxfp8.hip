@@ -1,0 +1,299 @@
+// MXFP8 input-side projections on gfx950: the quantiser and the block-scaled GEMM.
+//
+// The model card of vdn-minimax-h3 (ModelScope, sections "Inference with Diffusers" and
+// "Inference with SGLang") runs the wide Linears in fp8 e4m3 after the LoRA adapters are
+// merged into the backbone, the fastest leg in MXFP8; the VDN-MiniMax-H3 article
+// (modelscope.csdn.net, method section, adaptation stage B) puts LoRA on the QKV
+// projections.  Here the token rows x [N, D] are quantised to MXFP8 and multiplied by
+// the merged, quantised weight of the five input-side projections (q, k, v and the two
+// gate logits) in one GEMM that writes each projection to its own bf16 tensor.
+//
+// Quantiser: one lane converts 8 consecutive elements; the 4 lanes of a 32-element block
+// exchange their maxima (two lane swaps); the lane that starts 4 blocks writes their 4
+// scale codes as one dword.  Scaling by the power of two is exact (v_ldexp); values are
+// clamped to +-448 and then converted by v_cvt_pk_fp8_f32, which rounds to nearest even
+// and turns magnitudes above the clamp into NaN codes, hence the clamp.
+//
+// GEMM: v_mfma_scale_f32_32x32x64_f8f6f4 takes, per lane, one E8M0 code for a 32-wide
+// k-block of its row (A row lane % 32, B row lane % 32, k-block lane / 32), so the MX
+// scales go straight into the matrix core and the accumulators hold exact products of
+// scaled values summed in float32.  Workgroup = 4 waves (one per SIMD) = a 256 x 256
+// output tile; each wave owns 128 x 128 (16 accumulator tiles of 32 x 32).  k advances in
+// stages of 64: A and B stage tiles (16 KB each, rows of 64 bytes) go from HBM into LDS
+// by global_load_lds (16 bytes per lane), four stage buffers deep, so three stages are in
+// flight while one is multiplied; one barrier per stage.  The 16-byte chunks of a row are
+// XOR-swizzled by (row / 4) mod 4, which makes every 16-lane LDS read of one chunk from 16
+// consecutive rows hit 16 distinct bank groups.  Scale codes of two stages (one dword per
+// row) are copied into LDS with the even stage's tiles and read once into registers.
+// Workgroups are numbered so that each XCD walks a contiguous range of output tiles,
+// 8 row tiles by all column tiles: the 32 tiles one XCD runs at a time share 8 A and 4 B
+// row panels in its L2.
+#include "mxfp8.h"
+
+namespace vdn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---- quantiser ------------------------------------------------------------------------
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& w, float (&v)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+
+template <bool LORA>
+__global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantArgs a) {
+  const int64_t n8 = a.rows * a.cols / 8;  // a multiple of 16 (cols % 128 == 0)
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;  // whole 16-lane groups leave together
+  const int64_t e0 = t * 8;
+  float v[8];
+  bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.x + e0), v);
+  if constexpr (LORA) {
+    const int64_t row = e0 / a.cols, col = e0 - row * a.cols;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t* bp = reinterpret_cast<const uint16_t*>(a.lora_b) + row * a.rank;
+    for (int r = 0; r < a.rank; ++r) {
+      const float br = __uint_as_float((uint32_t)bp[r] << 16);
+      float av[8];
+      bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.lora_a + (int64_t)r * a.cols + col), av);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(br, av[i], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fmaf(a.lora_scale, acc[i], v[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  // shared exponent floor(log2 amax) - 8; frexp gives amax = f 2^x with f in [0.5, 1)
+  int e = -127;
+  if (amax > 0.0f) e = imax(-127, imin(127, __builtin_amdgcn_frexp_expf(amax) - 1 - 8));
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = fminf(fmaxf(__builtin_amdgcn_ldexpf(v[i], -e), -448.0f), 448.0f);
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(s[6], s[7], w1, true);
+  *reinterpret_cast<uint2*>(a.codes + e0) = make_uint2((uint32_t)w0, (uint32_t)w1);
+  const int code = e + 127;
+  const int c1 = __shfl_down(code, 4), c2 = __shfl_down(code, 8), c3 = __shfl_down(code, 12);
+  if ((threadIdx.x & 15) == 0)
+    *reinterpret_cast<uint32_t*>(a.scales + e0 / 32) =
+        (uint32_t)code | ((uint32_t)c1 << 8) | ((uint32_t)c2 << 16) | ((uint32_t)c3 << 24);
+}
+
+// ---- GEMM -------------------------------------------------------------------------------
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kABytes = kBM * kBK, kBBytes = kBN * kBK, kStage = kABytes + kBBytes;  // 32 KB
+constexpr int kScBytes = (kBM + kBN) * 4;  // one scale dword per row, two stages
+constexpr int kGroupM = 8;                 // row tiles per tile group
+
+// Stage copies are written as inline asm so that the compiler, which cannot tell the four
+// stage buffers apart, does not wait for every copy in flight before each LDS read; the
+// waits are explicit (wait_barrier).  M0 holds the wave's LDS base; lane i's bytes land
+// at M0 + size * i.  One wait state separates the M0 write from the copy.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's copies are in flight, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_kernel(MxGemmArgs a) {
+  // four stage buffers (A tile then B tile), then two scale slots (A rows then B rows)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStage + 2 * kScBytes];
+
+  // ---- output tile of this workgroup
+  const int tiles_m = (a.m + kBM - 1) / kBM, tiles_n = (a.n + kBN - 1) / kBN;
+  const int per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
+  const int logical = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= tiles_m * tiles_n) return;
+  const int group = logical / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = imin(kGroupM, tiles_m - first_m);
+  const int within = logical - group * kGroupM * tiles_n;
+  const int row0 = (first_m + within % gm) * kBM, col0 = (within / gm) * kBN;
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nst = a.k / kBK;  // a multiple of 4
+
+  // ---- stage copies: instruction i of wave w fills tile rows (4 w + i) * 16 + lane / 4.
+  // Per-lane 32-bit offsets from a uniform base (rows * k < 2^32 is checked by the host).
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+    const uint32_t pc = (uint32_t)((lane & 3) ^ swz4(r)) * 16;
+    oa[i] = (uint32_t)imin(row0 + r, a.m - 1) * (uint32_t)a.k + pc;
+    ob[i] = (uint32_t)imin(col0 + r, a.n - 1) * (uint32_t)a.k + pc;
+  }
+  // scale dwords: wave w copies rows 64 w + lane of the A and B tiles
+  const uint32_t kb = (uint32_t)a.k / 32;
+  const uint32_t osa = (uint32_t)imin(row0 + wave * 64 + lane, a.m - 1) * kb;
+  const uint32_t osb = (uint32_t)imin(col0 + wave * 64 + lane, a.n - 1) * kb;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  const uint32_t wdst = __builtin_amdgcn_readfirstlane(lds0 + wave * 4096);
+  const uint32_t wsc = __builtin_amdgcn_readfirstlane(lds0 + 4 * kStage + wave * 256);
+
+  // copies of stage s into buffer B; an even stage also brings its pair's scales into
+  // slot P: 8 instructions, 10 for an even stage
+  auto issue = [&](int s, auto b, auto p, auto even) {
+    constexpr int B = decltype(b)::value, P = decltype(p)::value;
+    const uint8_t* ba = a.a + (size_t)s * kBK;
+    const uint8_t* bb = a.b + (size_t)s * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(ba, oa[i], wdst + B * kStage + i * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(bb, ob[i], wdst + B * kStage + kABytes + i * 1024);
+    if constexpr (decltype(even)::value) {
+      const uint32_t o = (uint32_t)(s / 2) * 4;
+      dma4(a.as + o, osa, wsc + P * kScBytes);
+      dma4(a.bs + o, osb, wsc + P * kScBytes + kBM * 4);
+    }
+  };
+
+  // MFMA operand reads.  In v_mfma_scale_f32_32x32x64_f8f6f4, lane l (row l % 32, half
+  // h = l / 32) holds k = 16 h + 0..15 in its first 16 bytes and k = 32 + 16 h + 0..15 in
+  // its last 16, and its scale covers k = 32 h .. 32 h + 31.  So half h reads 16-byte
+  // chunks h and 2 + h of the 64-byte stage row: the two halves of MX block 2 s + h are
+  // then the k-block whose scale half h supplies.
+  int rdo[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) rdo[e] = l32 * 64 + (((2 * e + half) ^ swz4(l32)) * 16);
+  auto operand = [&](const uint8_t* tile) -> i32x8 {
+    const uint4 lo = *reinterpret_cast<const uint4*>(tile + rdo[0]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(tile + rdo[1]);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  int sa[4], sb[4];
+
+  issue(0, IC<0>{}, IC<0>{}, IC<true>{});
+  issue(1, IC<1>{}, IC<0>{}, IC<false>{});
+  issue(2, IC<2>{}, IC<1>{}, IC<true>{});
+
+  // one stage s = 4 j + U from buffer U; the pair's scale byte is selected by U mod 2.
+  // W = copies allowed in flight once stage s has landed (those of stages s + 1 and
+  // s + 2: 8 each, plus 2 for the even one); ISSUE: start the copies of stage s + 3.
+  auto step = [&](int s, auto uc, auto wc, auto ic) {
+    constexpr int U = decltype(uc)::value;
+    wait_barrier<decltype(wc)::value>();
+    if constexpr (decltype(ic)::value)
+      issue(s + 3, IC<(U + 3) & 3>{}, IC<((U + 3) / 2) % 2>{}, IC<((U + 3) % 2 == 0)>{});
+    if constexpr (U % 2 == 0) {
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(lds + 4 * kStage + (U / 2) * kScBytes);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sa[t] = (int)(sc[wm * 128 + t * 32 + l32] >> (8 * half));
+        sb[t] = (int)(sc[kBM + wn * 128 + t * 32 + l32] >> (8 * half));
+      }
+    }
+    const uint8_t* A = lds + U * kStage + wm * 128 * kBK;
+    const uint8_t* B = lds + U * kStage + kABytes + wn * 128 * kBK;
+    i32x8 av[4], bv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      av[t] = operand(A + t * 32 * kBK);
+      bv[t] = operand(B + t * 32 * kBK);
+    }
+    constexpr int SEL = 2 * (U % 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv[j], acc[i][j], 0, 0, SEL, sa[i],
+                                                                     SEL, sb[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 4 < nst; s += 4) {
+    step(s, IC<0>{}, IC<18>{}, IC<true>{});
+    step(s + 1, IC<1>{}, IC<18>{}, IC<true>{});
+    step(s + 2, IC<2>{}, IC<18>{}, IC<true>{});
+    step(s + 3, IC<3>{}, IC<18>{}, IC<true>{});
+  }
+  // the last four stages (nst is a multiple of 4)
+  step(s, IC<0>{}, IC<18>{}, IC<true>{});
+  step(s + 1, IC<1>{}, IC<18>{}, IC<false>{});
+  step(s + 2, IC<2>{}, IC<8>{}, IC<false>{});
+  step(s + 3, IC<3>{}, IC<0>{}, IC<false>{});
+
+  // ---- epilogue: C[row][col], row = 8 (r / 4) + 4 half + r % 4 within a 32 x 32 tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cbase = col0 + wn * 128 + j * 32;  // 32 columns of one output
+    if (cbase >= a.n) continue;
+    const int o = cbase / a.cols_per_out;
+    const int c = cbase - o * a.cols_per_out + l32;
+    const float bias = a.bias ? a.bias[cbase + l32] : 0.0f;
+    __bf16* out = a.out[o];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rbase = row0 + wm * 128 + i * 32 + 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + 8 * (r / 4) + (r % 4);
+        if (row < a.m) out[(size_t)row * a.cols_per_out + c] = (__bf16)(acc[i][j][r] + bias);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant(const MxQuantArgs& a, hipStream_t stream) {
+  const int64_t n8 = a.rows * a.cols / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.lora_b)
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(mx_quant_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(mx_quant_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const MxGemmArgs& a, hipStream_t stream) {
+  if (a.m == 0 || a.n == 0) return hipSuccess;
+  if (a.k % 256 || a.k < 256 || a.n % 32 || a.cols_per_out % 32 || a.n / a.cols_per_out > kMxMaxOut)
+    return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)((a.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mx_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace vdn

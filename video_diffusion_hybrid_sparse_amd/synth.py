@@ -17,6 +17,11 @@ Recipe (stated once so a reader can regenerate any tensor):
   or for the fp8 workload OCP e4m3fn codes with one per-tensor scale amax / 448 taken
   over the bf16-rounded tensor.  The fp8 workload also keeps those bf16 tensors as the
   linear branch's q/k/v.
+* Input-side projections (MXFP8 path), indices 20-24: token rows x [N, D] = n with every
+  97th channel multiplied by 16 (activation outlier channels); the stacked q/k/v/gate
+  weight w [5 H d, D] = n / sqrt(D); bias [5 H d] = 0.02 n (float32); LoRA factors
+  lora_b [5 H d, r] = 0.02 n and lora_a [r, D] = n / sqrt(r), scale alpha / r with
+  alpha = 2 r.  All bf16 except the bias.
 """
 from __future__ import annotations
 
@@ -202,3 +207,27 @@ def membership_probe_inputs(shape: LayerShape) -> LayerInputs:
         inp.v, inp.v_scale = quantize_e4m3(v.to(torch.bfloat16))
     inp.q_lin, inp.k_lin, inp.v_lin = e0.to(at), e0.to(at), v.to(at)
     return inp
+
+
+@dataclass
+class ProjectionInputs:
+    """Inputs of the layer's input-side projections (see the module recipe)."""
+    x: torch.Tensor        # [N, D] bf16
+    w: torch.Tensor        # [5 H d, D] bf16
+    bias: torch.Tensor     # [5 H d] float32
+    lora_b: torch.Tensor   # [5 H d, r] bf16
+    lora_a: torch.Tensor   # [r, D] bf16
+    lora_scale: float
+
+
+def projection_inputs(n_tokens: int, model_dim: int, out_features: int, rank: int = 64,
+                      seed: int = 7001) -> ProjectionInputs:
+    D = model_dim
+    x = _normal(seed, 20, n_tokens * D).reshape(n_tokens, D)
+    x[:, ::97] *= 16.0
+    w = _normal(seed, 21, out_features * D).reshape(out_features, D) / np.float32(np.sqrt(D))
+    bias = 0.02 * _normal(seed, 22, out_features)
+    lb = 0.02 * _normal(seed, 23, out_features * rank).reshape(out_features, rank)
+    la = _normal(seed, 24, rank * D).reshape(rank, D) / np.float32(np.sqrt(rank))
+    return ProjectionInputs(x=_round(x, "bf16"), w=_round(w, "bf16"), bias=torch.from_numpy(bias.astype(np.float32)),
+                            lora_b=_round(lb, "bf16"), lora_a=_round(la, "bf16"), lora_scale=2.0)
