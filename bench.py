@@ -26,6 +26,7 @@ import time
 
 METRIC = "hybrid-attn layer ms + TFLOP/s (% MFMA peak) at 768p 60-frame shape, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
@@ -101,6 +102,8 @@ def main() -> int:
     ap.add_argument("--linear-variant", type=int, default=0, choices=(0, 1))
     ap.add_argument("--delta-beta", type=float, default=0.5)
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead of the forward")
+    ap.add_argument("--projections", action="store_true",
+                    help="time the MXFP8 input-side projections (quantise x, block-scaled GEMM) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the layer is not sharded across GPUs (asked for --gpus {args.gpus})",
@@ -112,6 +115,8 @@ def main() -> int:
     from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth, workload
 
     shape = shapes.P768
+    if args.projections:
+        return bench_projections(args, shape)
     if args.linear_variant == 1:
         shape = dataclasses.replace(shape, name=f"{shape.name}_delta", linear_variant=1, delta_beta=args.delta_beta)
     log("bench: generating inputs", shape.name)
@@ -208,6 +213,80 @@ def bench_backward(args, shape, inp, dl) -> int:
         "data": "synthetic: seeded N(0,1) activations, gate logits and upstream gradient, 768p layer shape",
         "config": {"workload": shape.name + "_backward", "layer_backward_tflop": round(fl["total"] / 1e12, 3),
                    "includes": "forward recompute (not counted in the FLOPs)"},
+    }), flush=True)
+    return 0
+
+
+def bench_projections(args, shape) -> int:
+    """Times the MXFP8 input-side projections of the 768p layer: quantise the token rows
+    x [N, D] (bf16) and multiply by the LoRA-merged, quantised q/k/v/gate weight
+    [5 H d, D] into five bf16 outputs.  The weight is prepared once, outside the timed
+    region, as a served model would hold it."""
+    import torch
+
+    from video_diffusion_hybrid_sparse_amd import binding, synth
+
+    N, D, hd = shape.frames * shape.tokens_per_frame, shape.model_dim, shape.heads * shape.head_dim
+    n = 5 * hd
+    log("bench: generating projection inputs", N, D, n)
+    p = synth.projection_inputs(N, D, n, rank=64, seed=shape.seed)
+    dev = torch.device("cuda")
+    x, w, bias = p.x.to(dev), p.w.to(dev), p.bias.to(dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    xc, xs = torch.empty(N, D, **u8), torch.empty(N, D // 32, **u8)
+    wc, ws = torch.empty(n, D, **u8), torch.empty(n, D // 32, **u8)
+    binding.mxfp8_quantize(w, wc, ws, p.lora_b.to(dev), p.lora_a.to(dev), p.lora_scale)
+    outs = [torch.empty(N, hd, dtype=torch.bfloat16, device=dev) for _ in range(5)]
+
+    def step():
+        binding.mxfp8_quantize(x, xc, xs)
+        binding.mxfp8_linear(xc, xs, wc, ws, outs, bias)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[3 * i].record()
+        binding.mxfp8_quantize(x, xc, xs)
+        ev[3 * i + 1].record()
+        binding.mxfp8_linear(xc, xs, wc, ws, outs, bias)
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    q_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)) / args.steps
+    g_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)) / args.steps
+    gemm_flop = 2.0 * N * D * n
+    q_bytes = N * D * 2 + N * D + N * D // 32  # read bf16, write codes and scales
+    # the same product in bf16 through torch (hipBLASLt), for context
+    xt, wt = x, w.t().contiguous()
+    for _ in range(2):
+        torch.mm(xt, wt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        torch.mm(xt, wt)
+    e1.record()
+    torch.cuda.synchronize()
+    bf16_ms = e0.elapsed_time(e1) / 3
+    achieved = gemm_flop / (g_ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "MXFP8 input-side projections (q/k/v/gate) TFLOP/s at the 768p layer shape, 1 GPU",
+        "value": round(gemm_flop / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8 (MXFP8 e4m3, E8M0 per 32), fp32 accumulate",
+        "data": "synthetic: seeded N(0,1) token rows with outlier channels, N(0,1/D) weights, rank-64 LoRA",
+        "config": {"workload": f"{shape.name}_input_projections", "tokens": N, "model_dim": D, "out_features": n,
+                   "outputs": 5, "gemm_tflop": round(gemm_flop / 1e12, 3)},
+        "roofline": {"kernel": "mx_gemm_kernel", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None},
+        "steps_ms": {"quantize_x": round(q_ms, 4), "gemm": round(g_ms, 4)},
+        "steps_rate": {"quantize_x_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "gemm_tflops": round(achieved, 1)},
+        "context": {"bf16_torch_mm_ms": round(bf16_ms, 3),
+                    "bf16_torch_mm_tflops": round(gemm_flop / (bf16_ms * 1e-3) / 1e12, 1)},
     }), flush=True)
     return 0
 

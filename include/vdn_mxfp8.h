@@ -62,12 +62,13 @@ vdn_status vdn_mxfp8_quantize_lora(const void* w, const void* lora_b, const void
  * [n, k]; the sum is accumulated in float32 by the matrix cores and rounded once to bf16
  * (nearest even).  With n_out = 5 and W the stacked q, k, v, softmax-gate and
  * linear-gate weights, the five outputs are the layer's q, k, v, g_s and g_l.
- *   a_codes  uint8 [m, k], 16-byte aligned;  a_scales uint8 [m, k / 32], 4-byte aligned.
- *   w_codes  uint8 [n, k], 16-byte aligned;  w_scales uint8 [n, k / 32], 4-byte aligned.
- *   bias     float32 [n], 4-byte aligned, or NULL for none.
- *   m >= 0;  k a positive multiple of 256;  1 <= n_out <= 8;  n / n_out a multiple of 32;
+ *   a_codes  uint8 [m, k], 16-byte aligned;  a_scales uint8 [m, k / 32], 16-byte aligned.
+ *   w_codes  uint8 [n, k], 16-byte aligned;  w_scales uint8 [n, k / 32], 16-byte aligned.
+ *   bias     float32 [n], 16-byte aligned, or NULL for none.
+ *   m >= 0;  k a positive multiple of 512;  1 <= n_out <= 8;  n / n_out a multiple of 32;
  *   m * k and n * k below 2^32 (else VDN_ERR_UNSUPPORTED).
- *   outs     host array of n_out device pointers, each bf16 [m, n / n_out], written. */
+ *   outs     host array of n_out device pointers, each bf16 [m, n / n_out], 8-byte
+ *            aligned, written. */
 vdn_status vdn_mxfp8_linear(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
                             const uint8_t* w_scales, const float* bias, int64_t m, int64_t n, int64_t k, int32_t n_out,
                             void* const* outs, void* stream);

@@ -230,16 +230,16 @@ def test_mxfp8_argument_checks_launch_nothing():
 
     assert lin() == NO_DEVICE
     assert lin(bias=0x50000) == NO_DEVICE
-    assert lin(bias=0x50002) == INVALID
-    assert lin(k=384) == UNSUPPORTED  # k % 256
+    assert lin(bias=0x50004) == INVALID  # bias 16-byte aligned
+    assert lin(k=768) == UNSUPPORTED  # k % 512
     assert lin(n=600) == UNSUPPORTED  # n / n_out = 120 is not a multiple of 32
     assert lin(n_out=9) == INVALID
     assert lin(n_out=0) == INVALID
-    assert lin(m=(1 << 24) - 1, k=1 << 8) == NO_DEVICE
-    assert lin(m=1 << 24, k=1 << 8) == UNSUPPORTED  # m * k = 2^32
+    assert lin(m=(1 << 23) - 1, k=1 << 9) == NO_DEVICE
+    assert lin(m=1 << 23, k=1 << 9) == UNSUPPORTED  # m * k = 2^32
     assert lin(ac=None) == INVALID
     assert lin(wc=wc + 4) == INVALID
-    assert lin(ws=ws + 1) == INVALID
+    assert lin(ws=ws + 4) == INVALID  # scales 16-byte aligned
     bad = (ctypes.c_void_p * 5)(*[0x100000 * (i + 1) for i in range(4)], None)
     assert lin(o=bad) == INVALID
     assert "outs[4]" in binding.last_error()

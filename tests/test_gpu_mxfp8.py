@@ -103,11 +103,11 @@ def test_no_rows_is_a_no_op():
     binding.mxfp8_quantize(x, torch.empty(0, 128, dtype=torch.uint8, device="cuda"),
                            torch.empty(0, 4, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
-    e = torch.empty(0, 256, dtype=torch.uint8, device="cuda")
     outs = [torch.empty(0, 64, dtype=torch.bfloat16, device="cuda") for _ in range(5)]
-    w = torch.zeros(320, 256, dtype=torch.uint8, device="cuda")
-    binding.mxfp8_linear(e, torch.empty(0, 8, dtype=torch.uint8, device="cuda"), w,
-                         torch.zeros(320, 8, dtype=torch.uint8, device="cuda"), outs)
+    binding.mxfp8_linear(torch.empty(0, 512, dtype=torch.uint8, device="cuda"),
+                         torch.empty(0, 16, dtype=torch.uint8, device="cuda"),
+                         torch.zeros(320, 512, dtype=torch.uint8, device="cuda"),
+                         torch.zeros(320, 16, dtype=torch.uint8, device="cuda"), outs)
     torch.cuda.synchronize()
 
 
@@ -160,12 +160,12 @@ def test_quantize_lora(rows, cols, rank):
 # ---- GEMM -----------------------------------------------------------------------------------
 
 GEMM_CASES = [  # m, n_out, cols_per_out, k, bias
-    (1, 5, 64, 256, True),
-    (37, 5, 64, 512, False),
-    (300, 5, 32, 256, True),
-    (513, 1, 256, 768, True),
+    (1, 5, 64, 512, True),
+    (37, 5, 64, 1024, False),
+    (300, 5, 32, 512, True),
+    (513, 1, 256, 1536, True),
     (257, 8, 96, 1024, True),
-    (600, 3, 160, 512, False),
+    (600, 3, 160, 4608, False),
 ]
 
 

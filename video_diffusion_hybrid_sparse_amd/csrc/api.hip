@@ -541,10 +541,10 @@ vdn_status vdn_mxfp8_linear(const uint8_t* a_codes, const uint8_t* a_scales, con
   if (m > 0 && (!a_codes || !a_scales || !w_codes || !w_scales || !outs))
     return fail(VDN_ERR_INVALID_ARG, "codes, scales and outs must be non-NULL");
   if (!aligned16(a_codes) || !aligned16(w_codes)) return fail(VDN_ERR_INVALID_ARG, "codes must be 16-byte aligned");
-  if (((uintptr_t)a_scales & 3u) || ((uintptr_t)w_scales & 3u) || ((uintptr_t)bias & 3u))
-    return fail(VDN_ERR_INVALID_ARG, "scales and bias must be 4-byte aligned");
+  if (!aligned16(a_scales) || !aligned16(w_scales)) return fail(VDN_ERR_INVALID_ARG, "scales must be 16-byte aligned");
+  if (!aligned16(bias)) return fail(VDN_ERR_INVALID_ARG, "bias must be 16-byte aligned");
   if (m < 0 || n <= 0 || k <= 0) return fail(VDN_ERR_INVALID_ARG, "need m >= 0, n > 0, k > 0");
-  if (k % 256 != 0) return fail(VDN_ERR_UNSUPPORTED, "k must be a multiple of 256 (got %lld)", (long long)k);
+  if (k % 512 != 0) return fail(VDN_ERR_UNSUPPORTED, "k must be a multiple of 512 (got %lld)", (long long)k);
   if (n_out < 1 || n_out > kMxMaxOut)
     return fail(VDN_ERR_INVALID_ARG, "n_out must lie in [1, %d] (got %d)", kMxMaxOut, n_out);
   if (n % n_out != 0 || (n / n_out) % 32 != 0)
@@ -553,8 +553,8 @@ vdn_status vdn_mxfp8_linear(const uint8_t* a_codes, const uint8_t* a_scales, con
     return fail(VDN_ERR_UNSUPPORTED, "m * k and n * k must stay below 2^32");
   MxGemmArgs g{};
   for (int i = 0; i < n_out && m > 0; ++i) {
-    if (!outs[i] || ((uintptr_t)outs[i] & 1u))
-      return fail(VDN_ERR_INVALID_ARG, "outs[%d] must be non-NULL and 2-byte aligned", i);
+    if (!outs[i] || ((uintptr_t)outs[i] & 7u))
+      return fail(VDN_ERR_INVALID_ARG, "outs[%d] must be non-NULL and 8-byte aligned", i);
     g.out[i] = static_cast<__bf16*>(outs[i]);
   }
   const vdn_status s = check_device();

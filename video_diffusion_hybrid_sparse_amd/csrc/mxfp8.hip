@@ -95,19 +95,16 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(MxQuantArgs a) {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kABytes = kBM * kBK, kBBytes = kBN * kBK, kStage = kABytes + kBBytes;  // 32 KB
-constexpr int kScBytes = (kBM + kBN) * 4;  // one scale dword per row, two stages
+constexpr int kWin = 8;                    // stages per scale window: 16 scale bytes per row
+constexpr int kScSlot = (kBM + kBN) * 16;  // one window of A then B row scales (8 KB)
 constexpr int kGroupM = 8;                 // row tiles per tile group
 
 // Stage copies are written as inline asm so that the compiler, which cannot tell the four
 // stage buffers apart, does not wait for every copy in flight before each LDS read; the
-// waits are explicit (wait_barrier).  M0 holds the wave's LDS base; lane i's bytes land
-// at M0 + size * i.  One wait state separates the M0 write from the copy.
+// waits are explicit (wait_barrier).  M0 holds the wave's LDS base; lane i's 16 bytes
+// land at M0 + 16 i.  One wait state separates the M0 write from the copy.
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
 
@@ -125,8 +122,8 @@ struct IC {
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_kernel(MxGemmArgs a) {
-  // four stage buffers (A tile then B tile), then two scale slots (A rows then B rows)
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStage + 2 * kScBytes];
+  // four stage buffers (A tile then B tile), then two scale windows (A rows then B rows)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStage + 2 * kScSlot];
 
   // ---- output tile of this workgroup
   const int tiles_m = (a.m + kBM - 1) / kBM, tiles_n = (a.n + kBN - 1) / kBN;
@@ -142,10 +139,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int nst = a.k / kBK;  // a multiple of 4
+  const int nst = a.k / kBK;  // a multiple of 8
 
-  // ---- stage copies: instruction i of wave w fills tile rows (4 w + i) * 16 + lane / 4.
-  // Per-lane 32-bit offsets from a uniform base (rows * k < 2^32 is checked by the host).
+  // ---- stage copies: copy i of wave w fills tile rows (4 w + i) * 16 + lane / 4 (A for
+  // i < 4, B after).  Per-lane 32-bit offsets from a uniform base (rows * k < 2^32).
   uint32_t oa[4], ob[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -154,32 +151,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     oa[i] = (uint32_t)imin(row0 + r, a.m - 1) * (uint32_t)a.k + pc;
     ob[i] = (uint32_t)imin(col0 + r, a.n - 1) * (uint32_t)a.k + pc;
   }
-  // scale dwords: wave w copies rows 64 w + lane of the A and B tiles
+  // scale windows: wave w copies the 16 window bytes of A and B rows 64 w + lane
   const uint32_t kb = (uint32_t)a.k / 32;
   const uint32_t osa = (uint32_t)imin(row0 + wave * 64 + lane, a.m - 1) * kb;
   const uint32_t osb = (uint32_t)imin(col0 + wave * 64 + lane, a.n - 1) * kb;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
   const uint32_t wdst = __builtin_amdgcn_readfirstlane(lds0 + wave * 4096);
-  const uint32_t wsc = __builtin_amdgcn_readfirstlane(lds0 + 4 * kStage + wave * 256);
+  const uint32_t wsc = __builtin_amdgcn_readfirstlane(lds0 + 4 * kStage + wave * 1024);
 
-  // copies of stage s into buffer B; an even stage also brings its pair's scales into
-  // slot P: 8 instructions, 10 for an even stage
-  auto issue = [&](int s, auto b, auto p, auto even) {
-    constexpr int B = decltype(b)::value, P = decltype(p)::value;
-    const uint8_t* ba = a.a + (size_t)s * kBK;
-    const uint8_t* bb = a.b + (size_t)s * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(ba, oa[i], wdst + B * kStage + i * 1024);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(bb, ob[i], wdst + B * kStage + kABytes + i * 1024);
-    if constexpr (decltype(even)::value) {
-      const uint32_t o = (uint32_t)(s / 2) * 4;
-      dma4(a.as + o, osa, wsc + P * kScBytes);
-      dma4(a.bs + o, osb, wsc + P * kScBytes + kBM * 4);
-    }
+  // copy i of stage s into buffer B
+  auto copy = [&](int s, auto b, int i) {
+    constexpr int B = decltype(b)::value;
+    if (i < 4) dma16(a.a + (size_t)s * kBK, oa[i], wdst + B * kStage + i * 1024);
+    else dma16(a.b + (size_t)s * kBK, ob[i - 4], wdst + B * kStage + kABytes + (i - 4) * 1024);
+  };
+  // the scale window w (stages 8 w .. 8 w + 7) into slot w % 2: two copies
+  auto copy_scales = [&](int w) {
+    const uint32_t slot = wsc + (uint32_t)(w & 1) * kScSlot;
+    dma16(a.as + (size_t)w * 16, osa, slot);
+    dma16(a.bs + (size_t)w * 16, osb, slot + kBM * 16);
   };
 
-  // MFMA operand reads.  In v_mfma_scale_f32_32x32x64_f8f6f4, lane l (row l % 32, half
+  // MFMA operands.  In v_mfma_scale_f32_32x32x64_f8f6f4, lane l (row l % 32, half
   // h = l / 32) holds k = 16 h + 0..15 in its first 16 bytes and k = 32 + 16 h + 0..15 in
   // its last 16, and its scale covers k = 32 h .. 32 h + 31.  So half h reads 16-byte
   // chunks h and 2 + h of the 64-byte stage row: the two halves of MX block 2 s + h are
@@ -187,10 +180,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int rdo[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) rdo[e] = l32 * 64 + (((2 * e + half) ^ swz4(l32)) * 16);
-  auto operand = [&](const uint8_t* tile) -> i32x8 {
-    const uint4 lo = *reinterpret_cast<const uint4*>(tile + rdo[0]);
-    const uint4 hi = *reinterpret_cast<const uint4*>(tile + rdo[1]);
-    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  auto read16 = [&](int off) -> uint4 { return *reinterpret_cast<const uint4*>(lds + off); };
+  // register slot r (0..15) of a stage's operands: A tile t at 2 t + e, B tile t at
+  // 8 + 2 t + e (e: low or high 16 bytes)
+  auto operand_read = [&](auto b, int r) -> uint4 {
+    constexpr int B = decltype(b)::value;
+    const int t = (r >> 1) & 3, e = r & 1;
+    const int base = r < 8 ? B * kStage + (wm * 128 + t * 32) * kBK : B * kStage + kABytes + (wn * 128 + t * 32) * kBK;
+    return read16(base + rdo[e]);
+  };
+  // the reads of the next stage go out in the order its first MFMAs use them: A tile 0,
+  // B tiles 0..3, then A tiles 1..3
+  constexpr int kReadOrder[16] = {0, 1, 8, 9, 10, 11, 12, 13, 14, 15, 2, 3, 4, 5, 6, 7};
+  // scale dwords of pair P (stages 2P, 2P + 1) for this lane's 4 A and 4 B rows; the
+  // byte of stage 2 P + j for k-block h sits at bit 8 (2 j + h) of the dword, shifted so
+  // that op_sel 2 j picks it
+  auto scale_read = [&](int slot, int dw, int (&sa_)[4], int (&sb_)[4]) {
+    const uint8_t* sc = lds + 4 * kStage + slot * kScSlot + dw * 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sa_[t] = (int)(*reinterpret_cast<const uint32_t*>(sc + (wm * 128 + t * 32 + l32) * 16) >> (8 * half));
+      sb_[t] = (int)(*reinterpret_cast<const uint32_t*>(sc + kBM * 16 + (wn * 128 + t * 32 + l32) * 16) >> (8 * half));
+    }
   };
 
   f32x16 acc[4][4];
@@ -198,74 +209,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  int sa[4], sb[4];
+  uint4 R[2][16];    // operand registers of two stages
+  int SA[2][4], SB[2][4];  // scale dwords of two pairs
 
-  issue(0, IC<0>{}, IC<0>{}, IC<true>{});
-  issue(1, IC<1>{}, IC<0>{}, IC<false>{});
-  issue(2, IC<2>{}, IC<1>{}, IC<true>{});
-
-  // one stage s = 4 j + U from buffer U; the pair's scale byte is selected by U mod 2.
-  // W = copies allowed in flight once stage s has landed (those of stages s + 1 and
-  // s + 2: 8 each, plus 2 for the even one); ISSUE: start the copies of stage s + 3.
-  auto step = [&](int s, auto uc, auto wc, auto ic) {
-    constexpr int U = decltype(uc)::value;
-    wait_barrier<decltype(wc)::value>();
-    if constexpr (decltype(ic)::value)
-      issue(s + 3, IC<(U + 3) & 3>{}, IC<((U + 3) / 2) % 2>{}, IC<((U + 3) % 2 == 0)>{});
-    if constexpr (U % 2 == 0) {
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(lds + 4 * kStage + (U / 2) * kScBytes);
+  // prologue: stages 0, 1, 2 in flight (window 0 with stage 0); stage 0 into registers
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        sa[t] = (int)(sc[wm * 128 + t * 32 + l32] >> (8 * half));
-        sb[t] = (int)(sc[kBM + wn * 128 + t * 32 + l32] >> (8 * half));
+  for (int i = 0; i < 8; ++i) copy(0, IC<0>{}, i);
+  copy_scales(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy(1, IC<1>{}, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy(2, IC<2>{}, i);
+  wait_barrier<16>();
+  scale_read(0, 0, SA[0], SB[0]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) R[0][r] = operand_read(IC<0>{}, r);
+
+  // One stage s = s8 + U (U = s mod 8): wait for stage s + 1 and meet the other waves;
+  // then the 16 MFMAs of stage s, with the copies of stage s + 3 (and of a scale window)
+  // and the register reads of stage s + 1 spread between them.  W: copies allowed in
+  // flight once stage s + 1 has landed (-1: no wait); COPY: copy stage s + 3; NEXT: read
+  // stage s + 1.
+  auto step = [&](int s8, auto uc, auto wc, auto cc, auto nc) {
+    constexpr int U = decltype(uc)::value, W = decltype(wc)::value;
+    constexpr bool COPY = decltype(cc)::value, NEXT = decltype(nc)::value;
+    constexpr int CUR = U % 2, NXT = 1 - CUR, SCUR = (U / 2) % 2, SEL = 2 * (U % 2);
+    const int s = s8 + U;
+    if constexpr (W >= 0) wait_barrier<W>();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = q >> 2, j = q & 3;
+      const i32x8 av = __builtin_bit_cast(i32x8, (uint4[2]){R[CUR][2 * i], R[CUR][2 * i + 1]});
+      const i32x8 bv = __builtin_bit_cast(i32x8, (uint4[2]){R[CUR][8 + 2 * j], R[CUR][8 + 2 * j + 1]});
+      // the weight tile is the A operand: acc[i][j] holds C^T, a lane one token row
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, SEL, SB[SCUR][j], SEL,
+                                                                   SA[SCUR][i]);
+      if constexpr (COPY) {
+        if (q % 2 == 0) copy(s + 3, IC<(U + 3) & 3>{}, q / 2);
+        if constexpr ((U + 3) % kWin == 0)
+          if (q == 15) copy_scales((s + 3) / kWin);
       }
+      if constexpr (NEXT) {
+        R[NXT][kReadOrder[q]] = operand_read(IC<(U + 1) & 3>{}, kReadOrder[q]);
+        if constexpr (U % 2 == 1)
+          if (q == 15) scale_read(((s + 1) / kWin) & 1, ((U + 1) / 2) % 4, SA[1 - SCUR], SB[1 - SCUR]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const uint8_t* A = lds + U * kStage + wm * 128 * kBK;
-    const uint8_t* B = lds + U * kStage + kABytes + wn * 128 * kBK;
-    i32x8 av[4], bv[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      av[t] = operand(A + t * 32 * kBK);
-      bv[t] = operand(B + t * 32 * kBK);
-    }
-    constexpr int SEL = 2 * (U % 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv[j], acc[i][j], 0, 0, SEL, sa[i],
-                                                                     SEL, sb[j]);
-    __builtin_amdgcn_sched_barrier(0);
   };
-  int s = 0;
-  for (; s + 4 < nst; s += 4) {
-    step(s, IC<0>{}, IC<18>{}, IC<true>{});
-    step(s + 1, IC<1>{}, IC<18>{}, IC<true>{});
-    step(s + 2, IC<2>{}, IC<18>{}, IC<true>{});
-    step(s + 3, IC<3>{}, IC<18>{}, IC<true>{});
+  int s8 = 0;
+  for (; s8 + kWin < nst; s8 += kWin) {
+    step(s8, IC<0>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<1>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<2>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<3>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<4>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<5>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<6>{}, IC<10>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<7>{}, IC<8>{}, IC<true>{}, IC<true>{});
   }
-  // the last four stages (nst is a multiple of 4)
-  step(s, IC<0>{}, IC<18>{}, IC<true>{});
-  step(s + 1, IC<1>{}, IC<18>{}, IC<false>{});
-  step(s + 2, IC<2>{}, IC<8>{}, IC<false>{});
-  step(s + 3, IC<3>{}, IC<0>{}, IC<false>{});
+  // the last eight stages
+  step(s8, IC<0>{}, IC<8>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<1>{}, IC<8>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<2>{}, IC<8>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<3>{}, IC<8>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<4>{}, IC<8>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<5>{}, IC<8>{}, IC<false>{}, IC<true>{});
+  step(s8, IC<6>{}, IC<0>{}, IC<false>{}, IC<true>{});
+  step(s8, IC<7>{}, IC<-1>{}, IC<false>{}, IC<false>{});
+  // keep the last MFMAs here: otherwise they sink into the branches of the epilogue, and
+  // the operands of the last stages stay live (and spill) across them
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
 
-  // ---- epilogue: C[row][col], row = 8 (r / 4) + 4 half + r % 4 within a 32 x 32 tile
+  // ---- epilogue.  acc[i][j][4 g + e] is output column 8 g + 4 half + e of column tile j
+  // for the token l32 of row tile i: four consecutive columns per g, stored as 8 bytes.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int cbase = col0 + wn * 128 + j * 32;  // 32 columns of one output
     if (cbase >= a.n) continue;
     const int o = cbase / a.cols_per_out;
-    const int c = cbase - o * a.cols_per_out + l32;
-    const float bias = a.bias ? a.bias[cbase + l32] : 0.0f;
+    const int c = cbase - o * a.cols_per_out + 4 * half;
     __bf16* out = a.out[o];
+    float4 bias[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bias[g] = a.bias ? *reinterpret_cast<const float4*>(a.bias + cbase + 8 * g + 4 * half)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rbase = row0 + wm * 128 + i * 32 + 4 * half;
+      const int row = row0 + wm * 128 + i * 32 + l32;
+      if (row >= a.m) continue;
+      __bf16* orow = out + (size_t)row * a.cols_per_out + c;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + 8 * (r / 4) + (r % 4);
-        if (row < a.m) out[(size_t)row * a.cols_per_out + c] = (__bf16)(acc[i][j][r] + bias);
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& v = acc[i][j];
+        *reinterpret_cast<uint2*>(orow + 8 * g) =
+            make_uint2(pack_bf16x2(v[4 * g] + bias[g].x, v[4 * g + 1] + bias[g].y),
+                       pack_bf16x2(v[4 * g + 2] + bias[g].z, v[4 * g + 3] + bias[g].w));
       }
     }
   }
@@ -287,7 +330,7 @@ hipError_t launch_mx_quant(const MxQuantArgs& a, hipStream_t stream) {
 
 hipError_t launch_mx_gemm(const MxGemmArgs& a, hipStream_t stream) {
   if (a.m == 0 || a.n == 0) return hipSuccess;
-  if (a.k % 256 || a.k < 256 || a.n % 32 || a.cols_per_out % 32 || a.n / a.cols_per_out > kMxMaxOut)
+  if (a.k % 512 || a.k < 512 || a.n % 32 || a.cols_per_out % 32 || a.n / a.cols_per_out > kMxMaxOut)
     return hipErrorInvalidValue;
   const int64_t tiles = (int64_t)((a.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
   const int64_t grid = (tiles + 7) / 8 * 8;
