@@ -20,8 +20,9 @@
 // scaled values summed in float32.  Workgroup = 4 waves (one per SIMD) = a 256 x 256
 // output tile; each wave owns 128 x 128 (16 accumulator tiles of 32 x 32).  k advances in
 // stages of 64: A and B stage tiles (16 KB each, rows of 64 bytes) go from HBM into LDS
-// by global_load_lds (16 bytes per lane), four stage buffers deep, so three stages are in
-// flight while one is multiplied; one barrier per stage.  The 16-byte chunks of a row are
+// by global_load_lds (16 bytes per lane), four stage buffers deep: a stage's operands
+// are read into registers one stage ahead, so while stage s is multiplied, stages s + 2
+// .. s + 4 are in flight; one barrier per stage.  The 16-byte chunks of a row are
 // XOR-swizzled by (row / 4) mod 4, which makes every 16-lane LDS read of one chunk from 16
 // consecutive rows hit 16 distinct bank groups.  Scale codes of two stages (one dword per
 // row) are copied into LDS with the even stage's tiles and read once into registers.
@@ -108,10 +109,11 @@ __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint3
                : "memory", "m0");
 }
 
-// Wait until at most N of this wave's copies are in flight, then meet the other waves.
+// Wait until at most N of this wave's copies are in flight and its LDS reads are done,
+// then meet the other waves.
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int V>
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   uint4 R[2][16];    // operand registers of two stages
   int SA[2][4], SB[2][4];  // scale dwords of two pairs
 
-  // prologue: stages 0, 1, 2 in flight (window 0 with stage 0); stage 0 into registers
+  // prologue: stages 0..3 in flight (window 0 with stage 0); stage 0 into registers
 #pragma unroll
   for (int i = 0; i < 8; ++i) copy(0, IC<0>{}, i);
   copy_scales(0);
@@ -220,16 +222,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < 8; ++i) copy(1, IC<1>{}, i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) copy(2, IC<2>{}, i);
-  wait_barrier<16>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy(3, IC<3>{}, i);
+  wait_barrier<24>();
   scale_read(0, 0, SA[0], SB[0]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) R[0][r] = operand_read(IC<0>{}, r);
 
   // One stage s = s8 + U (U = s mod 8): wait for stage s + 1 and meet the other waves;
-  // then the 16 MFMAs of stage s, with the copies of stage s + 3 (and of a scale window)
-  // and the register reads of stage s + 1 spread between them.  W: copies allowed in
-  // flight once stage s + 1 has landed (-1: no wait); COPY: copy stage s + 3; NEXT: read
-  // stage s + 1.
+  // then the 16 MFMAs of stage s, with the copies of stage s + 4 (and of a scale window)
+  // and the register reads of stage s + 1 spread between them.  Stage s + 4 goes into
+  // the buffer of stage s, whose operands every wave holds in registers by then.  W:
+  // copies allowed in flight once stage s + 1 has landed (those of stages s + 2 and
+  // s + 3; -1: no wait); COPY: copy stage s + 4; NEXT: read stage s + 1.
   auto step = [&](int s8, auto uc, auto wc, auto cc, auto nc) {
     constexpr int U = decltype(uc)::value, W = decltype(wc)::value;
     constexpr bool COPY = decltype(cc)::value, NEXT = decltype(nc)::value;
@@ -245,9 +250,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, SEL, SB[SCUR][j], SEL,
                                                                    SA[SCUR][i]);
       if constexpr (COPY) {
-        if (q % 2 == 0) copy(s + 3, IC<(U + 3) & 3>{}, q / 2);
-        if constexpr ((U + 3) % kWin == 0)
-          if (q == 15) copy_scales((s + 3) / kWin);
+        if (q % 2 == 0) copy(s + 4, IC<U & 3>{}, q / 2);
+        if constexpr ((U + 4) % kWin == 0)
+          if (q == 15) copy_scales((s + 4) / kWin);
       }
       if constexpr (NEXT) {
         R[NXT][kReadOrder[q]] = operand_read(IC<(U + 1) & 3>{}, kReadOrder[q]);
@@ -259,21 +264,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   int s8 = 0;
   for (; s8 + kWin < nst; s8 += kWin) {
-    step(s8, IC<0>{}, IC<8>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<1>{}, IC<8>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<2>{}, IC<8>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<3>{}, IC<8>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<4>{}, IC<8>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<5>{}, IC<8>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<6>{}, IC<10>{}, IC<true>{}, IC<true>{});
-    step(s8, IC<7>{}, IC<8>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<0>{}, IC<16>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<1>{}, IC<16>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<2>{}, IC<16>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<3>{}, IC<16>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<4>{}, IC<16>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<5>{}, IC<18>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<6>{}, IC<18>{}, IC<true>{}, IC<true>{});
+    step(s8, IC<7>{}, IC<16>{}, IC<true>{}, IC<true>{});
   }
   // the last eight stages
-  step(s8, IC<0>{}, IC<8>{}, IC<true>{}, IC<true>{});
-  step(s8, IC<1>{}, IC<8>{}, IC<true>{}, IC<true>{});
-  step(s8, IC<2>{}, IC<8>{}, IC<true>{}, IC<true>{});
-  step(s8, IC<3>{}, IC<8>{}, IC<true>{}, IC<true>{});
-  step(s8, IC<4>{}, IC<8>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<0>{}, IC<16>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<1>{}, IC<16>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<2>{}, IC<16>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<3>{}, IC<16>{}, IC<true>{}, IC<true>{});
+  step(s8, IC<4>{}, IC<16>{}, IC<false>{}, IC<true>{});
   step(s8, IC<5>{}, IC<8>{}, IC<false>{}, IC<true>{});
   step(s8, IC<6>{}, IC<0>{}, IC<false>{}, IC<true>{});
   step(s8, IC<7>{}, IC<-1>{}, IC<false>{}, IC<false>{});
