@@ -32,19 +32,29 @@ PEAK_HBM_GBS = 8000.0
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
 PMC_TRAFFIC = {"source_sha256_16": "74fa942776c6cc68", "bytes": 13.105e9}
+# the same for the MXFP8 GEMM (profiles/kernel_stats_768p_mxfp8_projections.md)
+PMC_TRAFFIC_MX = {"source_sha256_16": "c48082bff0878d49", "bytes": 24.441e9}
+MX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/mxfp8.hip", "video_diffusion_hybrid_sparse_amd/csrc/mxfp8.h",
+              "video_diffusion_hybrid_sparse_amd/csrc/common.h")
 SOFTMAX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/softmax_bf16.hip",
                    "video_diffusion_hybrid_sparse_amd/csrc/common.h",
                    "video_diffusion_hybrid_sparse_amd/csrc/kernels.h")
 
 
-def softmax_traffic():
+def measured_traffic(sources, record):
+    """HBM bytes per launch from the committed counter record, or None once the kernel's
+    sources differ from those the counters were taken on."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in SOFTMAX_SOURCES:
+    for f in sources:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
-    return PMC_TRAFFIC["bytes"] if h.hexdigest()[:16] == PMC_TRAFFIC["source_sha256_16"] else None
+    return record["bytes"] if h.hexdigest()[:16] == record["source_sha256_16"] else None
+
+
+def softmax_traffic():
+    return measured_traffic(SOFTMAX_SOURCES, PMC_TRAFFIC)
 
 
 def log(*a):
@@ -282,7 +292,7 @@ def bench_projections(args, shape) -> int:
                    "outputs": 5, "gemm_tflop": round(gemm_flop / 1e12, 3)},
         "roofline": {"kernel": "mx_gemm_kernel", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(MX_SOURCES, PMC_TRAFFIC_MX)},
         "steps_ms": {"quantize_x": round(q_ms, 4), "gemm": round(g_ms, 4)},
         "steps_rate": {"quantize_x_gbs": round(q_bytes / (q_ms * 1e-3) / 1e9, 1), "gemm_tflops": round(achieved, 1)},
         "context": {"bf16_torch_mm_ms": round(bf16_ms, 3),

@@ -27,8 +27,8 @@
 // consecutive rows hit 16 distinct bank groups.  Scale codes of two stages (one dword per
 // row) are copied into LDS with the even stage's tiles and read once into registers.
 // Workgroups are numbered so that each XCD walks a contiguous range of output tiles,
-// 8 row tiles by all column tiles: the 32 tiles one XCD runs at a time share 8 A and 4 B
-// row panels in its L2.
+// 4 row tiles by all column tiles: the 32 tiles one XCD runs at a time share 4 token
+// panels (x does not fit in the 256 MB last-level cache) and 8 weight panels in its L2.
 #include "mxfp8.h"
 
 namespace vdn {
@@ -98,7 +98,7 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kABytes = kBM * kBK, kBBytes = kBN * kBK, kStage = kABytes + kBBytes;  // 32 KB
 constexpr int kWin = 8;                    // stages per scale window: 16 scale bytes per row
 constexpr int kScSlot = (kBM + kBN) * 16;  // one window of A then B row scales (8 KB)
-constexpr int kGroupM = 8;                 // row tiles per tile group
+constexpr int kGroupM = 4;                 // row tiles per tile group
 
 // Stage copies are written as inline asm so that the compiler, which cannot tell the four
 // stage buffers apart, does not wait for every copy in flight before each LDS read; the
