@@ -385,3 +385,106 @@ def layer_backward(q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, x, dout, 
                                                   neighbor_chunks)
     return dict(dq=sq + lq, dk=sk + lk, dv=sv + lv, dtext_k=stk + ltk, dtext_v=stv + ltv, dg_s=dg_s,
                 dg_l=dg_l, dw_rms=dw_rms, dw_s=dw_s, dw_l=dw_l, dx=dout.copy(), d_o=d_o, du=du)
+
+
+def layer_backward_head(q, k, v, text_k, text_v, g_s, g_l, w_rms, w_s, w_l, dout, frames: int,
+                        chunk_frames: int, head: int, q_rows, k_rows, neighbor_chunks: int = 1,
+                        eps: float = 1e-6, scale: float | None = None) -> dict:
+    """The gradients of layer_backward that involve one head h, at full size.
+
+    Heads only meet in the two projections, so head h's share of every gradient follows
+    from head h's slices of the inputs and of the projection weights.  Returns dq at
+    q_rows, dk and dv at k_rows (all [rows, d]); dtext_k, dtext_v [L, d]; dg_s, dg_l at
+    q_rows; dw_rms [d]; dw_s, dw_l [D, d] (head h's columns).  Same arithmetic as
+    layer_backward, taken query frame by query frame.
+    """
+    h = head
+    sl_h = slice(h * q.shape[2], (h + 1) * q.shape[2])
+    qh, kh, vh = (_f64(a[:, h]) for a in (q, k, v))
+    tkh, tvh = _f64(text_k[:, h]), _f64(text_v[:, h])
+    gsh, glh = _f64(g_s[:, h]), _f64(g_l[:, h])
+    w_rms_h = _f64(w_rms[h])
+    w_s_h, w_l_h = _f64(w_s[:, sl_h]), _f64(w_l[:, sl_h])
+    dout = _f64(dout)
+    N, d = qh.shape
+    L = tkh.shape[0]
+    T = N // frames
+    scale = d ** -0.5 if scale is None else scale
+    q_rows, k_rows = np.asarray(q_rows, np.int64), np.asarray(k_rows, np.int64)
+    da_s = dout @ w_s_h  # [N, d]
+    da_l = dout @ w_l_h
+    ss, sl = sigmoid(gsh), sigmoid(glh)
+
+    # softmax branch, one query frame at a time
+    dq_s = np.zeros((N, d))
+    dk_s, dv_s = np.zeros((len(k_rows), d)), np.zeros((len(k_rows), d))
+    dtk, dtv = np.zeros((L, d)), np.zeros((L, d))
+    dw_s = np.zeros((dout.shape[1], d))
+    dg_s = np.zeros((N, d))
+    for f in range(frames):
+        rows = np.arange(f * T, (f + 1) * T)
+        idx = frame_tokens(sets.softmax_frames(f, frames, chunk_frames, neighbor_chunks), T)
+        keys = np.concatenate([tkh, kh[idx]], axis=0)
+        vals = np.concatenate([tvh, vh[idx]], axis=0)
+        s = scale * (qh[rows] @ keys.T)
+        s -= s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ vals
+        d_o = da_s[rows] * ss[rows]
+        dw_s += dout[rows].T @ (ss[rows] * o)
+        dg_s[rows] = da_s[rows] * o * ss[rows] * (1.0 - ss[rows])
+        dp = d_o @ vals.T
+        ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        dq_s[rows] = scale * (ds @ keys)
+        dtk += scale * (ds[:, :L].T @ qh[rows])
+        dtv += p[:, :L].T @ d_o
+        # sampled key tokens that are keys of this frame: their columns in the key list
+        pos = {int(t): L + i for i, t in enumerate(idx)}
+        for i, j in enumerate(k_rows):
+            c = pos.get(int(j))
+            if c is not None:
+                dk_s[i] += scale * (ds[:, c] @ qh[rows])
+                dv_s[i] += p[:, c] @ d_o
+
+    # linear branch
+    S = np.zeros((frames, d, d))
+    for g in range(frames):
+        if not sets.is_anchor(g, frames):
+            S[g] = kh[g * T:(g + 1) * T].T @ vh[g * T:(g + 1) * T]
+    Tx = tkh.T @ tvh
+    fwd, bwd = side_states(S[:, None], Tx[None], frames, chunk_frames, neighbor_chunks)
+    fwd, bwd = fwd[:, 0], bwd[:, 0]
+    u = np.zeros((N, d))
+    for f in range(frames):
+        u[f * T:(f + 1) * T] = qh[f * T:(f + 1) * T] @ (fwd[f] + bwd[f])
+    rho = 1.0 / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    rhat = u * rho
+    dr = da_l * sl
+    dg_l = da_l * rhat * w_rms_h * sl * (1.0 - sl)
+    dw_rms = np.sum(dr * rhat, axis=0)
+    dw_l = dout.T @ (sl * rhat * w_rms_h)
+    drhat = dr * w_rms_h
+    du = rho * (drhat - rhat * np.mean(drhat * rhat, axis=-1, keepdims=True))
+    dq_l = np.zeros((N, d))
+    dS = np.zeros((frames, d, d))
+    dTx = np.zeros((d, d))
+    for f in range(frames):
+        rows = slice(f * T, (f + 1) * T)
+        dq_l[rows] = du[rows] @ (fwd[f] + bwd[f]).T
+        dside = qh[rows].T @ du[rows]
+        dTx += dside
+        for g in sets.forward_frames(f, frames, chunk_frames, neighbor_chunks):
+            dS[g] += dside
+        for g in sets.backward_frames(f, frames, chunk_frames, neighbor_chunks):
+            dS[g] += dside
+    dk_l, dv_l = np.zeros((len(k_rows), d)), np.zeros((len(k_rows), d))
+    for i, j in enumerate(k_rows):
+        g = int(j) // T
+        if not sets.is_anchor(g, frames):
+            dk_l[i] = vh[j] @ dS[g].T
+            dv_l[i] = kh[j] @ dS[g]
+    dtk += tvh @ dTx.T
+    dtv += tkh @ dTx
+    return dict(dq=(dq_s + dq_l)[q_rows], dk=dk_s + dk_l, dv=dv_s + dv_l, dtext_k=dtk, dtext_v=dtv,
+                dg_s=dg_s[q_rows], dg_l=dg_l[q_rows], dw_rms=dw_rms, dw_s=dw_s, dw_l=dw_l)

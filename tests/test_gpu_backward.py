@@ -57,3 +57,41 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+def test_768p_backward_sampled():
+    """The 768p layer backward, in the configuration the bench times, against the
+    oracle's one-head backward at full size for two heads: dq at sampled query tokens
+    (anchor frames, chunk edges, interior), dk and dv at sampled key tokens, the text
+    gradients, both gate gradients at the sampled tokens, the RMSNorm weight and the
+    heads' projection-weight columns."""
+    shape = shapes.P768
+    inp = synth.make_inputs(shape)
+    dout = synth.upstream_grad(shape)
+    dl = runner.upload(inp)
+    got = dl.backward(dout.cuda())
+    torch.cuda.synchronize()
+    F, T, C, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.head_dim
+    N = F * T
+    q_rows = np.array([0, T - 1, T + 500, 5 * T, 5 * T - 1, 7 * T + 3, N // 2, N - T - 1, N - 1])
+    k_rows = np.array([2, T + 7, 5 * T, 10 * T - 1, N // 2 + 7, N - 2 * T, N - 3])
+    f = synth.f64
+    dout64 = f(dout)
+    for h in (0, 29):
+        one = slice(h, h + 1)
+        cols = slice(h * d, (h + 1) * d)
+        want = oracle.layer.layer_backward_head(
+            f(inp.q[:, one]), f(inp.k[:, one]), f(inp.v[:, one]), f(inp.text_k[:, one]), f(inp.text_v[:, one]),
+            f(inp.g_s[:, one]), f(inp.g_l[:, one]), f(inp.w_rms[one]), f(inp.w_s[:, cols]), f(inp.w_l[:, cols]),
+            dout64, F, C, 0, q_rows, k_rows, shape.neighbor_chunks, shape.rms_eps)
+        qi, ki = torch.from_numpy(q_rows).cuda(), torch.from_numpy(k_rows).cuda()
+        have = dict(dq=got["dq"].index_select(0, qi)[:, h], dk=got["dk"].index_select(0, ki)[:, h],
+                    dv=got["dv"].index_select(0, ki)[:, h], dtext_k=got["dtext_k"][:, h],
+                    dtext_v=got["dtext_v"][:, h], dg_s=got["dg_s"].index_select(0, qi)[:, h],
+                    dg_l=got["dg_l"].index_select(0, qi)[:, h], dw_rms=got["dw_rms"][h],
+                    dw_s=got["dw_s"][:, cols], dw_l=got["dw_l"][:, cols])
+        errs = {n: rel_l2(_np(t), want[n]) for n, t in have.items()}
+        print("768p head", h, {n: f"{e:.2e}" for n, e in errs.items()}, flush=True)
+        for n, e in errs.items():
+            assert np.isfinite(_np(have[n])).all(), n
+            assert e <= TOL, (n, e)

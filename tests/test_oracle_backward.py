@@ -64,3 +64,22 @@ def test_residual_gradient_is_dout():
     g = layer.layer_backward(t["q"], t["k"], t["v"], t["text_k"], t["text_v"], t["g_s"], t["g_l"], t["w_rms"],
                              t["w_s"], t["w_l"], t["x"], dout, F, C)
     np.testing.assert_array_equal(g["dx"], dout)
+
+
+@pytest.mark.parametrize("geom,h", [(GEOMS[0], 1), (GEOMS[2], 0)], ids=["F7H2h1", "F9H1h0"])
+def test_head_backward_equals_full(geom, h):
+    """The one-head, sampled-rows form used at full size equals layer_backward's head h."""
+    F, T, H, d, L, C, D = geom
+    t, dout = make(geom, 3 * sum(geom))
+    full = layer.layer_backward(t["q"], t["k"], t["v"], t["text_k"], t["text_v"], t["g_s"], t["g_l"],
+                                t["w_rms"], t["w_s"], t["w_l"], t["x"], dout, F, C)
+    rows = np.array([0, 3, F * T - 1, T + 1])
+    one = layer.layer_backward_head(t["q"], t["k"], t["v"], t["text_k"], t["text_v"], t["g_s"], t["g_l"],
+                                    t["w_rms"], t["w_s"], t["w_l"], dout, F, C, h, rows, rows[::-1])
+    sl = slice(h * d, (h + 1) * d)
+    want = dict(dq=full["dq"][rows, h], dk=full["dk"][rows[::-1], h], dv=full["dv"][rows[::-1], h],
+                dtext_k=full["dtext_k"][:, h], dtext_v=full["dtext_v"][:, h], dg_s=full["dg_s"][rows, h],
+                dg_l=full["dg_l"][rows, h], dw_rms=full["dw_rms"][h], dw_s=full["dw_s"][:, sl],
+                dw_l=full["dw_l"][:, sl])
+    for n, w in want.items():
+        np.testing.assert_allclose(one[n], w, rtol=1e-11, atol=1e-12, err_msg=n)
