@@ -23,10 +23,13 @@
 //   O^T += V^T P^T: P^T comes straight from the S^T accumulators (bf16); the V^T operand is
 //     gathered from row-major V with the transposing LDS read (ds_read_b64_tr_b16) in the
 //     key order the accumulator layout implies.
-// Scores stay in the log2 domain (scale * log2 e, and the fp8 scales, folded into one
-// FMA); the running max only moves when a sub-tile exceeds it by more than 8, so the O
-// rescale is rare.  Any fixed reference point gives the same softmax; the row sum is
-// taken over the same bf16 probabilities that multiply V.
+// Scores stay in the log2 domain.  With bf16 inputs Q^T is pre-multiplied by
+// c2 = scale log2 e (one extra bf16 rounding of q) and every score accumulator starts at
+// -m, so the MFMA hands the exponent c2 s - m straight to v_exp; the fp8 path folds its
+// per-segment c2 into one FMA per score.  The reference m is the first sub-tile's max and
+// only moves when a sub-tile exceeds it by more than 8, so the O rescale is rare.  Any
+// fixed reference point gives the same softmax; the row sum is taken over the same bf16
+// probabilities that multiply V.
 //
 // fp8 inputs: video keys stay e4m3 in LDS and S^T uses v_mfma_f32_32x32x64_f8f6f4 with
 // the e4m3 query codes; text keys are bf16, so the text stages (walked first, in a loop
@@ -134,7 +137,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   } else {
     const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)qtok * rs + h * D + half * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(qp + 16 * s);
+    for (int s = 0; s < KS; ++s) {
+      // pre-multiplied by c2 = scale log2 e, so that a score accumulator started at -m
+      // holds the exponent c2 s - m itself
+      const bf16x8 raw = load_bf16x8(qp + 16 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)((float)raw[e] * a.c2_text);
+    }
   }
 
   // Per-lane constants of the stage loads: row inside the stage and swizzled column.
@@ -144,7 +153,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     lrow[i] = (wave * NI + i) * RPI + lane / CPR;
     lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
   }
-  auto issue = [&](int j, int buf) {
+  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     bool text;
     int start, valid;
     kw.stage_at(j, text, start, valid);
@@ -203,30 +212,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = 0.0f;
-  float m = -INFINITY, l = 0.0f;
+  // m: the reference of the exponents (log2 domain), the same in both lanes of a query;
+  // set by the first sub-tile, then moved up only when a sub-tile exceeds it by 2^8.
+  float m = 0.0f, l = 0.0f;
+  bool started = false;    // uniform: has any sub-tile been folded in
+  f32x16 negm = 0.0f;      // -m in every accumulator slot (bf16 inputs)
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // One 128-key stage: two 64-key sub-tiles of scores, softmax update and P V.
-  // VIDEO8 selects the e4m3 score path (fp8 inputs, video keys).
-  auto stage = [&](int j, auto video8) {
+  // One 128-key stage from LDS buffer BUF: two 64-key sub-tiles of scores, softmax
+  // update and P V.  VIDEO8 selects the e4m3 score path (fp8 inputs, video keys).  With
+  // bf16 inputs the scores come out of the MFMA as exponents relative to m (REL); the
+  // fp8 path scales raw scores by its per-segment c2.
+  auto stage = [&](int j, int BUF, auto video8) __attribute__((always_inline)) {
     constexpr bool VIDEO8 = decltype(video8)::value;
-    const int buf = j & 1;
+    constexpr bool REL = !FP8;
     bool text;
     int start, svalid;
     kw.stage_at(j, text, start, svalid);
     const float c2 = VIDEO8 ? a.c2_video : a.c2_text;
-    if (j + 1 < nst) issue(j + 1, buf ^ 1);
+    if (j + 1 < nst) issue(j + 1, BUF ^ 1);
 
+#pragma unroll 1
     for (int sub = 0; sub < BN / BC; ++sub) {
       const int valid = svalid - sub * BC;  // valid keys of this sub-tile (>= BC when full)
       if (valid <= 0) break;
-      const __bf16* V = Vs[buf] + sub * BC * D;
+      const __bf16* V = Vs[BUF] + sub * BC * D;
 
       f32x16 s[2];
-      s[0] = 0.0f;
-      s[1] = 0.0f;
       if constexpr (VIDEO8) {
-        const uint8_t* K8 = reinterpret_cast<const uint8_t*>(Ks[buf]) + sub * BC * D;
+        s[0] = 0.0f;
+        s[1] = 0.0f;
+        const uint8_t* K8 = reinterpret_cast<const uint8_t*>(Ks[BUF]) + sub * BC * D;
 #pragma unroll
         for (int k = 0; k < KS8; ++k)
 #pragma unroll
@@ -237,9 +253,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             s[rt] = mfma32x32x64_fp8(ka, q8[k], s[rt]);
           }
       } else {
-        const __bf16* K = Ks[buf] + sub * BC * D;
+        const __bf16* K = Ks[BUF] + sub * BC * D;
+        const f32x16 init = REL ? negm : f32x16(0.0f);
 #pragma unroll
-        for (int k = 0; k < KS; ++k)
+        for (int rt = 0; rt < 2; ++rt)
+          s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[0]), qreg[0], init);
+#pragma unroll
+        for (int k = 1; k < KS; ++k)
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt)
             s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[k]), qreg[k], s[rt]);
@@ -256,14 +276,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rt][r]);
-      mx = pair_max(mx) * c2;
-      if (__any(mx > m + 8.0f)) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
+      // the sub-tile's largest exponent relative to m (both lanes of the query)
+      const float rel = REL ? pair_max(mx) : pair_max(mx) * c2 - m;
+      if (!started || __any(rel > 8.0f)) {
+        const float shift = started ? fmaxf(rel, 0.0f) : rel;
+        const float alpha = started ? __builtin_amdgcn_exp2f(-shift) : 0.0f;
+        m += shift;
         l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        if constexpr (REL) {
+          negm = -m;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) s[rt] -= shift;
+        }
+        started = true;
       }
 
       bf16x8 pb[4];
@@ -272,8 +299,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(s[rt][r] * c2 - m),
-                                          __builtin_amdgcn_exp2f(s[rt][r + 1] * c2 - m));
+          const float x0 = REL ? s[rt][r] : s[rt][r] * c2 - m;
+          const float x1 = REL ? s[rt][r + 1] : s[rt][r + 1] * c2 - m;
+          const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
           psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one2, psum, false);
           uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
           const int e = (r & 7) >> 1;
@@ -296,14 +324,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
+  auto run_stage = [&](int j, auto video8) __attribute__((always_inline)) { stage(j, j & 1, video8); };
 
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // text stages first (bf16 keys), then the video stages
   int j = 0;
-  for (; j < kw.n0; ++j) stage(j, std::integral_constant<bool, false>{});
-  for (; j < nst; ++j) stage(j, std::integral_constant<bool, FP8>{});
+  for (; j < kw.n0; ++j) run_stage(j, std::integral_constant<bool, false>{});
+  for (; j < nst; ++j) run_stage(j, std::integral_constant<bool, FP8>{});
 
   l = pair_sum(l);
   if (a.lse && qok && half == 0) a.lse[(size_t)qtok * g.H + h] = m + __log2f(l);
