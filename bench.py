@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
-PMC_TRAFFIC = {"source_sha256_16": "74fa942776c6cc68", "bytes": 13.105e9}
+PMC_TRAFFIC = {"source_sha256_16": "ed0256d548ae6e37", "bytes": 12.235e9}
 # the same for the MXFP8 GEMM (profiles/kernel_stats_768p_mxfp8_projections.md)
 PMC_TRAFFIC_MX = {"source_sha256_16": "c48082bff0878d49", "bytes": 24.441e9}
 MX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/mxfp8.hip", "video_diffusion_hybrid_sparse_amd/csrc/mxfp8.h",
