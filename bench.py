@@ -197,7 +197,9 @@ def main() -> int:
 
 
 def bench_backward(args, shape, inp, dl) -> int:
-    """Times vdn_hybrid_attn_bwd (which recomputes the forward it needs) at the same shape."""
+    """Times one training step's backward at the same shape: vdn_hybrid_attn_bwd_saved,
+    which reads the record the training forward kept, and, for comparison, the stateless
+    vdn_hybrid_attn_bwd that recomputes the forward it needs."""
     import torch
 
     from video_diffusion_hybrid_sparse_amd import synth, workload
@@ -206,23 +208,38 @@ def bench_backward(args, shape, inp, dl) -> int:
         print("the backward is built for linear variant 0", file=sys.stderr)
         return 2
     dout = synth.upstream_grad(shape).cuda()
-    for _ in range(args.warmup):
-        dl.backward(dout)
-    torch.cuda.synchronize()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    dl.run_train()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dl.backward(dout)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    saved_ms = timed(lambda: dl.backward(dout, saved=True))
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    recompute_ms = timed(lambda: dl.backward(dout))
+    fwd_ms = timed(dl.run)
+    train_fwd_ms = timed(dl.run_train)
     fl = workload.backward_flops(shape)
     print(json.dumps({
         "metric": "hybrid-attn layer backward ms + TFLOP/s at 768p 60-frame shape, 1 GPU",
-        "value": round(fl["total"] / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "value": round(fl["total"] / (saved_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(saved_ms, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) activations, gate logits and upstream gradient, 768p layer shape",
         "config": {"workload": shape.name + "_backward", "layer_backward_tflop": round(fl["total"] / 1e12, 3),
-                   "includes": "forward recompute (not counted in the FLOPs)"},
+                   "reads": "the training forward's record (o, u, log-sum-exp, branch outputs)"},
+        "context": {"stateless_backward_ms": round(recompute_ms, 3), "forward_ms": round(fwd_ms, 3),
+                    "training_forward_ms": round(train_fwd_ms, 3),
+                    "stateless_backward_tflops": round(fl["total"] / (recompute_ms * 1e-3) / 1e12, 2)},
     }), flush=True)
     return 0
 

@@ -184,6 +184,35 @@ vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training record.  vdn_hybrid_attn_fwd_train is vdn_hybrid_attn_fwd (no qkv_lin, no debug
+ * outputs) that also keeps, in `saved`, what the backward would otherwise recompute;
+ * vdn_hybrid_attn_bwd_saved is vdn_hybrid_attn_bwd reading that record instead of
+ * recomputing the softmax branch and the linear read.  Built where the backward is
+ * (vdn_hybrid_attn_saved_bytes returns 0 elsewhere).
+ *
+ *   saved  device memory of at least vdn_hybrid_attn_saved_bytes(cfg) bytes, 16-byte
+ *          aligned, owned by the caller: o [N, H, d] float32 (softmax branch before its
+ *          gate) | u [N, H, d] float32 (linear read) | lse [N, H] float32 (log2 of the
+ *          softmax denominator plus its reference, log2 domain) | branch outputs
+ *          [N, 2*H*d] bf16 (a_s then a_l per token), each part starting on a 256-byte
+ *          boundary.  Written by the training forward; the backward reads it and must
+ *          get the same inputs that forward got.
+ * The forward's workspace is vdn_hybrid_attn_workspace_bytes(cfg); the backward's is
+ * vdn_hybrid_attn_bwd_workspace_bytes(cfg).  Argument checks and errors as for the calls
+ * they extend.
+ */
+size_t vdn_hybrid_attn_saved_bytes(const vdn_hybrid_cfg* cfg);
+vdn_status vdn_hybrid_attn_fwd_train(const void* q, const void* k, const void* v, const void* text_kv,
+                                     const void* gates, const float* rms_weight, const void* w_out,
+                                     const void* residual, void* out, const vdn_hybrid_cfg* cfg, void* saved,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+vdn_status vdn_hybrid_attn_bwd_saved(const void* q, const void* k, const void* v, const void* text_kv,
+                                     const void* gates, const float* rms_weight, const void* w_out,
+                                     const void* dout, const void* saved, const vdn_hybrid_cfg* cfg, float* dqkv,
+                                     float* dtext_kv, float* dgates, float* drms_weight, float* dw_out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Membership export: runs, on the current device, the same index functions the kernels
  * use and writes codes_host[f * F + g] (host memory, F*F bytes) = how query frame f reads
  * key frame g: 1 softmax, 2 forward state, 3 backward state, 0 not at all.

@@ -243,3 +243,22 @@ def test_mxfp8_argument_checks_launch_nothing():
     bad = (ctypes.c_void_p * 5)(*[0x100000 * (i + 1) for i in range(4)], None)
     assert lin(o=bad) == INVALID
     assert "outs[4]" in binding.last_error()
+
+
+def test_training_record_entry_points():
+    L = binding.lib()
+    cfg = binding.make_cfg(shapes.MID)
+    assert binding.saved_bytes(cfg) > 0
+    toy = binding.make_cfg(shapes.TOY)  # float32: no backward, so no record
+    assert L.vdn_hybrid_attn_saved_bytes(ctypes.byref(toy)) == 0
+    good = [0x10000 * (i + 1) for i in range(9)]
+    ws = binding.workspace_bytes(cfg)
+    assert L.vdn_hybrid_attn_fwd_train(*good, ctypes.byref(cfg), None, 0x200000, ws, None) == INVALID
+    assert L.vdn_hybrid_attn_fwd_train(*good, ctypes.byref(cfg), 0x300008, 0x200000, ws, None) == INVALID
+    if not torch.cuda.is_available():
+        assert L.vdn_hybrid_attn_fwd_train(*good, ctypes.byref(cfg), 0x300000, 0x200000, ws, None) == NO_DEVICE
+        grads = [0x400000 * (i + 1) for i in range(5)]
+        bws = binding.bwd_workspace_bytes(cfg)
+        assert L.vdn_hybrid_attn_bwd_saved(*good[:8], None, ctypes.byref(cfg), *grads, 0x200000, bws, None) == INVALID
+        assert L.vdn_hybrid_attn_bwd_saved(*good[:8], 0x300000, ctypes.byref(cfg), *grads, 0x200000, bws,
+                                           None) == NO_DEVICE

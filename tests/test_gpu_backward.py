@@ -95,3 +95,23 @@ def test_768p_backward_sampled():
         for n, e in errs.items():
             assert np.isfinite(_np(have[n])).all(), n
             assert e <= TOL, (n, e)
+
+
+@pytest.mark.parametrize("shape", [shapes.MID, RAGGED128], ids=lambda s: s.name)
+def test_training_record_matches_recompute(shape):
+    """The training forward writes the same output as the forward, and the backward from
+    its record equals, bit for bit, the backward that recomputes the forward."""
+    inp = synth.make_inputs(shape)
+    dout = synth.upstream_grad(shape).cuda()
+    dl = runner.upload(inp)
+    dl.run()
+    ref_out = dl.out.clone()
+    ref = dl.backward(dout)
+    ref = {k: t.clone() for k, t in ref.items()}
+    dl.out.fill_(float("nan"))
+    dl.run_train()
+    got = dl.backward(dout, saved=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dl.out, ref_out)
+    for n in ref:
+        assert torch.equal(got[n], ref[n]), n

@@ -24,6 +24,7 @@ PROFILE_STEPS = ("state_build", "state_scan", "linear_read", "softmax", "project
 
 EXPORTS = ("vdn_hybrid_attn_workspace_bytes", "vdn_hybrid_attn_workspace_layout", "vdn_hybrid_attn_fwd",
            "vdn_hybrid_attn_bwd_workspace_bytes", "vdn_hybrid_attn_bwd",
+           "vdn_hybrid_attn_saved_bytes", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
            "vdn_hybrid_attn_membership", "vdn_profile_enable", "vdn_profile_read", "vdn_last_error",
            "vdn_mxfp8_quantize", "vdn_mxfp8_quantize_lora", "vdn_mxfp8_linear")
 
@@ -70,6 +71,14 @@ def lib() -> ctypes.CDLL:
         L.vdn_hybrid_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Cfg), vp, vp, vp, vp, vp,
                                           vp, sz, vp]
         L.vdn_hybrid_attn_bwd.restype = i32
+        L.vdn_hybrid_attn_saved_bytes.argtypes = [ctypes.POINTER(Cfg)]
+        L.vdn_hybrid_attn_saved_bytes.restype = sz
+        L.vdn_hybrid_attn_fwd_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Cfg), vp, vp, sz,
+                                                vp]
+        L.vdn_hybrid_attn_fwd_train.restype = i32
+        L.vdn_hybrid_attn_bwd_saved.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Cfg), vp, vp, vp,
+                                                vp, vp, vp, sz, vp]
+        L.vdn_hybrid_attn_bwd_saved.restype = i32
         L.vdn_hybrid_attn_membership.argtypes = [ctypes.POINTER(Cfg), vp]
         L.vdn_hybrid_attn_membership.restype = i32
         L.vdn_profile_enable.argtypes = [i32]
@@ -198,13 +207,50 @@ def bwd_workspace_bytes(cfg: Cfg) -> int:
     return n
 
 
+def saved_bytes(cfg: Cfg) -> int:
+    n = lib().vdn_hybrid_attn_saved_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise VdnError(-1, last_error())
+    return n
+
+
+def hybrid_attn_fwd_train(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg: Cfg, saved,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue the forward and keep its training record in `saved` (a uint8 device tensor
+    of at least saved_bytes(cfg) bytes) for hybrid_attn_bwd(..., saved=saved)."""
+    N, H, d, L, D = cfg.frames * cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.text_len, cfg.model_dim
+    ad = _TORCH[cfg.act_dtype]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, n, (N, H, d), _TORCH[cfg.qkv_dtype])
+    _expect(text_kv, "text_kv", (2, L, H, d), ad)
+    _expect(gates, "gates", (2, N, H, d), ad)
+    _expect(rms_weight, "rms_weight", (H, d), (torch.float32,))
+    _expect(w_out, "w_out", (D, 2 * H * d), ad)
+    _expect(residual, "residual", (N, D), ad)
+    _expect(out, "out", (N, D), ad)
+    if saved.numel() < saved_bytes(cfg):
+        raise ValueError("saved is smaller than saved_bytes(cfg)")
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(lib().vdn_hybrid_attn_fwd_train(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None, _ptr(gates, "gates"),
+        _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(residual, "residual"), _ptr(out, "out"),
+        ctypes.byref(cfg), _ptr(saved, "saved"), _ptr(workspace, "workspace"), workspace.numel(), handle))
+
+
 def hybrid_attn_bwd(q, k, v, text_kv, gates, rms_weight, w_out, dout, cfg: Cfg, dqkv, dtext_kv, dgates,
-                    drms_weight, dw_out, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                    drms_weight, dw_out, workspace: Optional[torch.Tensor] = None, stream=None,
+                    saved: Optional[torch.Tensor] = None) -> None:
     """Enqueue the layer backward: gradients of sum(out * dout).
 
     Inputs as hybrid_attn_fwd (bf16, no qkv_lin) plus dout [N,D]; float32 outputs dqkv
     [3,N,H,d], dtext_kv [2,L,H,d] (None if L == 0), dgates [2,N,H,d], drms_weight [H,d],
-    dw_out [D,2*H*d]; workspace at least bwd_workspace_bytes(cfg) bytes.
+    dw_out [D,2*H*d]; workspace at least bwd_workspace_bytes(cfg) bytes.  With `saved`
+    (the record of hybrid_attn_fwd_train on the same inputs) the forward is not
+    recomputed.
     """
     N, H, d, L, D = cfg.frames * cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.text_len, cfg.model_dim
     qd, ad = _TORCH[cfg.qkv_dtype], _TORCH[cfg.act_dtype]
@@ -226,6 +272,16 @@ def hybrid_attn_bwd(q, k, v, text_kv, gates, rms_weight, w_out, dout, cfg: Cfg, 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if saved is not None:
+        if saved.numel() < saved_bytes(cfg):
+            raise ValueError("saved is smaller than saved_bytes(cfg)")
+        _check(lib().vdn_hybrid_attn_bwd_saved(
+            _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None,
+            _ptr(gates, "gates"), _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(dout, "dout"),
+            _ptr(saved, "saved"), ctypes.byref(cfg), _ptr(dqkv, "dqkv"), _ptr(dtext_kv, "dtext_kv") if L > 0 else None,
+            _ptr(dgates, "dgates"), _ptr(drms_weight, "drms_weight"), _ptr(dw_out, "dw_out"),
+            _ptr(workspace, "workspace"), workspace.numel(), handle))
+        return
     _check(lib().vdn_hybrid_attn_bwd(
         _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None, _ptr(gates, "gates"),
         _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(dout, "dout"), ctypes.byref(cfg),

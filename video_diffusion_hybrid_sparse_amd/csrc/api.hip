@@ -133,6 +133,21 @@ vdn_status check_bwd_cfg(const vdn_hybrid_cfg* c) {
   return VDN_OK;
 }
 
+// The training record of vdn_hybrid_attn_fwd_train: o [N,H,d] f32 | u [N,H,d] f32 |
+// lse [N,H] f32 | branch_out [N, 2Hd] bf16, each 256-byte aligned.
+struct SavedLayout {
+  size_t o, u, lse, acat, total;
+};
+void saved_layout_of(const vdn_hybrid_cfg* c, SavedLayout* S) {
+  const size_t N = (size_t)c->frames * c->tokens_per_frame, nh = N * c->heads, nhd = nh * c->head_dim;
+  size_t off = 0;
+  S->o = off; off = align_up(off + nhd * 4);
+  S->u = off; off = align_up(off + nhd * 4);
+  S->lse = off; off = align_up(off + nh * 4);
+  S->acat = off; off = align_up(off + 2 * nhd * 2);
+  S->total = off;
+}
+
 void bwd_layout_of(const vdn_hybrid_cfg* c, BwdLayout* B) {
   layout_of(c, &B->fwd);
   const size_t H = c->heads, d = c->head_dim, N = (size_t)c->frames * c->tokens_per_frame;
@@ -224,11 +239,10 @@ size_t vdn_hybrid_attn_bwd_workspace_bytes(const vdn_hybrid_cfg* cfg) {
   return B.total;
 }
 
-vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
-                               const float* rms_weight, const void* w_out, const void* dout,
-                               const vdn_hybrid_cfg* cfg, float* dqkv, float* dtext_kv, float* dgates,
-                               float* drms_weight, float* dw_out, void* workspace, size_t workspace_bytes,
-                               void* stream_ptr) {
+static vdn_status bwd_impl(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
+                           const float* rms_weight, const void* w_out, const void* dout, const vdn_hybrid_cfg* cfg,
+                           float* dqkv, float* dtext_kv, float* dgates, float* drms_weight, float* dw_out,
+                           void* workspace, size_t workspace_bytes, void* stream_ptr, const void* saved) {
   vdn_status s = check_bwd_cfg(cfg);
   if (s != VDN_OK) return s;
   const struct { const void* p; const char* name; } req[] = {
@@ -264,6 +278,15 @@ vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, cons
   float* O = reinterpret_cast<float*>(ws + B.o);
   float* U = reinterpret_cast<float*>(ws + B.u);
   float* lse = reinterpret_cast<float*>(ws + B.lse);
+  if (saved) {  // the training forward's record stands in for the recompute
+    SavedLayout SL;
+    saved_layout_of(cfg, &SL);
+    char* r = const_cast<char*>(static_cast<const char*>(saved));
+    acat = reinterpret_cast<__bf16*>(r + SL.acat);
+    O = reinterpret_cast<float*>(r + SL.o);
+    U = reinterpret_cast<float*>(r + SL.u);
+    lse = reinterpret_cast<float*>(r + SL.lse);
+  }
   float* delta = reinterpret_cast<float*>(ws + B.delta);
   float* dacat = reinterpret_cast<float*>(ws + B.dacat);
   __bf16* dO = reinterpret_cast<__bf16*>(ws + B.dO);
@@ -290,15 +313,18 @@ vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, cons
 #define VDN_LAUNCH(what, expr) \
   if ((e = (expr)) != hipSuccess) return fail(VDN_ERR_HIP, what " launch: %s", hipGetErrorString(e));
 
-  // forward recompute: states, linear read (u), softmax (o and its log-sum-exp)
+  // forward recompute: states (always: the linear dq reads them), then, without a saved
+  // record, the linear read (u) and the softmax (o and its log-sum-exp)
   BuildArgs<__bf16> ba{kb, vb, tk, tv, S, St, g};
   VDN_LAUNCH("state build", launch_build_bf16(ba, stream));
   ScanArgs sa{S, St, Sf, Sb, g, (int64_t)(g.H * (size_t)g.d * g.d / 4)};
   VDN_LAUNCH("scan", launch_scan(sa, stream));
-  ReadoutArgs<__bf16> ra{qb, Sf, Sb, St, gl, rms_weight, acat, U, g, cfg->rms_eps, 0};
-  VDN_LAUNCH("linear read", launch_readout_bf16(ra, stream));
-  SoftmaxArgs sm{q, k, vb, tk, tv, gs, acat, O, g, c2, c2, 1.0f, lse};
-  VDN_LAUNCH("softmax", launch_softmax_bf16(sm, stream));
+  if (!saved) {
+    ReadoutArgs<__bf16> ra{qb, Sf, Sb, St, gl, rms_weight, acat, U, g, cfg->rms_eps, 0};
+    VDN_LAUNCH("linear read", launch_readout_bf16(ra, stream));
+    SoftmaxArgs sm{q, k, vb, tk, tv, gs, acat, O, g, c2, c2, 1.0f, lse};
+    VDN_LAUNCH("softmax", launch_softmax_bf16(sm, stream));
+  }
 
   // d[a_s | a_l] = dout W (row-major N x 2Hd) and dW = dout^T [a_s | a_l] (D x 2Hd)
   const char* gerr = nullptr;
@@ -337,6 +363,25 @@ vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, cons
   return VDN_OK;
 }
 
+vdn_status vdn_hybrid_attn_bwd(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
+                               const float* rms_weight, const void* w_out, const void* dout,
+                               const vdn_hybrid_cfg* cfg, float* dqkv, float* dtext_kv, float* dgates,
+                               float* drms_weight, float* dw_out, void* workspace, size_t workspace_bytes,
+                               void* stream_ptr) {
+  return bwd_impl(q, k, v, text_kv, gates, rms_weight, w_out, dout, cfg, dqkv, dtext_kv, dgates, drms_weight, dw_out,
+                  workspace, workspace_bytes, stream_ptr, nullptr);
+}
+
+vdn_status vdn_hybrid_attn_bwd_saved(const void* q, const void* k, const void* v, const void* text_kv,
+                                     const void* gates, const float* rms_weight, const void* w_out, const void* dout,
+                                     const void* saved, const vdn_hybrid_cfg* cfg, float* dqkv, float* dtext_kv,
+                                     float* dgates, float* drms_weight, float* dw_out, void* workspace,
+                                     size_t workspace_bytes, void* stream_ptr) {
+  if (!saved || !aligned16(saved)) return fail(VDN_ERR_INVALID_ARG, "saved is NULL or not 16-byte aligned");
+  return bwd_impl(q, k, v, text_kv, gates, rms_weight, w_out, dout, cfg, dqkv, dtext_kv, dgates, drms_weight, dw_out,
+                  workspace, workspace_bytes, stream_ptr, saved);
+}
+
 vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_host) {
   vdn_status s = check_cfg(cfg);
   if (s != VDN_OK) return s;
@@ -354,11 +399,13 @@ vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_h
   return VDN_OK;
 }
 
-vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_kv,
-                               const void* gates, const float* rms_weight, const void* w_out,
-                               const void* residual, void* out, const vdn_hybrid_cfg* cfg,
-                               const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg, void* workspace,
-                               size_t workspace_bytes, void* stream_ptr) {
+// The forward; lse (softmax log-sum-exp, log2 domain) and acat_out (branch outputs in
+// place of the workspace's) are set only by the training forward.
+static vdn_status fwd_impl(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
+                           const float* rms_weight, const void* w_out, const void* residual, void* out,
+                           const vdn_hybrid_cfg* cfg, const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg,
+                           void* workspace, size_t workspace_bytes, void* stream_ptr, float* lse_out,
+                           void* acat_out) {
   vdn_status s = check_cfg(cfg);
   if (s != VDN_OK) return s;
   const struct { const void* p; const char* name; } req[] = {
@@ -390,7 +437,7 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
   float* St = reinterpret_cast<float*>(ws + L.text_state);
   float* Sf = reinterpret_cast<float*>(ws + L.fwd_states);
   float* Sb = reinterpret_cast<float*>(ws + L.bwd_states);
-  void* acat = ws + L.branch_out;
+  void* acat = acat_out ? acat_out : ws + L.branch_out;
   const char* tkv = static_cast<const char*>(text_kv);
   const void* tk = tkv;
   const void* tv = tkv ? tkv + (size_t)g.L * row * ab : nullptr;
@@ -466,7 +513,7 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
     e = launch_softmax_fp8(sm, stream);
   } else if (bf16) {
     SoftmaxArgs sm{q, k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv, (const __bf16*)gs, (__bf16*)acat,
-                   o_soft_dbg, g, c2, c2, 1.0f, nullptr};
+                   o_soft_dbg, g, c2, c2, 1.0f, lse_out};
     e = launch_softmax_bf16(sm, stream);
   } else {
     SoftmaxF32Args sm{(const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,
@@ -481,6 +528,37 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
     return fail(VDN_ERR_HIP, "projection: %s", gerr);
   mark(5);
   return VDN_OK;
+}
+
+vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const void* text_kv,
+                               const void* gates, const float* rms_weight, const void* w_out,
+                               const void* residual, void* out, const vdn_hybrid_cfg* cfg,
+                               const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg, void* workspace,
+                               size_t workspace_bytes, void* stream_ptr) {
+  return fwd_impl(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg, qkv_lin, o_soft_dbg, u_lin_dbg,
+                  workspace, workspace_bytes, stream_ptr, nullptr, nullptr);
+}
+
+size_t vdn_hybrid_attn_saved_bytes(const vdn_hybrid_cfg* cfg) {
+  if (check_bwd_cfg(cfg) != VDN_OK) return 0;
+  SavedLayout S;
+  saved_layout_of(cfg, &S);
+  return S.total;
+}
+
+vdn_status vdn_hybrid_attn_fwd_train(const void* q, const void* k, const void* v, const void* text_kv,
+                                     const void* gates, const float* rms_weight, const void* w_out,
+                                     const void* residual, void* out, const vdn_hybrid_cfg* cfg, void* saved,
+                                     void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  vdn_status s = check_bwd_cfg(cfg);
+  if (s != VDN_OK) return s;
+  if (!saved || !aligned16(saved)) return fail(VDN_ERR_INVALID_ARG, "saved is NULL or not 16-byte aligned");
+  SavedLayout S;
+  saved_layout_of(cfg, &S);
+  char* r = static_cast<char*>(saved);
+  return fwd_impl(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg, nullptr,
+                  reinterpret_cast<float*>(r + S.o), reinterpret_cast<float*>(r + S.u), workspace, workspace_bytes,
+                  stream_ptr, reinterpret_cast<float*>(r + S.lse), r + S.acat);
 }
 
 // ---- MXFP8 input-side projections ---------------------------------------------------

@@ -43,9 +43,18 @@ class DeviceLayer:
                                 o_soft_dbg=self.o_soft_dbg, u_lin_dbg=self.u_lin_dbg, workspace=self.workspace,
                                 stream=stream)
 
-    def backward(self, dout: torch.Tensor, stream=None) -> dict:
+    def run_train(self, stream=None) -> None:
+        """The forward, keeping its training record for backward(dout, saved=True)."""
+        if "saved" not in self.extra:
+            self.extra["saved"] = torch.empty(binding.saved_bytes(self.cfg), dtype=torch.uint8, device=self.q.device)
+        binding.hybrid_attn_fwd_train(self.q, self.k, self.v, self.text_kv, self.gates, self.rms_weight, self.w_out,
+                                      self.residual, self.out, self.cfg, self.extra["saved"],
+                                      workspace=self.workspace, stream=stream)
+
+    def backward(self, dout: torch.Tensor, stream=None, saved: bool = False) -> dict:
         """Layer backward for the upstream gradient dout [N, D]; returns float32 gradients
-        (dq, dk, dv, dtext_k, dtext_v, dg_s, dg_l, dw_rms, dw_s, dw_l)."""
+        (dq, dk, dv, dtext_k, dtext_v, dg_s, dg_l, dw_rms, dw_s, dw_l).  saved: use the
+        record of the last run_train instead of recomputing the forward."""
         c = self.cfg
         N, H, d, L, D = c.frames * c.tokens_per_frame, c.heads, c.head_dim, c.text_len, c.model_dim
         dev = self.q.device
@@ -59,7 +68,8 @@ class DeviceLayer:
             self.extra["bwd_ws"] = torch.empty(binding.bwd_workspace_bytes(c), dtype=torch.uint8, device=dev)
         binding.hybrid_attn_bwd(self.q, self.k, self.v, self.text_kv, self.gates, self.rms_weight, self.w_out,
                                 dout.contiguous(), c, dqkv, dtext if L > 0 else None, dgates, dw, dwo,
-                                workspace=self.extra["bwd_ws"], stream=stream)
+                                workspace=self.extra["bwd_ws"], stream=stream,
+                                saved=self.extra["saved"] if saved else None)
         hd = H * d
         return dict(dq=dqkv[0], dk=dqkv[1], dv=dqkv[2], dtext_k=dtext[0], dtext_v=dtext[1], dg_s=dgates[0],
                     dg_l=dgates[1], dw_rms=dw, dw_s=dwo[:, :hd], dw_l=dwo[:, hd:])
