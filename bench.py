@@ -31,9 +31,9 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
-PMC_TRAFFIC = {"source_sha256_16": "ed0256d548ae6e37", "bytes": 12.235e9}
+PMC_TRAFFIC = {"source_sha256_16": "9862555847330fc5", "bytes": 22.774e9}
 # the same for the MXFP8 GEMM (profiles/kernel_stats_768p_mxfp8_projections.md)
-PMC_TRAFFIC_MX = {"source_sha256_16": "c48082bff0878d49", "bytes": 24.441e9}
+PMC_TRAFFIC_MX = {"source_sha256_16": "cb0f1e10a0964a3b", "bytes": 25.021e9}
 MX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/mxfp8.hip", "video_diffusion_hybrid_sparse_amd/csrc/mxfp8.h",
               "video_diffusion_hybrid_sparse_amd/csrc/common.h")
 SOFTMAX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/softmax_bf16.hip",
@@ -176,7 +176,7 @@ def main() -> int:
                    "linear_variant": shape.linear_variant,
                    "layer_tflop": round(fl["total"] / 1e12, 3)},
         "pct_mfma_peak": round(100 * fl["total"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "softmax_kernel<128, false>", "bound": "mfma", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "softmax_sw_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": softmax_traffic()},
         "steps_ms": {k: round(v, 4) for k, v in per.items()},

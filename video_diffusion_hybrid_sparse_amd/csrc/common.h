@@ -202,6 +202,16 @@ __device__ __forceinline__ int swz(int row) {
   else return ((row & 2) << 1) | ((row >> 2) & 3);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes (global address
+// sbase + voff) land at LDS address m0 + 16 i.  Written as inline asm so that the compiler
+// neither tracks these copies (it would wait for all of them before any LDS read of the
+// kernel) nor forms 64-bit per-lane addresses; the caller waits for them (vmcnt) itself.
+// One wait state separates the M0 write from the copy.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
   return __builtin_bit_cast(
       bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p)));

@@ -100,14 +100,9 @@ constexpr int kWin = 8;                    // stages per scale window: 16 scale 
 constexpr int kScSlot = (kBM + kBN) * 16;  // one window of A then B row scales (8 KB)
 constexpr int kGroupM = 4;                 // row tiles per tile group
 
-// Stage copies are written as inline asm so that the compiler, which cannot tell the four
+// Stage copies use dma16 (inline asm) so that the compiler, which cannot tell the four
 // stage buffers apart, does not wait for every copy in flight before each LDS read; the
-// waits are explicit (wait_barrier).  M0 holds the wave's LDS base; lane i's 16 bytes
-// land at M0 + 16 i.  One wait state separates the M0 write from the copy.
-__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
-}
+// waits are explicit (wait_barrier).
 
 // Wait until at most N of this wave's copies are in flight and its LDS reads are done,
 // then meet the other waves.

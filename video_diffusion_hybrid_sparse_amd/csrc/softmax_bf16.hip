@@ -7,35 +7,35 @@
 // "独立门控，融合两条注意力分支") and stores it as bf16 into the first half of the branch
 // output row.  The mask is never materialised: a query group's keys are the text tokens
 // and at most three contiguous video token ranges (group_keys), walked one segment at a
-// time in stages of 128 contiguous keys; only a segment's last stage is partial and
-// masked.
+// time in stages of contiguous keys; only a segment's last stage is partial.
 //
-// Work split: one workgroup = 8 waves (two per SIMD) = 256 query tokens of one query
-// group and one head; each wave owns 32 queries.  Workgroups are numbered so that each
-// XCD runs a contiguous range of (head, group, query tile): tiles that read the same keys
-// share one L2.  Key and value stages go from HBM straight into LDS (global_load_lds, 16
-// bytes per lane), double-buffered, one barrier per 128-key stage; rows are stored with
-// an XOR swizzle of their 16-byte chunks that makes the LDS read patterns below
-// conflict-free.  Each stage is computed as two 64-key sub-tiles:
+// Common layout: one workgroup = 256 query tokens of one query group and one head.
+// Workgroups are numbered so that each XCD runs a contiguous range of (head, group,
+// query tile): tiles that read the same keys share one L2.  Key and value stages go from
+// HBM straight into LDS (global_load_lds, 16 bytes per lane); rows are stored with an XOR
+// swizzle of their 16-byte chunks that makes the LDS read patterns conflict-free.
 //   S^T = K Q^T (keys x queries): K is the MFMA A operand (16-byte LDS reads); Q^T stays
 //     in registers.  A lane holds the scores of one query, so the softmax statistics need
-//     one VALU lane swap (v_permlane32_swap) per sub-tile and the O rescale is lane-local.
+//     one VALU lane swap (v_permlane32_swap) and the O rescale is lane-local.
 //   O^T += V^T P^T: P^T comes straight from the S^T accumulators (bf16); the V^T operand is
 //     gathered from row-major V with the transposing LDS read (ds_read_b64_tr_b16) in the
 //     key order the accumulator layout implies.
-// Scores stay in the log2 domain.  With bf16 inputs Q^T is pre-multiplied by
-// c2 = scale log2 e (one extra bf16 rounding of q) and every score accumulator starts at
-// -m, so the MFMA hands the exponent c2 s - m straight to v_exp; the fp8 path folds its
-// per-segment c2 into one FMA per score.  The reference m is the first sub-tile's max and
-// only moves when a sub-tile exceeds it by more than 8, so the O rescale is rare.  Any
-// fixed reference point gives the same softmax; the row sum is taken over the same bf16
-// probabilities that multiply V.
+// Scores stay in the log2 domain, relative to a reference m that is set by the first
+// sub-tile and only moves when a sub-tile exceeds it by more than 8, so the O rescale is
+// rare.  Any fixed reference point gives the same softmax; the row sum is taken over the
+// same bf16 probabilities that multiply V.
 //
-// fp8 inputs: video keys stay e4m3 in LDS and S^T uses v_mfma_f32_32x32x64_f8f6f4 with
-// the e4m3 query codes; text keys are bf16, so the text stages (walked first, in a loop
-// of their own) use the bf16 MFMA with the query codes converted exactly to bf16.  P V
-// stays bf16 on the value codes converted exactly to bf16 (dequant_values), and the
-// per-tensor scales are applied to the scores and to the output.
+// bf16 inputs (softmax_sw_kernel): four waves, 64 queries each, one wave per SIMD, with
+// the matrix and vector work of each wave software-pipelined (see the kernel).  Q^T is
+// pre-multiplied by c2 = scale log2 e (one extra bf16 rounding of q) and every score
+// accumulator starts at -m, so the MFMA hands the exponent c2 s - m straight to v_exp.
+//
+// fp8 inputs (softmax_fp8_kernel): eight waves, 32 queries each, two per SIMD, 128-key
+// stages double-buffered.  Video keys stay e4m3 in LDS and S^T uses
+// v_mfma_f32_32x32x64_f8f6f4 with the e4m3 query codes; text keys are bf16, so the text
+// stages (walked first, in a loop of their own) use the bf16 MFMA with the query codes
+// converted exactly to bf16.  P V stays bf16 on the value codes converted exactly to bf16
+// (dequant_values), and the per-segment scale c2 is applied to each score by one FMA.
 #include "kernels.h"
 
 namespace vdn {
@@ -56,6 +56,15 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
 // Key stages of a query group: ceil(len / BN) stages per segment, segments in the order
 // text, video range 0, 1, 2.  stage_at gives a stage's first key (token index in the text
 // or video tensor) and its number of valid keys.
+// acc + (the two bf16 values of a packed pair), exactly as fp32 (bf16 -> fp32 is a shift
+// or a mask).  Plain VALU on purpose: v_dot2c_f32_bf16 does not overlap with the matrix
+// cores (each one held the MFMA stream for about 16 cycles in a probe on gfx950), while
+// these four instructions do.
+__device__ __forceinline__ float add_bf16x2(uint32_t pk, float acc) {
+  const float lo = __uint_as_float(pk << 16), hi = __uint_as_float(pk & 0xffff0000u);
+  return acc + (lo + hi);
+}
+
 template <int BN>
 struct KeyWalk {
   int L, s0, l0, s1, l1, s2, l2;
@@ -76,8 +85,8 @@ struct KeyWalk {
   }
 };
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_kernel(SoftmaxArgs a) {
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_fp8_kernel(SoftmaxArgs a) {
   constexpr int BM = 256, NW = 8;
   constexpr int BN = 128, BC = 64;           // keys per stage, keys per compute sub-tile
   constexpr int KS = D / 16;                 // bf16 MFMA k-steps over head_dim
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   constexpr int CPR8 = D / 16;               // 16-byte chunks per e4m3 row
   constexpr int RPI8 = 64 / CPR8;
   constexpr int NI8 = BN * CPR8 / (64 * NW);
-  static_assert(!FP8 || (NI8 >= 1 && CPR8 == 8), "fp8 path is laid out for head_dim 128");
+  static_assert(NI8 >= 1 && CPR8 == 8, "laid out for head_dim 128");
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * D];
 
@@ -112,10 +121,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   int qtok = t0 + wave * 32 + l32;
   const bool qok = qtok < t1;
   qtok = qok ? qtok : t1 - 1;
-  // Q^T operands: bf16 (all bf16 stages, and the fp8 path's text stages) and e4m3
+  // Q^T operands: e4m3 codes (video stages) and the same codes as bf16 (text stages)
   bf16x8 qreg[KS];
-  i32x8 q8[FP8 ? KS8 : 1];
-  if constexpr (FP8) {
+  i32x8 q8[KS8];
+  {
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (size_t)qtok * rs + h * D;
 #pragma unroll
     for (int s = 0; s < KS8; ++s) {
@@ -134,16 +143,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       qreg[s] = bf16x8{(__bf16)f0[0], (__bf16)f0[1], (__bf16)f1[0], (__bf16)f1[1],
                        (__bf16)f2[0], (__bf16)f2[1], (__bf16)f3[0], (__bf16)f3[1]};
     }
-  } else {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)qtok * rs + h * D + half * 8;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      // pre-multiplied by c2 = scale log2 e, so that a score accumulator started at -m
-      // holds the exponent c2 s - m itself
-      const bf16x8 raw = load_bf16x8(qp + 16 * s);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)((float)raw[e] * a.c2_text);
-    }
   }
 
   // Per-lane constants of the stage loads: row inside the stage and swizzled column.
@@ -157,7 +156,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     bool text;
     int start, valid;
     kw.stage_at(j, text, start, valid);
-    if (FP8 && !text) {
+    if (!text) {
       // e4m3 keys: rows of D bytes, CPR8 chunks
       const uint8_t* kb = static_cast<const uint8_t*>(a.k);
       uint8_t* kd = reinterpret_cast<uint8_t*>(Ks[buf]);
@@ -189,8 +188,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   int krd[KS];
 #pragma unroll
   for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
-  int krd8[FP8 ? 2 * KS8 : 1];
-  if constexpr (FP8) {
+  int krd8[2 * KS8];
+  {
 #pragma unroll
     for (int k = 0; k < KS8; ++k)
 #pragma unroll
@@ -216,16 +215,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // set by the first sub-tile, then moved up only when a sub-tile exceeds it by 2^8.
   float m = 0.0f, l = 0.0f;
   bool started = false;    // uniform: has any sub-tile been folded in
-  f32x16 negm = 0.0f;      // -m in every accumulator slot (bf16 inputs)
-  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One 128-key stage from LDS buffer BUF: two 64-key sub-tiles of scores, softmax
-  // update and P V.  VIDEO8 selects the e4m3 score path (fp8 inputs, video keys).  With
-  // bf16 inputs the scores come out of the MFMA as exponents relative to m (REL); the
-  // fp8 path scales raw scores by its per-segment c2.
+  // update and P V.  VIDEO8 selects the e4m3 score path (video keys); raw scores are
+  // scaled by the segment's c2.
   auto stage = [&](int j, int BUF, auto video8) __attribute__((always_inline)) {
     constexpr bool VIDEO8 = decltype(video8)::value;
-    constexpr bool REL = !FP8;
     bool text;
     int start, svalid;
     kw.stage_at(j, text, start, svalid);
@@ -254,7 +249,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
           }
       } else {
         const __bf16* K = Ks[BUF] + sub * BC * D;
-        const f32x16 init = REL ? negm : f32x16(0.0f);
+        const f32x16 init = 0.0f;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
           s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[0]), qreg[0], init);
@@ -277,7 +272,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[rt][r]);
       // the sub-tile's largest exponent relative to m (both lanes of the query)
-      const float rel = REL ? pair_max(mx) : pair_max(mx) * c2 - m;
+      const float rel = pair_max(mx) * c2 - m;
       if (!started || __any(rel > 8.0f)) {
         const float shift = started ? fmaxf(rel, 0.0f) : rel;
         const float alpha = started ? __builtin_amdgcn_exp2f(-shift) : 0.0f;
@@ -285,11 +280,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        if constexpr (REL) {
-          negm = -m;
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) s[rt] -= shift;
-        }
         started = true;
       }
 
@@ -299,10 +289,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float x0 = REL ? s[rt][r] : s[rt][r] * c2 - m;
-          const float x1 = REL ? s[rt][r + 1] : s[rt][r + 1] * c2 - m;
+          const float x0 = s[rt][r] * c2 - m;
+          const float x1 = s[rt][r + 1] * c2 - m;
           const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one2, psum, false);
+          psum = add_bf16x2(pk, psum);
           uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
           const int e = (r & 7) >> 1;
           if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
@@ -332,7 +322,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // text stages first (bf16 keys), then the video stages
   int j = 0;
   for (; j < kw.n0; ++j) run_stage(j, std::integral_constant<bool, false>{});
-  for (; j < nst; ++j) run_stage(j, std::integral_constant<bool, FP8>{});
+  for (; j < nst; ++j) run_stage(j, std::integral_constant<bool, true>{});
 
   l = pair_sum(l);
   if (a.lse && qok && half == 0) a.lse[(size_t)qtok * g.H + h] = m + __log2f(l);
@@ -371,14 +361,523 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
 }
 
+// ---- bf16 inputs: software-pipelined kernel, one wave per SIMD --------------------------
+// Four waves, each owning two blocks of 32 queries, so that every K and V operand read
+// from LDS feeds two MFMAs.  Keys advance in 32-key sub-tiles.  The work on sub-tile t+1
+// is one block: a single stream of 32 MFMAs (O += V^T P_t^T, then S_{t+2} = K Q^T - m)
+// with the vector work of sub-tile t+1 between them (its row maxima beside the P V
+// MFMAs, P_{t+1} = 2^{S_{t+1}} and its row sums beside the score MFMAs), one MFMA per
+// slot so that the matrix cores and the VALU of the wave run side by side.  The
+// exponentials are taken before the maxima are checked; in the rare block whose maximum
+// exceeds m by more than 8, m moves at the end of the block and that block's
+// exponentials are redone.  Operand reads from LDS run LA operands ahead of their MFMAs.
+//
+// Key and value stages hold 64 keys, four LDS buffers deep.  One barrier per stage: after
+// it, stage j + 3 is copied into the buffer of stage j - 1 (every wave is done with it),
+// its copy instructions spread over the MFMA slots of the two blocks that follow.  The
+// stage loop takes four stages at a time so that buffer offsets are immediates.
+//
+// Measured on MI355X (probes of single instruction kinds beside a stream of 32x32x16
+// MFMAs, one wave per SIMD): v_exp_f32, v_cvt_pk_bf16_f32, v_max3_f32, v_add_f32 and
+// v_mul_f32 cost under one cycle each beside an MFMA, v_dot2c_f32_bf16 about 16, so row
+// sums are formed with plain adds (add_bf16x2).
+//
+// The MFMAs are written as inline asm so that the scores stay in VGPRs (the VALU reads
+// them) while Q^T and O stay in AGPRs; the compiler's automatic choice moves them back
+// and forth.  The compiler does not see these as matrix instructions, so the wait states
+// a VALU read of an MFMA result needs (12 for this 8-pass MFMA) are given explicitly by
+// register-tied s_nop fences; every VALU write that an MFMA reads is at least two
+// instructions before it (fenced where it is not).
+namespace {
+__device__ __forceinline__ void mfma_qk0(f32x16& d, const bf16x8& k, const bf16x8& q, const f32x16& c) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(k), "a"(q), "v"(c));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_pv(f32x16& d, const bf16x8& v, const bf16x8& p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(v), "v"(p));
+}
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_sw_kernel(SoftmaxArgs a) {
+  constexpr int QB = 2, NW = 4, BM = 256;
+  constexpr int BN = 64, BC = 32, NBUF = 4;  // keys per stage, keys per sub-tile, stage buffers
+  constexpr int KS = D / 16;                 // MFMA k-steps over head_dim (K operands per sub-tile)
+  constexpr int DT = D / 32;                 // 32-row tiles of O^T
+  constexpr int NV = 2 * DT;                 // V operands per sub-tile
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;              // rows one wave-wide 16-byte load covers
+  constexpr int NI = BN * CPR / (64 * NW);   // loads per lane per stage (per tensor)
+  constexpr int LA = 2;                      // operand reads in flight ahead of their MFMAs
+  constexpr int EMAX = 16 * QB / NV;         // max operations per P V slot
+  constexpr int EEXP = 8 * QB / KS;          // exponential pairs per score slot
+  static_assert(NI >= 1 && NW * QB * 32 == BM && NV >= LA && KS >= LA, "shape");
+  static_assert(16 * QB % NV == 0 && 8 * QB % KS == 0, "vector work must split evenly");
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[NBUF][BN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[NBUF][BN * D];
+
+  const Geo g = a.geo;
+  const int per_head = count_tiles(g, BM);
+  const int total = per_head * g.H;
+  const int hid = blockIdx.x, xcd = hid & 7;
+  const int lid = xcd * (total >> 3) + imin(xcd, total & 7) + (hid >> 3);
+  const int h = lid / per_head;
+  int grp, t0, t1;
+  if (!locate_tile(g, lid - h * per_head, BM, grp, t0, t1)) return;
+  const KeyWalk<BN> kw(g.L, group_keys(g, grp));
+  const int nst = kw.stages();
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const size_t rs = (size_t)g.H * D;
+
+  int qtok[QB];
+  bool qok[QB];
+  bf16x8 qreg[QB][KS];  // Q^T pre-multiplied by c2 = scale log2 e, kept in AGPRs
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int t = t0 + (wave * QB + qb) * 32 + l32;
+    qok[qb] = t < t1;
+    qtok[qb] = qok[qb] ? t : t1 - 1;
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)qtok[qb] * rs + h * D + half * 8;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const bf16x8 raw = load_bf16x8(qp + 16 * k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[qb][k][e] = (__bf16)((float)raw[e] * a.c2_text);
+      asm volatile("" : "+a"(qreg[qb][k]));
+    }
+  }
+
+  // Stage copies: an SGPR base per stage (row `start` of the segment, head h) and per-lane
+  // 32-bit offsets (row inside the stage, clamped to the segment, and swizzled chunk).
+  const __bf16* k_text = a.tk;
+  const __bf16* k_video = static_cast<const __bf16*>(a.k);
+  const __bf16* v_text = a.tv;
+  const __bf16* v_video = a.v;
+  const uint32_t rs2 = (uint32_t)rs * 2;  // row stride in bytes
+  int lrow[NI];
+  uint32_t loff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    lrow[i] = (wave * NI + i) * RPI + lane / CPR;
+    loff[i] = (uint32_t)((lane % CPR) ^ swz<CPR>(lrow[i])) * 16;
+  }
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Ks[0][0] + wave * NI * RPI * D * 2);
+  const uint32_t lds_v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vs[0][0] + wave * NI * RPI * D * 2);
+  // A stage copy: source stage `src` (its rows past the segment: the segment's last row)
+  // into LDS buffer `buf`.  Prepared after a barrier, issued a few instructions at a time
+  // inside the blocks that follow (K rows by the first, V rows by the second): issued all
+  // at once they stall the wave behind the vector memory queue.
+  struct Copy {
+    const __bf16* kb;
+    const __bf16* vb;
+    uint32_t off[NI];
+    uint32_t m0k, m0v;
+  };
+  auto prep = [&](int src, int buf) __attribute__((always_inline)) {
+    bool text;
+    int start, valid;
+    kw.stage_at(src, text, start, valid);
+    Copy c;
+    const size_t base = (size_t)start * rs + h * D;
+    c.kb = (text ? k_text : k_video) + base;
+    c.vb = (text ? v_text : v_video) + base;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) c.off[i] = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
+    c.m0k = lds_k + (uint32_t)buf * (BN * D * 2);
+    c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
+    return c;
+  };
+  auto copy_k = [&](const Copy& c, int i) __attribute__((always_inline)) {
+    dma16(c.kb, c.off[i], c.m0k + i * RPI * D * 2);
+  };
+  auto copy_v = [&](const Copy& c, int i) __attribute__((always_inline)) {
+    dma16(c.vb, c.off[i], c.m0v + i * RPI * D * 2);
+  };
+
+  int krd[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  int vrd[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
+      const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      vrd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
+    }
+  // operand reads from LDS buffer `buf`, keys sub * BC ..: V operand i = (G, dt) =
+  // (i / DT, i % DT), K operand k.  The per-lane LDS addresses are opaque to the compiler,
+  // so that with constant buffers every other term becomes the read's immediate offset
+  // (else it keeps a base register per buffer).
+  using lds_b64 = __attribute__((address_space(3))) i16x4;
+  using lds_b128 = __attribute__((address_space(3))) const bf16x8;
+  uint32_t kad[KS], vad[DT][2];
+  {
+    const uint32_t kbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Ks[0][0];
+    const uint32_t vbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vs[0][0];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      kad[k] = kbase + 2 * krd[k];
+      asm volatile("" : "+v"(kad[k]));
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        vad[dt][c] = vbase + 2 * vrd[dt][c];
+        asm volatile("" : "+v"(vad[dt][c]));
+      }
+  }
+  auto rdv = [&](int buf, int sub, int i) __attribute__((always_inline)) {
+    const uint32_t off = 2 * (buf * BN + sub * BC + 16 * (i / DT)) * D;
+    const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (lds_b64*)(uintptr_t)(vad[i % DT][0] + off)));
+    const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (lds_b64*)(uintptr_t)(vad[i % DT][1] + off)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  auto rdk = [&](int buf, int sub, int k) __attribute__((always_inline)) {
+    return *(lds_b128*)(uintptr_t)(kad[k] + 2 * (buf * BN + sub * BC) * D);
+  };
+
+  // per query block: O^T accumulators (AGPRs), reference m (log2 domain: set by the first
+  // sub-tile, moved only when a sub-tile exceeds it by more than 8), row sum l
+  f32x16 o[QB][DT];
+  float m[QB], l[QB];
+  f32x16 negm[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qb][dt] = 0.0f;
+    m[qb] = 0.0f;
+    l[qb] = 0.0f;
+    negm[qb] = 0.0f;
+  }
+  f32x16 S[2][QB];  // scores of two consecutive sub-tiles
+  bf16x8 P[QB][2];  // probabilities of one sub-tile (MFMA B-operand order)
+
+  auto fence_s = [&](f32x16 (&s)[QB]) __attribute__((always_inline)) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+  };
+  auto fence_o = [&]() __attribute__((always_inline)) {
+    if constexpr (DT == 4)
+      asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+    else
+      asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+  };
+  // O lives in AGPRs from the start (its zero fill included)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(o[qb][dt]));
+
+  // exponential pair u = (qb, u % 8) of s into pb (bf16) and its sum into ps
+  auto expo_unit = [&](const f32x16 (&s)[QB], bf16x8 (&pb)[QB][2], float (&ps)[QB], int u)
+      __attribute__((always_inline)) {
+    const int qb = u / 8, r = 2 * (u % 8);
+    const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][r]), __builtin_amdgcn_exp2f(s[qb][r + 1]));
+    ps[qb] = add_bf16x2(pk, ps[qb]);
+    uint4 w = __builtin_bit_cast(uint4, pb[qb][r >> 3]);
+    const int e = (r & 7) >> 1;
+    if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
+    pb[qb][r >> 3] = __builtin_bit_cast(bf16x8, w);
+  };
+
+  // One block of work, a single stream of MFMAs with the vector work between them:
+  //   PREV:   O += V^T P^T for the previous sub-tile (buffer pbuf, keys psub * BC.., its
+  //           probabilities in P, its first LA V operands already in vin), beside the
+  //           lane-local row maxima of the current sub-tile's scores sc;
+  //   NEXT_S: scores of the next sub-tile (buffer nbuf, keys nsub * BC..) into sn, against
+  //           the current m, beside the current sub-tile's probabilities P = 2^sc (taken
+  //           before the maxima are checked) and their sums;
+  //   NEXT_V: the first LA V operands of (xbuf, xsub) into vout.
+  // At the end, if some score exceeds m by more than 8 (rare), m moves up: O, l and the
+  // scores are shifted and pc is redone.  Keys past the end of a segment (vc < BC) repeat
+  // its last key, so they leave the maxima unchanged; they are dropped from pc and l.
+  // CP: 0 none, 1 the K rows of copy cp, 2 its V rows, spread over the MFMA slots.
+  auto block = [&](auto prev, auto next_s, auto next_v, auto cpk, const Copy& cp, int pbuf, int psub,
+                   const bf16x8 (&vin)[LA], f32x16 (&sc)[QB], int vc, int nbuf, int nsub, f32x16 (&sn)[QB],
+                   int xbuf, int xsub, bf16x8 (&vout)[LA]) __attribute__((always_inline)) {
+    constexpr int CP = decltype(cpk)::value;
+    bf16x8 (&pc)[QB][2] = P;
+    constexpr bool PREV = decltype(prev)::value, NEXT_S = decltype(next_s)::value;
+    constexpr bool NEXT_V = decltype(next_v)::value;
+    constexpr int NOPV = PREV ? NV : 0, NOP = NOPV + (NEXT_S ? KS : 0);
+    constexpr int NMF = QB * NOP;          // MFMAs
+    constexpr int NMP = QB * NOPV;         // P V MFMAs (they read P: the exponentials come after)
+    constexpr int NIT = 8 * QB;            // items of each kind: maxima of pairs, exponential pairs
+    static_assert(NMF > 0, "a block issues MFMAs");
+    bf16x8 op[NOP + LA];
+    auto fetch = [&](int n) __attribute__((always_inline)) {
+      if (n < NOPV) op[n] = rdv(pbuf, psub, n);
+      else if (n < NOP) op[n] = rdk(nbuf, nsub, n - NOPV);
+      else if (NEXT_V) op[n] = rdv(xbuf, xsub, n - NOP);
+    };
+    if constexpr (PREV) {
+#pragma unroll
+      for (int n = 0; n < LA; ++n) op[n] = vin[n];
+    } else {
+#pragma unroll
+      for (int n = 0; n < LA; ++n) fetch(n);
+    }
+    float mx[QB], ps[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      mx[qb] = -INFINITY;
+      ps[qb] = 0.0f;
+    }
+    // (one v_max3 per pair: fmaxf would first quiet each operand, the scores come out of asm)
+    auto max_item = [&](int u) __attribute__((always_inline)) {
+      const int qb = u / 8, r = 2 * (u % 8);
+      asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx[qb]) : "v"(mx[qb]), "v"(sc[qb][r]), "v"(sc[qb][r + 1]));
+    };
+#pragma unroll
+    for (int sl = 0; sl < NMF; ++sl) {
+      const int n = sl / QB, qb = sl % QB;
+      if (qb == 0) fetch(n + LA);
+      if (n < NOPV) {
+        mfma_pv(o[qb][n % DT], op[n], P[qb][n / DT]);
+      } else {
+        const int k = n - NOPV;
+        if (k == 0) mfma_qk0(sn[qb], op[n], qreg[qb][0], negm[qb]);
+        else mfma_qk(sn[qb], op[n], qreg[qb][k]);
+      }
+      if (sl == 0) fence_s(sc);
+      if constexpr (CP != 0) {
+        constexpr int GAP = NMF / NI;  // MFMA slots per copy instruction
+        if (sl % GAP == GAP / 2) {
+          if (CP == 1) copy_k(cp, sl / GAP);
+          else copy_v(cp, sl / GAP);
+        }
+      }
+      // maxima beside the P V MFMAs, exponentials beside the score MFMAs (after every
+      // read of P); a block without one of the two spreads both kinds over its MFMAs
+      if constexpr (NMP > 0 && NMP < NMF) {
+        if (sl < NMP) {
+#pragma unroll
+          for (int it = sl * NIT / NMP; it < (sl + 1) * NIT / NMP; ++it) max_item(it);
+        } else {
+#pragma unroll
+          for (int it = (sl - NMP) * NIT / (NMF - NMP); it < (sl - NMP + 1) * NIT / (NMF - NMP); ++it)
+            expo_unit(sc, pc, ps, it);
+        }
+      } else {
+#pragma unroll
+        for (int it = sl * NIT / NMF; it < (sl + 1) * NIT / NMF; ++it) max_item(it);
+        if (NMP == 0 || sl == NMF - 1) {
+          // no P V to wait for (NMP == 0), or the last P V issued: the exponentials
+#pragma unroll
+          for (int it = (NMP == 0 ? sl * NIT / NMF : 0); it < (NMP == 0 ? (sl + 1) * NIT / NMF : NIT); ++it)
+            expo_unit(sc, pc, ps, it);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // (keeps the sums in the block: else they sink past the branch below)
+    asm volatile("" ::"v"(ps[0]), "v"(ps[1]));
+    if constexpr (NEXT_V) {
+#pragma unroll
+      for (int n = 0; n < LA; ++n) vout[n] = op[NOP + n];
+    }
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) up |= mx[qb] > 8.0f;
+    if (__any(up)) {
+      fence_o();
+      if constexpr (NEXT_S) fence_s(sn);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float shift = fmaxf(pair_max(mx[qb]), 0.0f);
+        const float alpha = __builtin_amdgcn_exp2f(-shift);
+        m[qb] += shift;
+        negm[qb] = -m[qb];
+        l[qb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
+        sc[qb] -= shift;
+        if constexpr (NEXT_S) sn[qb] -= shift;
+        ps[qb] = 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8 * QB; ++u) expo_unit(sc, pc, ps, u);
+      // VALU writes of negm and O, read next by MFMAs
+      asm volatile("s_nop 1" : "+v"(negm[0]), "+v"(negm[1]));
+      fence_o();
+    }
+    if (vc < BC) {
+      // keys R, R + 1 of pc's dword (G, e): R = 16 G + 8 (e >> 1) + 4 half + 2 (e & 1)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        ps[qb] = 0.0f;
+#pragma unroll
+        for (int G = 0; G < 2; ++G) {
+          uint4 w = __builtin_bit_cast(uint4, pc[qb][G]);
+          uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int R = 16 * G + 8 * (e >> 1) + 4 * half + 2 * (e & 1);
+            d[e] &= R + 1 < vc ? 0xffffffffu : (R < vc ? 0x0000ffffu : 0u);
+            ps[qb] = add_bf16x2(d[e], ps[qb]);
+          }
+          pc[qb][G] = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      l[qb] += ps[qb];
+      asm volatile("" ::"v"(pc[qb][0]), "v"(pc[qb][1]), "v"(l[qb]));
+    }
+  };
+  auto valid_of = [&](int j) __attribute__((always_inline)) {
+    bool text;
+    int start, valid;
+    kw.stage_at(j, text, start, valid);
+    return valid;
+  };
+  auto barrier_wait = [&]() __attribute__((always_inline)) {
+    // stage j + 1 landed in this wave (only the copy of stage j + 2 may still be in
+    // flight), this wave's LDS reads done, then every wave at the barrier
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NI) : "memory");
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+
+  // prologue: stages 0..2 in flight (always three copies, so that the waits below count
+  // the same in every tile: past the last stage, a repeat of it into the free buffer);
+  // stage 0 landed; scores of sub-tile 0; m = their row maxima
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    const Copy c = prep(imin(st, nst - 1), st);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) copy_k(c, i);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) copy_v(c, i);
+  }
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * NI) : "memory");
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const bf16x8 kop = rdk(0, 0, k);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (k == 0) mfma_qk0(S[0][qb], kop, qreg[qb][0], negm[qb]);
+      else mfma_qk(S[0][qb], kop, qreg[qb][k]);
+    }
+  }
+  fence_s(S[0]);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[0][qb][r]);
+    m[qb] = pair_max(mx);  // keys past a segment repeat its last key: no mask needed
+    negm[qb] = -m[qb];
+    S[0][qb] -= m[qb];
+  }
+  asm volatile("s_nop 1" : "+v"(negm[0]), "+v"(negm[1]));
+  bf16x8 va[LA], vb[LA];
+  int vj = valid_of(0);
+  // sub-tile 0: P_0, scores of sub-tile 1, the first V operands of sub-tile 0
+  const Copy none{};
+  using C0 = std::integral_constant<int, 0>;
+  using CK = std::integral_constant<int, 1>;
+  using CV = std::integral_constant<int, 2>;
+  block(F{}, T{}, T{}, C0{}, none, 0, 0, va, S[0], vj, 0, 1, S[1], 0, 0, va);
+
+  // Stage j (LDS buffer B = j % 4): sub-tiles 2 j + 1 and 2 j + 2.  The main loop takes
+  // four stages at a time, so that the buffers are constants; the rest go one by one.
+  auto iter = [&](int j, int B) __attribute__((always_inline)) {
+    const int B1 = (B + 1) & (NBUF - 1);
+    barrier_wait();
+    // stage j + 3 into the buffer of stage j - 1, which every wave is done with
+    const Copy cp = prep(imin(j + 3, nst - 1), (B + 3) & (NBUF - 1));
+    const int vn = valid_of(j + 1);
+    // P V of sub-tile 2 j; sub-tile 2 j + 1 (stage j, keys 32..63); scores of 2 j + 2
+    block(T{}, T{}, T{}, CK{}, cp, B, 0, va, S[1], vj - BC, B1, 0, S[0], B, 1, vb);
+    // P V of sub-tile 2 j + 1; sub-tile 2 j + 2 (stage j + 1, keys 0..31); scores of 2 j + 3
+    block(T{}, T{}, T{}, CV{}, cp, B, 1, vb, S[0], vn, B1, 1, S[1], B1, 0, va);
+    vj = vn;
+  };
+  int j = 0;
+  for (; j + 4 < nst; j += 4) {
+    iter(j, 0);
+    iter(j + 1, 1);
+    iter(j + 2, 2);
+    iter(j + 3, 3);
+  }
+  for (; j + 1 < nst; ++j) iter(j, j & (NBUF - 1));
+  // last stage: P V of sub-tile 2 j; sub-tile 2 j + 1; then its P V
+  const int bl = j & (NBUF - 1);
+  block(T{}, F{}, T{}, C0{}, none, bl, 0, va, S[1], vj - BC, 0, 0, S[0], bl, 1, vb);
+  {
+    bf16x8 op[NV + LA];
+#pragma unroll
+    for (int n = 0; n < LA; ++n) op[n] = vb[n];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if (i + LA < NV) op[i + LA] = rdv(bl, 1, i + LA);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mfma_pv(o[qb][i % DT], op[i], P[qb][i / DT]);
+    }
+  }
+  // the repeated copies issued for stages past the last may still be landing
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  fence_o();
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lq = pair_sum(l[qb]);
+    if (a.lse && qok[qb] && half == 0) a.lse[(size_t)qtok[qb] * g.H + h] = m[qb] + __log2f(lq);
+    const float inv = 1.0f / lq;
+    const size_t orow = (size_t)qtok[qb] * rs + h * D;
+    __bf16* arow = a.acat + (size_t)qtok[qb] * 2 * rs + h * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        float x[4], y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = o[qb][dt][4 * (2 * ip) + e] * inv;
+          y[e] = o[qb][dt][4 * (2 * ip + 1) + e] * inv;
+        }
+        permlane32_swap4(x, y);
+        const int c0 = 32 * dt + 16 * ip + 8 * half;
+        const float ov[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        const uint4 graw = *reinterpret_cast<const uint4*>(a.gs + orow + c0);
+        const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          r[e] = sigmoid(bf16_to_f32((e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffff))) * ov[e];
+        if (qok[qb]) {
+          *reinterpret_cast<uint4*>(arow + c0) = make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]),
+                                                             pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7]));
+          if (a.o_dbg) {
+            *reinterpret_cast<float4*>(a.o_dbg + orow + c0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+            *reinterpret_cast<float4*>(a.o_dbg + orow + c0 + 4) = make_float4(ov[4], ov[5], ov[6], ov[7]);
+          }
+        }
+      }
+  }
+}
+
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream) {
   const int tiles = count_tiles(a.geo, 256);
   if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles * a.geo.H), block(512);
+  dim3 grid(tiles * a.geo.H), block(256);
   if (a.geo.d == 128)
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_kernel<128, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128>), grid, block, 0, stream, a);
   else if (a.geo.d == 64)
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_kernel<64, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -389,7 +888,7 @@ hipError_t launch_softmax_fp8(const SoftmaxArgs& a, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   if (a.geo.d != 128) return hipErrorInvalidValue;
   dim3 grid(tiles * a.geo.H), block(512);
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_kernel<128, true>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_fp8_kernel<128>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
