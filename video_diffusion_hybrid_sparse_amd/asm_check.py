@@ -1,0 +1,208 @@
+"""Static check of the wait states around the inline-asm MFMAs of the bf16 softmax kernel.
+
+The software-pipelined softmax writes its MFMAs as inline asm (to pin register classes),
+so the compiler's hazard recognizer does not see them as matrix instructions and inserts
+no wait states for them.  The kernel places its own (register-tied s_nop fences), but the
+compiler is still free to put a VALU move (a rematerialised constant, a register copy)
+right before an MFMA that reads its result.  This module compiles the kernel to gfx950
+assembly and checks, on the control-flow graph of each kernel, the CDNA3/CDNA4 rules that
+apply to these instructions:
+
+  - a VALU write of a VGPR or AGPR that an MFMA then reads (A, B or C operand): at least
+    2 wait states between them;
+  - an 8-pass MFMA's result (32x32x16 bf16) read or overwritten by the VALU, or read by a
+    store: at least 12 wait states (NumPasses + 3, plus one on gfx950);
+  - an MFMA's C operand overwritten by the VALU: at least 11 wait states.
+
+A wait state is one issued instruction; s_nop N counts N + 1.  Used by build() and by a
+CPU test; the build fails on any violation.
+"""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import tempfile
+
+VALU_TO_MFMA = 2
+MFMA_TO_VALU_READ = 12
+MFMA_SRCC_TO_VALU_WRITE = 11
+KERNEL_PREFIX = "_ZN3vdn17softmax_sw_kernel"
+
+_REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
+_STORE = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store", "flat_store")
+_LOAD = ("ds_read", "ds_load", "global_load", "buffer_load", "scratch_load", "flat_load")
+
+
+def _regs(text: str) -> set[tuple[str, int]]:
+    out = set()
+    for m in _REG.finditer(text):
+        if m.group(1):
+            out.update((m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1))
+        else:
+            out.add((m.group(4), int(m.group(5))))
+    return out
+
+
+class _Inst:
+    __slots__ = ("op", "dst", "src", "srcc", "nop", "text")
+
+    def __init__(self, op, dst, src, srcc, nop, text):
+        self.op, self.dst, self.src, self.srcc, self.nop, self.text = op, dst, src, srcc, nop, text
+
+    @property
+    def valu(self) -> bool:
+        return self.op.startswith("v_") and not self.op.startswith("v_mfma")
+
+    @property
+    def mfma(self) -> bool:
+        return self.op.startswith("v_mfma")
+
+
+def _parse(line: str):
+    line = line.split(";")[0].strip()
+    if not line:
+        return None
+    parts = line.split(None, 1)
+    op, rest = parts[0], (parts[1] if len(parts) > 1 else "")
+    operands = [x.strip() for x in re.split(r",(?![^\[]*\])", rest)] if rest else []
+    if op == "s_nop":
+        return _Inst(op, set(), set(), set(), int(operands[0], 0) + 1, line)
+    if op.startswith("s_") or op.startswith("v_cmp"):
+        # scalar instructions touch no vector registers; v_cmp writes VCC or SGPRs
+        src = set()
+        for x in (operands[1:] if op.startswith("v_cmp") else []):
+            src |= _regs(x)
+        return _Inst(op, set(), src, set(), 1, line)
+    if op.startswith(_STORE):
+        src = set()
+        for x in operands:
+            src |= _regs(x)
+        return _Inst(op, set(), src, set(), 1, line)
+    dst = _regs(operands[0]) if operands else set()
+    src = set()
+    for x in operands[1:]:
+        src |= _regs(x)
+    srcc = _regs(operands[3]) if op.startswith("v_mfma") and len(operands) > 3 else set()
+    return _Inst(op, dst, src, srcc, 1, line)
+
+
+def _kernels(asm: str) -> dict[str, list]:
+    """Kernel name -> list of (label or None, instruction or None) in program order."""
+    out, cur, name = {}, None, None
+    for raw in asm.split("\n"):
+        if re.match(r"^[A-Za-z_][\w.]*:", raw) and not raw.startswith("."):
+            label = raw.split(":")[0]
+            if label.startswith(KERNEL_PREFIX):
+                name, cur = label, []
+                out[name] = cur
+                continue
+        if cur is None:
+            continue
+        if raw.startswith("\ts_endpgm") or raw.strip() == "s_endpgm":
+            cur.append((None, _parse("s_endpgm")))
+            cur = None
+            continue
+        m = re.match(r"^(\.LBB\d+_\d+):", raw)
+        if m:
+            cur.append((m.group(1), None))
+            continue
+        if raw.startswith("\t") and not raw.startswith("\t."):
+            inst = _parse(raw)
+            if inst is not None:
+                cur.append((None, inst))
+    return out
+
+
+def _preds(items):
+    """Index -> list of predecessor instruction indices (program order plus branches)."""
+    idx_of_label = {}
+    for i, (lab, _) in enumerate(items):
+        if lab:
+            idx_of_label[lab] = i
+    preds = {i: [] for i in range(len(items))}
+    for i, (lab, inst) in enumerate(items):
+        if i + 1 < len(items):
+            prev_uncond = inst is not None and (inst.op in ("s_branch", "s_endpgm", "s_setpc_b64"))
+            if not prev_uncond:
+                preds[i + 1].append(i)
+        if inst is not None and inst.op.startswith(("s_branch", "s_cbranch")):
+            target = inst.text.split()[-1]
+            if target in idx_of_label:
+                preds[idx_of_label[target]].append(i)
+    return preds
+
+
+def _search(items, preds, start, need, hit):
+    """Walk back from instruction `start` through the CFG while fewer than `need` wait
+    states separate it; return the first instruction for which hit(inst) holds."""
+    stack = [(p, 0) for p in preds[start]]
+    seen = set()
+    while stack:
+        i, waited = stack.pop()
+        if (i, waited) in seen:
+            continue
+        seen.add((i, waited))
+        lab, inst = items[i]
+        if inst is None:
+            stack.extend((p, waited) for p in preds[i])
+            continue
+        if hit(inst):
+            return inst, waited
+        waited += inst.nop
+        if waited < need:
+            stack.extend((p, waited) for p in preds[i])
+    return None
+
+
+def check_asm(asm: str) -> list[str]:
+    problems = []
+    kernels = _kernels(asm)
+    if not kernels:
+        return ["no softmax_sw_kernel in the assembly"]
+    for name, items in kernels.items():
+        preds = _preds(items)
+        for i, (lab, inst) in enumerate(items):
+            if inst is None:
+                continue
+            if inst.mfma:
+                reads = inst.src
+                r = _search(items, preds, i, VALU_TO_MFMA, lambda p: p.valu and (p.dst & reads))
+                if r:
+                    problems.append(f"{name}: VALU write '{r[0].text}' then MFMA read after {r[1]} wait states: '{inst.text}'")
+            if inst.valu or inst.op.startswith(_STORE):
+                touched = inst.src | (inst.dst if inst.valu else set())
+                r = _search(items, preds, i, MFMA_TO_VALU_READ, lambda p: p.mfma and (p.dst & touched))
+                if r:
+                    problems.append(f"{name}: MFMA result '{r[0].text}' used after {r[1]} wait states: '{inst.text}'")
+                if inst.valu and inst.dst:
+                    w = inst.dst
+                    r = _search(items, preds, i, MFMA_SRCC_TO_VALU_WRITE, lambda p: p.mfma and (p.srcc & w) and not (p.dst & w))
+                    if r:
+                        problems.append(f"{name}: MFMA C operand '{r[0].text}' overwritten after {r[1]} wait states: '{inst.text}'")
+    return problems
+
+
+def kernel_asm(src: str | None = None) -> str:
+    """gfx950 assembly of the softmax source, compiled with the library's flags."""
+    from .build import CSRC, FLAGS, HIPCC
+    src = src or os.path.join(CSRC, "softmax_bf16.hip")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "softmax.s")
+        flags = [f for f in FLAGS if f != "-fPIC"]
+        r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", out], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("compiling the softmax kernel to assembly failed:\n" + r.stderr[-4000:])
+        with open(out) as fh:
+            return fh.read()
+
+
+def check(src: str | None = None) -> list[str]:
+    return check_asm(kernel_asm(src))
+
+
+if __name__ == "__main__":
+    import sys
+    found = check(sys.argv[1] if len(sys.argv) > 1 else None)
+    print("\n".join(found) if found else "no MFMA wait-state violations")
+    sys.exit(1 if found else 0)

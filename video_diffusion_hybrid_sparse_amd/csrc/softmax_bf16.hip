@@ -23,7 +23,8 @@
 // Scores stay in the log2 domain, relative to a reference m that is set by the first
 // sub-tile and only moves when a sub-tile exceeds it by more than 8, so the O rescale is
 // rare.  Any fixed reference point gives the same softmax; the row sum is taken over the
-// same bf16 probabilities that multiply V.
+// same bf16 probabilities that multiply V (fp8: VALU adds; bf16: ones x P^T on the
+// matrix cores).
 //
 // bf16 inputs (softmax_sw_kernel): four waves, 64 queries each, one wave per SIMD, with
 // the matrix and vector work of each wave software-pipelined (see the kernel).  Q^T is
@@ -377,21 +378,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // its copy instructions spread over the MFMA slots of the two blocks that follow.  The
 // stage loop takes four stages at a time so that buffer offsets are immediates.
 //
-// Measured on MI355X (probes of single instruction kinds beside a stream of 32x32x16
-// MFMAs, one wave per SIMD): v_exp_f32, v_cvt_pk_bf16_f32, v_max3_f32, v_add_f32 and
-// v_mul_f32 cost under one cycle each beside an MFMA, v_dot2c_f32_bf16 about 16, so row
-// sums are formed with plain adds (add_bf16x2).
+// Row sums are formed by the matrix cores: one more MFMA per 16 keys and query block,
+// ones x P^T, over exactly the bf16 P that multiplies V (every row of the accumulator
+// holds the sum).  Measured on MI355X (probes of single instruction kinds beside a stream
+// of 32x32x16 MFMAs, one wave per SIMD): v_exp_f32, v_cvt_pk_bf16_f32, v_max3_f32,
+// v_add_f32 and v_mul_f32 cost under one cycle each beside an MFMA, v_dot2c_f32_bf16
+// about 16; the vector work of a block is what bounds it, so it moves to the matrix cores
+// wherever an MFMA can do it.
 //
 // The MFMAs are written as inline asm so that the scores stay in VGPRs (the VALU reads
 // them) while Q^T and O stay in AGPRs; the compiler's automatic choice moves them back
 // and forth.  The compiler does not see these as matrix instructions, so the wait states
 // a VALU read of an MFMA result needs (12 for this 8-pass MFMA) are given explicitly by
 // register-tied s_nop fences; every VALU write that an MFMA reads is at least two
-// instructions before it (fenced where it is not).
+// instructions before it (fenced where it is not).  asm_check.py verifies these wait
+// states on the compiled code (the build fails on a violation).
 namespace {
-__device__ __forceinline__ void mfma_qk0(f32x16& d, const bf16x8& k, const bf16x8& q, const f32x16& c) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(k), "a"(q), "v"(c));
-}
 __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& k, const bf16x8& q) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
 }
@@ -548,18 +550,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   // per query block: O^T accumulators (AGPRs), reference m (log2 domain: set by the first
-  // sub-tile, moved only when a sub-tile exceeds it by more than 8), row sum l
-  f32x16 o[QB][DT];
-  float m[QB], l[QB];
-  f32x16 negm[QB];
+  // sub-tile, moved only when a sub-tile exceeds it by more than 8), and the row sums,
+  // formed by the matrix cores as ones x P^T over the same bf16 P that multiplies V
+  // (every row of lsum holds the sum of its column's query; AGPRs)
+  f32x16 o[QB][DT], lsum[QB];
+  float m[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qb][dt] = 0.0f;
+    lsum[qb] = 0.0f;
     m[qb] = 0.0f;
-    l[qb] = 0.0f;
-    negm[qb] = 0.0f;
   }
+  bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                 (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  // opaque from here on: a constant the compiler rematerialises (VALU moves) right before
+  // the asm MFMA that reads it, without the wait states it does not know are needed
+  asm volatile("" : "+v"(ones));
   f32x16 S[2][QB];  // scores of two consecutive sub-tiles
   bf16x8 P[QB][2];  // probabilities of one sub-tile (MFMA B-operand order)
 
@@ -569,22 +576,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto fence_o = [&]() __attribute__((always_inline)) {
     if constexpr (DT == 4)
       asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+                   "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]), "+a"(lsum[0]), "+a"(lsum[1]));
     else
-      asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+      asm volatile("s_nop 7\n\ts_nop 7" : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]),
+                   "+a"(lsum[0]), "+a"(lsum[1]));
   };
-  // O lives in AGPRs from the start (its zero fill included)
+  // O and the row sums live in AGPRs from the start (their zero fill included)
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(o[qb][dt]));
+    asm volatile("" : "+a"(lsum[qb]));
+  }
 
-  // exponential pair u = (qb, u % 8) of s into pb (bf16) and its sum into ps
-  auto expo_unit = [&](const f32x16 (&s)[QB], bf16x8 (&pb)[QB][2], float (&ps)[QB], int u)
-      __attribute__((always_inline)) {
+  // exponential pair u = (qb, u % 8) of s into pb (bf16)
+  auto expo_unit = [&](const f32x16 (&s)[QB], bf16x8 (&pb)[QB][2], int u) __attribute__((always_inline)) {
     const int qb = u / 8, r = 2 * (u % 8);
     const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][r]), __builtin_amdgcn_exp2f(s[qb][r + 1]));
-    ps[qb] = add_bf16x2(pk, ps[qb]);
     uint4 w = __builtin_bit_cast(uint4, pb[qb][r >> 3]);
     const int e = (r & 7) >> 1;
     if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
@@ -592,16 +600,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   // One block of work, a single stream of MFMAs with the vector work between them:
-  //   PREV:   O += V^T P^T for the previous sub-tile (buffer pbuf, keys psub * BC.., its
-  //           probabilities in P, its first LA V operands already in vin), beside the
-  //           lane-local row maxima of the current sub-tile's scores sc;
+  //   PREV:   O += V^T P^T and lsum += ones P^T for the previous sub-tile (buffer pbuf,
+  //           keys psub * BC.., its probabilities in P, its first LA V operands already
+  //           in vin), beside the lane-local row maxima of the current sub-tile's scores sc;
   //   NEXT_S: scores of the next sub-tile (buffer nbuf, keys nsub * BC..) into sn, against
   //           the current m, beside the current sub-tile's probabilities P = 2^sc (taken
-  //           before the maxima are checked) and their sums;
+  //           before the maxima are checked);
   //   NEXT_V: the first LA V operands of (xbuf, xsub) into vout.
-  // At the end, if some score exceeds m by more than 8 (rare), m moves up: O, l and the
-  // scores are shifted and pc is redone.  Keys past the end of a segment (vc < BC) repeat
-  // its last key, so they leave the maxima unchanged; they are dropped from pc and l.
+  // At the end, if some score exceeds m by more than 8 (rare), m moves up: O, the row sums
+  // and the scores are shifted and pc is redone.  Keys past the end of a segment (vc < BC)
+  // repeat its last key, so they leave the maxima unchanged; they are dropped from pc.
   // CP: 0 none, 1 the K rows of copy cp, 2 its V rows, spread over the MFMA slots.
   auto block = [&](auto prev, auto next_s, auto next_v, auto cpk, const Copy& cp, int pbuf, int psub,
                    const bf16x8 (&vin)[LA], f32x16 (&sc)[QB], int vc, int nbuf, int nsub, f32x16 (&sn)[QB],
@@ -611,8 +619,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr bool PREV = decltype(prev)::value, NEXT_S = decltype(next_s)::value;
     constexpr bool NEXT_V = decltype(next_v)::value;
     constexpr int NOPV = PREV ? NV : 0, NOP = NOPV + (NEXT_S ? KS : 0);
-    constexpr int NMF = QB * NOP;          // MFMAs
-    constexpr int NMP = QB * NOPV;         // P V MFMAs (they read P: the exponentials come after)
+    constexpr int NMP = QB * (NOPV + (PREV ? 2 : 0));  // P V and row-sum MFMAs (they read P)
+    constexpr int NMF = NMP + QB * (NOP - NOPV);      // MFMAs
     constexpr int NIT = 8 * QB;            // items of each kind: maxima of pairs, exponential pairs
     static_assert(NMF > 0, "a block issues MFMAs");
     bf16x8 op[NOP + LA];
@@ -628,12 +636,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int n = 0; n < LA; ++n) fetch(n);
     }
-    float mx[QB], ps[QB];
+    float mx[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      mx[qb] = -INFINITY;
-      ps[qb] = 0.0f;
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
+    if constexpr (NEXT_S && NMP < 2) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sn[qb] = -m[qb];
+      asm volatile("s_nop 1" : "+v"(sn[0]), "+v"(sn[1]));  // VALU write, then MFMA read
     }
+
     // (one v_max3 per pair: fmaxf would first quiet each operand, the scores come out of asm)
     auto max_item = [&](int u) __attribute__((always_inline)) {
       const int qb = u / 8, r = 2 * (u % 8);
@@ -641,16 +652,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 #pragma unroll
     for (int sl = 0; sl < NMF; ++sl) {
-      const int n = sl / QB, qb = sl % QB;
-      if (qb == 0) fetch(n + LA);
-      if (n < NOPV) {
+      const int qb = sl % QB;
+      if (sl < QB * NOPV) {
+        // P V: operand n of the stream
+        const int n = sl / QB;
+        if (qb == 0) fetch(n + LA);
         mfma_pv(o[qb][n % DT], op[n], P[qb][n / DT]);
+      } else if (sl < NMP) {
+        // row sums of keys 16 G .. 16 G + 15
+        mfma_pv(lsum[qb], ones, P[qb][(sl - QB * NOPV) / QB]);
       } else {
-        const int k = n - NOPV;
-        if (k == 0) mfma_qk0(sn[qb], op[n], qreg[qb][0], negm[qb]);
-        else mfma_qk(sn[qb], op[n], qreg[qb][k]);
+        // scores: operand n = NOPV + k of the stream
+        const int k = (sl - NMP) / QB, n = NOPV + k;
+        if (qb == 0) fetch(n + LA);
+        mfma_qk(sn[qb], op[n], qreg[qb][k]);
       }
       if (sl == 0) fence_s(sc);
+      // the next scores start at -m: their accumulators (the registers of the sub-tile
+      // before the current one, done with) are filled by the VALU two slots before the
+      // first score MFMA reads them (a block without P V fills them before its first slot)
+      if constexpr (NEXT_S && NMP >= 2) {
+        if (sl == NMP - 2) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) sn[qb] = -m[qb];
+          // (all sixteen moves here: else the compiler sinks copies to just before the MFMA)
+          asm volatile("" : "+v"(sn[0]), "+v"(sn[1]));
+        }
+      }
       if constexpr (CP != 0) {
         constexpr int GAP = NMF / NI;  // MFMA slots per copy instruction
         if (sl % GAP == GAP / 2) {
@@ -667,7 +695,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         } else {
 #pragma unroll
           for (int it = (sl - NMP) * NIT / (NMF - NMP); it < (sl - NMP + 1) * NIT / (NMF - NMP); ++it)
-            expo_unit(sc, pc, ps, it);
+            expo_unit(sc, pc, it);
         }
       } else {
 #pragma unroll
@@ -676,13 +704,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           // no P V to wait for (NMP == 0), or the last P V issued: the exponentials
 #pragma unroll
           for (int it = (NMP == 0 ? sl * NIT / NMF : 0); it < (NMP == 0 ? (sl + 1) * NIT / NMF : NIT); ++it)
-            expo_unit(sc, pc, ps, it);
+            expo_unit(sc, pc, it);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // (keeps the sums in the block: else they sink past the branch below)
-    asm volatile("" ::"v"(ps[0]), "v"(ps[1]));
+    // (keeps the exponentials in the block: else they sink past the branches below)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(pc[qb][0]), "v"(pc[qb][1]));
     if constexpr (NEXT_V) {
 #pragma unroll
       for (int n = 0; n < LA; ++n) vout[n] = op[NOP + n];
@@ -698,25 +727,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float shift = fmaxf(pair_max(mx[qb]), 0.0f);
         const float alpha = __builtin_amdgcn_exp2f(-shift);
         m[qb] += shift;
-        negm[qb] = -m[qb];
-        l[qb] *= alpha;
+        // one 16-register tile at a time through the VALU, each put back into AGPRs
+        // before the next (else the compiler stages all of O in VGPRs at once)
+        lsum[qb] *= alpha;
+        asm volatile("" : "+a"(lsum[qb]));
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[qb][dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) {
+          o[qb][dt] *= alpha;
+          asm volatile("" : "+a"(o[qb][dt]));
+        }
         sc[qb] -= shift;
         if constexpr (NEXT_S) sn[qb] -= shift;
-        ps[qb] = 0.0f;
       }
 #pragma unroll
-      for (int u = 0; u < 8 * QB; ++u) expo_unit(sc, pc, ps, u);
-      // VALU writes of negm and O, read next by MFMAs
-      asm volatile("s_nop 1" : "+v"(negm[0]), "+v"(negm[1]));
+      for (int u = 0; u < 8 * QB; ++u) expo_unit(sc, pc, u);
+      // VALU writes of O and the row sums, read next by MFMAs
       fence_o();
     }
     if (vc < BC) {
       // keys R, R + 1 of pc's dword (G, e): R = 16 G + 8 (e >> 1) + 4 half + 2 (e & 1)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        ps[qb] = 0.0f;
 #pragma unroll
         for (int G = 0; G < 2; ++G) {
           uint4 w = __builtin_bit_cast(uint4, pc[qb][G]);
@@ -725,16 +756,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           for (int e = 0; e < 4; ++e) {
             const int R = 16 * G + 8 * (e >> 1) + 4 * half + 2 * (e & 1);
             d[e] &= R + 1 < vc ? 0xffffffffu : (R < vc ? 0x0000ffffu : 0u);
-            ps[qb] = add_bf16x2(d[e], ps[qb]);
           }
           pc[qb][G] = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
         }
       }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      l[qb] += ps[qb];
-      asm volatile("" ::"v"(pc[qb][0]), "v"(pc[qb][1]), "v"(l[qb]));
     }
   };
   auto valid_of = [&](int j) __attribute__((always_inline)) {
@@ -764,12 +789,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * NI) : "memory");
 #pragma unroll
+  for (int qb = 0; qb < QB; ++qb) S[0][qb] = 0.0f;
+  asm volatile("s_nop 1" : "+v"(S[0][0]), "+v"(S[0][1]));  // VALU write, then MFMA read
+#pragma unroll
   for (int k = 0; k < KS; ++k) {
     const bf16x8 kop = rdk(0, 0, k);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (k == 0) mfma_qk0(S[0][qb], kop, qreg[qb][0], negm[qb]);
-      else mfma_qk(S[0][qb], kop, qreg[qb][k]);
+      mfma_qk(S[0][qb], kop, qreg[qb][k]);
     }
   }
   fence_s(S[0]);
@@ -779,10 +806,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[0][qb][r]);
     m[qb] = pair_max(mx);  // keys past a segment repeat its last key: no mask needed
-    negm[qb] = -m[qb];
     S[0][qb] -= m[qb];
   }
-  asm volatile("s_nop 1" : "+v"(negm[0]), "+v"(negm[1]));
   bf16x8 va[LA], vb[LA];
   int vj = valid_of(0);
   // sub-tile 0: P_0, scores of sub-tile 1, the first V operands of sub-tile 0
@@ -827,6 +852,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mfma_pv(o[qb][i % DT], op[i], P[qb][i / DT]);
     }
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mfma_pv(lsum[qb], ones, P[qb][G]);
   }
   // the repeated copies issued for stages past the last may still be landing
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -834,7 +863,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lq = pair_sum(l[qb]);
+    const float lq = lsum[qb][0];  // every row of lsum holds its query's sum
     if (a.lse && qok[qb] && half == 0) a.lse[(size_t)qtok[qb] * g.H + h] = m[qb] + __log2f(lq);
     const float inv = 1.0f / lq;
     const size_t orow = (size_t)qtok[qb] * rs + h * D;
