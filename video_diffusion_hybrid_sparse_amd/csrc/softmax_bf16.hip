@@ -379,8 +379,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // stage loop takes four stages at a time so that buffer offsets are immediates.
 //
 // Row sums are formed by the matrix cores: one more MFMA per 16 keys and query block,
-// ones x P^T, over exactly the bf16 P that multiplies V (every row of the accumulator
-// holds the sum).  Measured on MI355X (probes of single instruction kinds beside a stream
+// e0 x P^T (row 0 of A all ones, the other rows zero), over exactly the bf16 P that
+// multiplies V.  Measured on MI355X (probes of single instruction kinds beside a stream
 // of 32x32x16 MFMAs, one wave per SIMD): v_exp_f32, v_cvt_pk_bf16_f32, v_max3_f32,
 // v_add_f32 and v_mul_f32 cost under one cycle each beside an MFMA, v_dot2c_f32_bf16
 // about 16; the vector work of a block is what bounds it, so it moves to the matrix cores
@@ -551,8 +551,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // per query block: O^T accumulators (AGPRs), reference m (log2 domain: set by the first
   // sub-tile, moved only when a sub-tile exceeds it by more than 8), and the row sums,
-  // formed by the matrix cores as ones x P^T over the same bf16 P that multiplies V
-  // (every row of lsum holds the sum of its column's query; AGPRs)
+  // formed by the matrix cores as e0 x P^T over the same bf16 P that multiplies V (row 0
+  // of lsum holds the sum of its column's query, the other rows stay zero; AGPRs)
   f32x16 o[QB][DT], lsum[QB];
   float m[QB];
 #pragma unroll
@@ -564,8 +564,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                  (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-  // opaque from here on: a constant the compiler rematerialises (VALU moves) right before
-  // the asm MFMA that reads it, without the wait states it does not know are needed
+  // One-hot in fact: A rows other than row 0 are zero (only row 0 of the product is used,
+  // and zero operands cost the matrix cores less power).  Opaque from here on: a constant
+  // the compiler rematerialises (VALU moves) right before the asm MFMA that reads it,
+  // without the wait states it does not know are needed.
+  if (l32 != 0) ones = bf16x8{};
   asm volatile("" : "+v"(ones));
   f32x16 S[2][QB];  // scores of two consecutive sub-tiles
   bf16x8 P[QB][2];  // probabilities of one sub-tile (MFMA B-operand order)
@@ -863,7 +866,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lq = lsum[qb][0];  // every row of lsum holds its query's sum
+    const float lq = pair_sum(lsum[qb][0]);  // row 0 (lanes 0-31, element 0) + zeros
     if (a.lse && qok[qb] && half == 0) a.lse[(size_t)qtok[qb] * g.H + h] = m[qb] + __log2f(lq);
     const float inv = 1.0f / lq;
     const size_t orow = (size_t)qtok[qb] * rs + h * D;
