@@ -378,8 +378,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // its copy instructions spread over the MFMA slots of the two blocks that follow.  The
 // stage loop takes four stages at a time so that buffer offsets are immediates.
 //
-// Row sums are formed by the matrix cores: one more MFMA per 16 keys and query block,
-// e0 x P^T (row 0 of A all ones, the other rows zero), over exactly the bf16 P that
+// Row sums are formed by the matrix cores: one 16x16x32 MFMA per 16 keys and query block,
+// a two-row selector times P^T (its other rows zero), over exactly the bf16 P that
 // multiplies V.  Measured on MI355X (probes of single instruction kinds beside a stream
 // of 32x32x16 MFMAs, one wave per SIMD): v_exp_f32, v_cvt_pk_bf16_f32, v_max3_f32,
 // v_add_f32 and v_mul_f32 cost under one cycle each beside an MFMA, v_dot2c_f32_bf16
@@ -399,6 +399,12 @@ __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& k, const bf16x8
 }
 __device__ __forceinline__ void mfma_pv(f32x16& d, const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(v), "v"(p));
+}
+// 16x16x32: lane l supplies A[l % 16][its 8 k] and B[its 8 k][l % 16], where "its 8 k"
+// are the same k for A and B and depend only on the lane group l / 16; lane l receives
+// C[4 (l / 16) + r][l % 16], r = 0..3
+__device__ __forceinline__ void mfma_sum(f32x4& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 }  // namespace
 
@@ -551,9 +557,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // per query block: O^T accumulators (AGPRs), reference m (log2 domain: set by the first
   // sub-tile, moved only when a sub-tile exceeds it by more than 8), and the row sums,
-  // formed by the matrix cores as e0 x P^T over the same bf16 P that multiplies V (row 0
-  // of lsum holds the sum of its column's query, the other rows stay zero; AGPRs)
-  f32x16 o[QB][DT], lsum[QB];
+  // formed by the matrix cores over the same bf16 P that multiplies V (AGPRs)
+  f32x16 o[QB][DT];
+  f32x4 lsum[QB];
   float m[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -562,13 +568,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lsum[qb] = 0.0f;
     m[qb] = 0.0f;
   }
+  // Row-sum selector for the 16x16x32 MFMA.  P^T as its B operand: lane l holds 8 keys of
+  // query l % 32, so lane groups 0 and 2 (lanes j, j + 32) hold the 16 keys of query j and
+  // groups 1 and 3 (lanes j + 16, j + 48) those of query j + 16.  A row 0 = ones on the k
+  // of groups 0 and 2, row 1 = ones on the k of groups 1 and 3, the other rows zero: C[0][j]
+  // and C[1][j], in lane j (elements 0 and 1), are the sums of queries j and j + 16.
+  // Opaque from here on: a constant the compiler rematerialises (VALU moves) right before
+  // the asm MFMA that reads it, without the wait states it does not know are needed.
+  const int lg = lane >> 4, lr = lane & 15;
   bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                  (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-  // One-hot in fact: A rows other than row 0 are zero (only row 0 of the product is used,
-  // and zero operands cost the matrix cores less power).  Opaque from here on: a constant
-  // the compiler rematerialises (VALU moves) right before the asm MFMA that reads it,
-  // without the wait states it does not know are needed.
-  if (l32 != 0) ones = bf16x8{};
+  if (!((lr == 0 && (lg & 1) == 0) || (lr == 1 && (lg & 1) == 1))) ones = bf16x8{};
   asm volatile("" : "+v"(ones));
   f32x16 S[2][QB];  // scores of two consecutive sub-tiles
   bf16x8 P[QB][2];  // probabilities of one sub-tile (MFMA B-operand order)
@@ -603,7 +613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   // One block of work, a single stream of MFMAs with the vector work between them:
-  //   PREV:   O += V^T P^T and lsum += ones P^T for the previous sub-tile (buffer pbuf,
+  //   PREV:   O += V^T P^T and the row sums for the previous sub-tile (buffer pbuf,
   //           keys psub * BC.., its probabilities in P, its first LA V operands already
   //           in vin), beside the lane-local row maxima of the current sub-tile's scores sc;
   //   NEXT_S: scores of the next sub-tile (buffer nbuf, keys nsub * BC..) into sn, against
@@ -663,7 +673,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mfma_pv(o[qb][n % DT], op[n], P[qb][n / DT]);
       } else if (sl < NMP) {
         // row sums of keys 16 G .. 16 G + 15
-        mfma_pv(lsum[qb], ones, P[qb][(sl - QB * NOPV) / QB]);
+        mfma_sum(lsum[qb], ones, P[qb][(sl - QB * NOPV) / QB]);
       } else {
         // scores: operand n = NOPV + k of the stream
         const int k = (sl - NMP) / QB, n = NOPV + k;
@@ -722,7 +732,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     bool up = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) up |= mx[qb] > 8.0f;
-    if (__any(up)) {
+    if (__builtin_expect(__any(up), 0)) {  // rare: keep it out of the block's straight line
       fence_o();
       if constexpr (NEXT_S) fence_s(sn);
 #pragma unroll
@@ -732,7 +742,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         m[qb] += shift;
         // one 16-register tile at a time through the VALU, each put back into AGPRs
         // before the next (else the compiler stages all of O in VGPRs at once)
-        lsum[qb] *= alpha;
+        // lane j < 16 holds the sums of queries j and j + 16 (alpha of query q: lane q)
+        const float alpha_hi = __shfl(alpha, lr + 16);
+        lsum[qb][0] *= alpha;
+        lsum[qb][1] *= alpha_hi;
         asm volatile("" : "+a"(lsum[qb]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -747,7 +760,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // VALU writes of O and the row sums, read next by MFMAs
       fence_o();
     }
-    if (vc < BC) {
+    if (__builtin_expect(vc < BC, 0)) {
       // keys R, R + 1 of pc's dword (G, e): R = 16 G + 8 (e >> 1) + 4 half + 2 (e & 1)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -858,7 +871,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int G = 0; G < 2; ++G)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) mfma_pv(lsum[qb], ones, P[qb][G]);
+      for (int qb = 0; qb < QB; ++qb) mfma_sum(lsum[qb], ones, P[qb][G]);
   }
   // the repeated copies issued for stages past the last may still be landing
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -866,7 +879,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lq = pair_sum(lsum[qb][0]);  // row 0 (lanes 0-31, element 0) + zeros
+    // the sum of query l32: lane l32 % 16, element l32 / 16
+    const float s0 = __shfl(lsum[qb][0], l32 & 15), s1 = __shfl(lsum[qb][1], l32 & 15);
+    const float lq = l32 < 16 ? s0 : s1;
     if (a.lse && qok[qb] && half == 0) a.lse[(size_t)qtok[qb] * g.H + h] = m[qb] + __log2f(lq);
     const float inv = 1.0f / lq;
     const size_t orow = (size_t)qtok[qb] * rs + h * D;
