@@ -23,9 +23,10 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+// LDS address of a shared-memory location plus a byte offset, as a wave-uniform value.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p, int off) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p + off);
 }
 
 __device__ __forceinline__ float sig(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -296,16 +297,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   const float lse = a.lse[(size_t)qtok * g.H + h];
   const float delta = a.delta[(size_t)qtok * g.H + h];
-  const intptr_t tk_off = reinterpret_cast<intptr_t>(a.tk) - reinterpret_cast<intptr_t>(a.k);
-  const intptr_t tv_off = reinterpret_cast<intptr_t>(a.tv) - reinterpret_cast<intptr_t>(a.v);
   __builtin_amdgcn_s_waitcnt(0);
 
-  int lrow[NI], lcol[NI];
+  // stage copies (dma16, not tracked by the compiler's waits): an SGPR base per stage and
+  // per-lane 32-bit offsets (row inside the stage, clamped to the segment; swizzled chunk)
+  const uint32_t rs2 = (uint32_t)rs * 2;
+  int lrow[NI];
+  uint32_t loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
+    loff[i] = (uint32_t)((lane % CPR) ^ swz<CPR>(lrow[i])) * 16;
   }
+  const uint32_t m0k = lds_addr(&Ks[0][0], wave * NI * RPI * D * 2);
+  const uint32_t m0v = lds_addr(&Vs[0][0], wave * NI * RPI * D * 2);
   auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
     int len, base;
     if (j < n0) { base = 0; len = g.L; }
@@ -319,13 +324,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     int start, valid;
     stage_at(j, start, valid);
     const bool text = j < n0;
-    const __bf16* kb = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.k) + (text ? tk_off : 0));
-    const __bf16* vb = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.v) + (text ? tv_off : 0));
+    const size_t base = (size_t)start * rs + h * D;
+    const __bf16* kb = (text ? a.tk : a.k) + base;
+    const __bf16* vb = (text ? a.tv : a.v) + base;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const size_t row = (size_t)(start + imin(lrow[i], valid - 1));
-      load_lds16(kb + row * rs + lcol[i], &Ks[buf][(wave * NI + i) * RPI * D]);
-      load_lds16(vb + row * rs + lcol[i], &Vs[buf][(wave * NI + i) * RPI * D]);
+      const uint32_t off = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
+      dma16(kb, off, m0k + (uint32_t)buf * (BN * D * 2) + i * RPI * D * 2);
+      dma16(vb, off, m0v + (uint32_t)buf * (BN * D * 2) + i * RPI * D * 2);
     }
   };
   int krd[KS];
@@ -471,20 +477,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // copies of its last row)
   if constexpr (PASS == 1) {
     constexpr int NIV = BK * CPR / (64 * NW);
+    const __bf16* vb = vbase + (size_t)kstart * rs + h * D;
+    const uint32_t m0 = lds_addr(&Vt[0], wave * 64 * 16);
 #pragma unroll
     for (int i = 0; i < NIV; ++i) {
       const int q = i * 64 * NW + tid, r = q / CPR, c = q % CPR;
-      const size_t row = (size_t)(kstart + imin(r, kvalid - 1));
-      load_lds16(vbase + row * rs + h * D + (c ^ swz<CPR>(r)) * 8, &Vt[(i * 64 * NW + wave * 64) * 8]);
+      dma16(vb, (uint32_t)imin(r, kvalid - 1) * ((uint32_t)rs * 2) + (uint32_t)(c ^ swz<CPR>(r)) * 16,
+            m0 + i * 64 * NW * 16);
     }
   }
 
-  int lrow[NI], lcol[NI];
+  const uint32_t rs2 = (uint32_t)rs * 2;
+  int lrow[NI];
+  uint32_t loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
+    loff[i] = (uint32_t)((lane % CPR) ^ swz<CPR>(lrow[i])) * 16;
   }
+  const uint32_t m0q = lds_addr(&Qs[0][0], wave * NI * RPI * D * 2);
+  const uint32_t m0o = lds_addr(&Os[0][0], wave * NI * RPI * D * 2);
   auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
     int len, base;
     if (j < n1) { base = qs.s0; len = qs.l0; }
@@ -505,11 +517,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       lse_next = a.lse[(size_t)row * g.H + h];
       delta_next = a.delta[(size_t)row * g.H + h];
     }
+    const size_t base = (size_t)start * rs + h * D;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const size_t row = (size_t)(start + imin(lrow[i], valid - 1));
-      load_lds16(a.q + row * rs + lcol[i], &Qs[buf][(wave * NI + i) * RPI * D]);
-      load_lds16(a.dO + row * rs + lcol[i], &Os[buf][(wave * NI + i) * RPI * D]);
+      const uint32_t off = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
+      dma16(a.q + base, off, m0q + (uint32_t)buf * (BQ * D * 2) + i * RPI * D * 2);
+      dma16(a.dO + base, off, m0o + (uint32_t)buf * (BQ * D * 2) + i * RPI * D * 2);
     }
   };
   auto put_stats = [&](int buf) __attribute__((always_inline)) {
