@@ -44,11 +44,6 @@ namespace vdn {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void load_lds16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
-}
-
 __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // e4m3 x e4m3 (format selectors 0), unit block scales (E8M0 127 = 2^0)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -146,42 +141,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   }
 
-  // Per-lane constants of the stage loads: row inside the stage and swizzled column.
-  int lrow[NI], lcol[NI];
+  // Stage copies (dma16: the compiler does not wait for them before LDS reads; the loop
+  // waits for each stage itself): an SGPR base per stage (row `start`, head h) and per-lane
+  // 32-bit offsets (row inside the stage, clamped to the segment, and swizzled chunk).
+  // Rows past the segment are copies of its last row, masked later.
+  const uint32_t rsb = (uint32_t)rs * 2;  // bf16 row stride in bytes
+  int lrow[NI];
+  uint32_t loff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    lcol[i] = ((lane % CPR) ^ swz<CPR>(lrow[i])) * 8 + h * D;
+    loff[i] = (uint32_t)((lane % CPR) ^ swz<CPR>(lrow[i])) * 16;
   }
+  const uint32_t m0k = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Ks[0][0] + wave * NI * RPI * D * 2);
+  const uint32_t m0k8 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Ks[0][0] + wave * NI8 * RPI8 * D);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vs[0][0] + wave * NI * RPI * D * 2);
   auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     bool text;
     int start, valid;
     kw.stage_at(j, text, start, valid);
+    const uint32_t bo = (uint32_t)buf * (BN * D * 2);
     if (!text) {
       // e4m3 keys: rows of D bytes, CPR8 chunks
-      const uint8_t* kb = static_cast<const uint8_t*>(a.k);
-      uint8_t* kd = reinterpret_cast<uint8_t*>(Ks[buf]);
+      const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)start * rs + h * D;
 #pragma unroll
       for (int i = 0; i < NI8; ++i) {
         const int r = (wave * NI8 + i) * RPI8 + lane / CPR8;
-        const int row = start + imin(r, valid - 1);
-        const size_t o = (size_t)row * rs + h * D + ((lane % CPR8) ^ swz<CPR8>(r)) * 16;
-        load_lds16(kb + o, kd + (wave * NI8 + i) * RPI8 * D);
+        const uint32_t o = (uint32_t)imin(r, valid - 1) * (uint32_t)rs + (uint32_t)((lane % CPR8) ^ swz<CPR8>(r)) * 16;
+        dma16(kb, o, m0k8 + bo + i * RPI8 * D);
       }
     } else {
-      const __bf16* kb = text ? a.tk : static_cast<const __bf16*>(a.k);
+      const __bf16* kb = a.tk + (size_t)start * rs + h * D;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int row = start + imin(lrow[i], valid - 1);  // rows past the segment: masked later
-        load_lds16(kb + (size_t)row * rs + lcol[i], &Ks[buf][(wave * NI + i) * RPI * D]);
-      }
+      for (int i = 0; i < NI; ++i) dma16(kb, (uint32_t)imin(lrow[i], valid - 1) * rsb + loff[i], m0k + bo + i * RPI * D * 2);
     }
-    const __bf16* vb = text ? a.tv : a.v;
+    const __bf16* vb = (text ? a.tv : a.v) + (size_t)start * rs + h * D;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = start + imin(lrow[i], valid - 1);
-      load_lds16(vb + (size_t)row * rs + lcol[i], &Vs[buf][(wave * NI + i) * RPI * D]);
-    }
+    for (int i = 0; i < NI; ++i) dma16(vb, (uint32_t)imin(lrow[i], valid - 1) * rsb + loff[i], m0v + bo + i * RPI * D * 2);
   };
 
   // LDS read offsets (elements / bytes), the same for every sub-tile (the swizzle depends
