@@ -1,4 +1,4 @@
-"""The static wait-state check of the bf16 softmax kernel's inline-asm MFMAs: the checker
+"""The static wait-state check of the inline-asm MFMAs (bf16 softmax, merged dK/dV backward): the checker
 flags planted hazards in small assembly listings, and the kernel as compiled is clean."""
 import shutil
 
@@ -42,5 +42,6 @@ def test_agpr_write_then_mfma_accumulate_flagged():
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not __import__("os").path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not installed")
-def test_softmax_kernel_as_compiled_is_clean():
+def test_kernels_as_compiled_are_clean():
+    """The bf16 softmax and the merged dK/dV backward, compiled with the library's flags."""
     assert asm_check.check() == []

@@ -1,12 +1,13 @@
-"""Static check of the wait states around the inline-asm MFMAs of the bf16 softmax kernel.
+"""Static check of the wait states around inline-asm MFMAs: the bf16 softmax kernel and
+the merged dK/dV softmax backward kernel.
 
-The software-pipelined softmax writes its MFMAs as inline asm (to pin register classes),
-so the compiler's hazard recognizer does not see them as matrix instructions and inserts
-no wait states for them.  The kernel places its own (register-tied s_nop fences), but the
-compiler is still free to put a VALU move (a rematerialised constant, a register copy)
-right before an MFMA that reads its result.  This module compiles the kernel to gfx950
-assembly and checks, on the control-flow graph of each kernel, the CDNA3/CDNA4 rules that
-apply to these instructions:
+Both kernels write their MFMAs as inline asm (to pin register classes), so the compiler's
+hazard recognizer does not see them as matrix instructions and inserts no wait states for
+them.  The kernels place their own (register-tied s_nop fences), but the compiler is
+still free to put a VALU move (a rematerialised constant, a register copy) right before
+an MFMA that reads its result.  This module compiles the sources to gfx950 assembly and
+checks, on the control-flow graph of each such kernel, the CDNA3/CDNA4 rules that apply
+to these instructions:
 
   - a VALU write of a VGPR or AGPR that an MFMA then reads (A, B or C operand): at least
     2 wait states between them;
@@ -27,7 +28,10 @@ import tempfile
 VALU_TO_MFMA = 2
 MFMA_TO_VALU_READ = 12
 MFMA_SRCC_TO_VALU_WRITE = 11
-KERNEL_PREFIX = "_ZN3vdn17softmax_sw_kernel"
+# (source file under csrc/, mangled-name prefix of the kernels written with asm MFMAs)
+TARGETS = (("softmax_bf16.hip", "_ZN3vdn17softmax_sw_kernel"),
+           ("backward.hip", "_ZN3vdn21softmax_bwd_kv_kernel"))
+PREFIXES = tuple(p for _, p in TARGETS)
 
 _REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
 _STORE = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store", "flat_store")
@@ -87,13 +91,13 @@ def _parse(line: str):
     return _Inst(op, dst, src, srcc, 1, line)
 
 
-def _kernels(asm: str) -> dict[str, list]:
+def _kernels(asm: str, prefixes=PREFIXES) -> dict[str, list]:
     """Kernel name -> list of (label or None, instruction or None) in program order."""
     out, cur, name = {}, None, None
     for raw in asm.split("\n"):
         if re.match(r"^[A-Za-z_][\w.]*:", raw) and not raw.startswith("."):
             label = raw.split(":")[0]
-            if label.startswith(KERNEL_PREFIX):
+            if label.startswith(tuple(prefixes)):
                 name, cur = label, []
                 out[name] = cur
                 continue
@@ -155,11 +159,11 @@ def _search(items, preds, start, need, hit):
     return None
 
 
-def check_asm(asm: str) -> list[str]:
+def check_asm(asm: str, prefixes=PREFIXES) -> list[str]:
     problems = []
-    kernels = _kernels(asm)
+    kernels = _kernels(asm, prefixes)
     if not kernels:
-        return ["no softmax_sw_kernel in the assembly"]
+        return ["none of the kernels " + ", ".join(prefixes) + " in the assembly"]
     for name, items in kernels.items():
         preds = _preds(items)
         for i, (lab, inst) in enumerate(items):
@@ -183,22 +187,29 @@ def check_asm(asm: str) -> list[str]:
     return problems
 
 
-def kernel_asm(src: str | None = None) -> str:
-    """gfx950 assembly of the softmax source, compiled with the library's flags."""
-    from .build import CSRC, FLAGS, HIPCC
-    src = src or os.path.join(CSRC, "softmax_bf16.hip")
+def kernel_asm(src: str) -> str:
+    """gfx950 assembly of a source file, compiled with the library's flags."""
+    from .build import FLAGS, HIPCC
     with tempfile.TemporaryDirectory() as d:
-        out = os.path.join(d, "softmax.s")
+        out = os.path.join(d, "kernels.s")
         flags = [f for f in FLAGS if f != "-fPIC"]
         r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", out], capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError("compiling the softmax kernel to assembly failed:\n" + r.stderr[-4000:])
+            raise RuntimeError(f"compiling {src} to assembly failed:\n" + r.stderr[-4000:])
         with open(out) as fh:
             return fh.read()
 
 
 def check(src: str | None = None) -> list[str]:
-    return check_asm(kernel_asm(src))
+    """Problems found in one source file (every checked kernel in it), or, with no
+    argument, in each of the library's sources that holds asm-MFMA kernels."""
+    if src is not None:
+        return check_asm(kernel_asm(src))
+    from .build import CSRC
+    problems = []
+    for name, prefix in TARGETS:
+        problems += check_asm(kernel_asm(os.path.join(CSRC, name)), (prefix,))
+    return problems
 
 
 if __name__ == "__main__":

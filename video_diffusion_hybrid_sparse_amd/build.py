@@ -52,11 +52,12 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs, "-L", os.path.join(ROCM, "lib"),
           "-lhipblaslt", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"])
     os.replace(tmp, LIB)
-    # the bf16 softmax writes its MFMAs as inline asm: check the wait states around them
+    # the bf16 softmax and the merged dK/dV backward write their MFMAs as inline asm:
+    # check the wait states around them
     from .asm_check import check
     problems = check()
     if problems:
-        raise RuntimeError("softmax kernel: MFMA wait-state violations:\n" + "\n".join(problems))
+        raise RuntimeError("MFMA wait-state violations:\n" + "\n".join(problems))
     return LIB
 
 

@@ -419,38 +419,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
-// ---- 3b. softmax backward, dK and dV ----------------------------------------------------
-// One workgroup = 256 keys of one frame (or of the text) and one head, 8 waves x 32 keys
-// (two waves per SIMD).  The queries that read a video key frame are the key segments of
-// its chunk's group (anchor frames and text: every query).  Queries arrive in 64-query
-// stages (HBM -> LDS, double-buffered), computed as two 32-query halves so that the score
-// tiles of one half fit beside the key-side registers.  Per half: S = Q K^T and
-// dP = dO V^T (Q and dO rows are MFMA A operands, the key is lane-local);
-// P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and dK^T += Q^T dS with dO^T
-// and Q^T gathered by the transposing LDS read.  dk = scale dK.  The two gradients are
-// separate passes (PASS 0: dV from S; PASS 1: dK from S and dP, the tile's values in LDS
-// as the B operand of dP): one set of accumulators per pass fits two waves per SIMD.
-template <int D, int PASS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bwd_dkdv_kernel(SoftmaxBwdArgs a) {
-  constexpr int NW = 8, BK = 256, BQ = 64;
+// ---- 3b. softmax backward, dK and dV in one pass ---------------------------------------
+// One workgroup = 256 keys of one frame (or of the text) and one head, 4 waves x 64 keys
+// (one wave per SIMD).  The wave keeps its keys' K and V rows in registers (MFMA B
+// operands, key lane-local) and its dK^T and dV^T accumulators (64 keys x D each) in the
+// matrix registers.  Queries stream through LDS in 64-query stages, three buffers deep,
+// with their log-sum-exp and Delta; each stage runs as two 32-query halves.  Per half:
+// S = Q K^T and dP = dO V^T (Q and dO rows from LDS are the A operands, each feeding both
+// 32-key sub-tiles); P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and
+// dK^T += Q^T dS (dO^T and Q^T by the transposing LDS read, each feeding both sub-tiles).
+// Per (query, key) pair 8 d multiply-adds against 10 d for separate dV and dK passes,
+// and every LDS operand read feeds two MFMAs.
+// The kernel's MFMAs are inline asm so that the register classes are fixed: scores in
+// VGPRs (the vector unit reads them), dK^T and dV^T in AGPRs.  The compiler's hazard
+// recognizer does not see them, so the kernel places the wait states itself: 2 between
+// a vector write and an MFMA reading it, 16 between an MFMA and a vector read of its
+// result (asm_check verifies the compiled code).
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void mma_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_a(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_bwd_kv_kernel(SoftmaxBwdArgs a) {
+  constexpr int NW = 4, BK = 256, BQ = 64, NBUF = 3;
   constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
-  constexpr int NI = BQ * CPR / (64 * NW);
+  constexpr int NI = BQ * CPR / (64 * NW);  // 16-byte copies per lane per stage and tensor
   static_assert(NI >= 1, "stage size");
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Os[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[BK * D];  // the tile's values (B operand of dP)
-  __shared__ __attribute__((aligned(16))) float Ls[2][BQ], Dl[2][BQ];
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[NBUF][BQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Os[NBUF][BQ * D];
+  __shared__ __attribute__((aligned(16))) float Ls[NBUF][BQ], Dl[NBUF][BQ];
   const Geo g = a.geo;
-  // key tiles of one head: text tiles, then the tiles of frames 0 .. F-1; anchors' and
-  // text tiles first (they see every query)
+  // key tiles of one head: anchor 0's tiles, anchor F-1's tiles, text tiles, then frames
+  // 1 .. F-2 (the anchors' and the text's tiles see every query: largest first);
+  // XCD-aware: XCD x takes a contiguous range of the logical order
   const int ntt = (g.L + BK - 1) / BK, tpf = (g.T + BK - 1) / BK;
   const int per_head = ntt + g.F * tpf;
-  const int h = blockIdx.x / per_head;
-  int kt = blockIdx.x - h * per_head;
+  const int total = per_head * g.H;
+  const int hid = blockIdx.x, xcd = hid & 7;
+  const int lid = xcd * (total >> 3) + imin(xcd, total & 7) + (hid >> 3);
+  const int h = lid / per_head;
+  int kt = lid - h * per_head;
   bool text;
   int kframe = -1, kstart, kvalid;
   {
-    // order: anchor 0's tiles, anchor F-1's tiles, text tiles, then frames 1 .. F-2
     if (kt < tpf) { text = false; kframe = 0; kstart = kt * BK; }
     else if ((kt -= tpf) < tpf) { text = false; kframe = g.F - 1; kstart = (g.F - 1) * g.T + kt * BK; }
     else if ((kt -= tpf) < ntt) { text = true; kstart = kt * BK; }
@@ -461,32 +482,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const KeySegs qs = group_keys(g, (text || kframe == 0 || kframe == g.F - 1) ? 0 : 2 + kframe / g.C);
   const int n1 = (qs.l0 + BQ - 1) / BQ, n2 = (qs.l1 + BQ - 1) / BQ, n3 = (qs.l2 + BQ - 1) / BQ;
   const int nst = n1 + n2 + n3;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)g.H * D;
 
-  int ktok = kstart + wave * 32 + l32;
-  const bool kok = wave * 32 + l32 < kvalid;
-  ktok = kok ? ktok : kstart + kvalid - 1;
+  // the wave's keys: 64 w + 32 t + l32 of the tile (t = 0, 1), clamped to the tile
   const __bf16* kbase = text ? a.tk : a.k;
   const __bf16* vbase = text ? a.tv : a.v;
-  bf16x8 kreg[KS];
+  bf16x8 kreg[2][KS], vreg[2][KS];
+  int ktok[2];
+  bool kok[2];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) kreg[s] = load_bf16x8(kbase + (size_t)ktok * rs + h * D + half * 8 + 16 * s);
-  __builtin_amdgcn_s_waitcnt(0);
-  // value rows of the tile into LDS (XOR-swizzled 16-byte chunks; rows past the tile are
-  // copies of its last row)
-  if constexpr (PASS == 1) {
-    constexpr int NIV = BK * CPR / (64 * NW);
-    const __bf16* vb = vbase + (size_t)kstart * rs + h * D;
-    const uint32_t m0 = lds_addr(&Vt[0], wave * 64 * 16);
+  for (int t = 0; t < 2; ++t) {
+    const int kr = wave * 64 + t * 32 + l32;
+    kok[t] = kr < kvalid;
+    ktok[t] = kstart + imin(kr, kvalid - 1);
 #pragma unroll
-    for (int i = 0; i < NIV; ++i) {
-      const int q = i * 64 * NW + tid, r = q / CPR, c = q % CPR;
-      dma16(vb, (uint32_t)imin(r, kvalid - 1) * ((uint32_t)rs * 2) + (uint32_t)(c ^ swz<CPR>(r)) * 16,
-            m0 + i * 64 * NW * 16);
+    for (int s2 = 0; s2 < KS; ++s2) {
+      kreg[t][s2] = load_bf16x8(kbase + (size_t)ktok[t] * rs + h * D + half * 8 + 16 * s2);
+      vreg[t][s2] = load_bf16x8(vbase + (size_t)ktok[t] * rs + h * D + half * 8 + 16 * s2);
     }
   }
 
+  // stage copies (dma16/dma4, waited for explicitly): SGPR base per stage, per-lane offsets
   const uint32_t rs2 = (uint32_t)rs * 2;
   int lrow[NI];
   uint32_t loff[NI];
@@ -497,6 +515,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   const uint32_t m0q = lds_addr(&Qs[0][0], wave * NI * RPI * D * 2);
   const uint32_t m0o = lds_addr(&Os[0][0], wave * NI * RPI * D * 2);
+  const uint32_t m0s = lds_addr(wave == 0 ? &Ls[0][0] : &Dl[0][0], 0);
   auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
     int len, base;
     if (j < n1) { base = qs.s0; len = qs.l0; }
@@ -505,17 +524,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     start = base + BQ * j;
     valid = len - BQ * j;
   };
-  // per-query lse and Delta of the next sub-tile: loaded into registers before its
-  // HBM -> LDS copies (so waiting for them does not wait for the copies), written to LDS
-  // at the end of the current sub-tile
-  float lse_next = 0.0f, delta_next = 0.0f;
+  // stage j into buffer buf: waves 0 and 1 first copy the 64 log-sum-exps / Deltas (one
+  // dword per lane), then every wave its share of the Q and dO rows (2 NI copies)
   auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     int start, valid;
     stage_at(j, start, valid);
-    if (tid < BQ) {
-      const int row = start + imin(tid, valid - 1);
-      lse_next = a.lse[(size_t)row * g.H + h];
-      delta_next = a.delta[(size_t)row * g.H + h];
+    if (wave < 2) {
+      const float* sb = (wave == 0 ? a.lse : a.delta) + (size_t)start * g.H + h;
+      dma4(sb, (uint32_t)imin(lane, valid - 1) * (uint32_t)g.H * 4, m0s + (uint32_t)buf * (BQ * 4));
     }
     const size_t base = (size_t)start * rs + h * D;
 #pragma unroll
@@ -523,12 +539,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       const uint32_t off = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
       dma16(a.q + base, off, m0q + (uint32_t)buf * (BQ * D * 2) + i * RPI * D * 2);
       dma16(a.dO + base, off, m0o + (uint32_t)buf * (BQ * D * 2) + i * RPI * D * 2);
-    }
-  };
-  auto put_stats = [&](int buf) __attribute__((always_inline)) {
-    if (tid < BQ) {
-      Ls[buf][tid] = lse_next;
-      Dl[buf][tid] = delta_next;
     }
   };
   int qrd[KS];
@@ -545,86 +555,130 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
       trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
     }
 
-  f32x16 acc[DT];  // PASS 0: dV^T, PASS 1: dK^T
+  f32x16 dv[DT][2], dk[DT][2];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      dv[i][t] = 0.0f;
+      dk[i][t] = 0.0f;
+    }
+  // the accumulators live in the matrix registers from here on (also on the path that
+  // skips the loop)
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    asm volatile("s_nop 1" : "+a"(dv[dt][0]), "+a"(dv[dt][1]), "+a"(dk[dt][0]), "+a"(dk[dt][1]));
   const float c2 = a.c2;
 
-  if (nst > 0) {
-    issue(0, 0);
-    put_stats(0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (nst > 0) issue(0, 0);
+  if (nst > 1) issue(1, 1);
+  // stage 0 landed: at most the 2 NI row copies of stage 1 (issued after its dword copy)
+  // may still be outstanding
+  if (nst > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int j = 0; j < nst; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nst) issue(j + 1, buf ^ 1);
+    const int buf = j % NBUF;
+    if (j + 2 < nst) issue(j + 2, (j + 2) % NBUF);
     int start, valid;
     stage_at(j, start, valid);
+#pragma unroll 1
     for (int rt = 0; rt < 2; ++rt) {  // 32-query halves of the stage
-    if (rt * 32 >= valid) break;
-    const __bf16* Q = Qs[buf] + 32 * rt * D;
-    const __bf16* O = Os[buf] + 32 * rt * D;
-    f32x16 s = 0.0f, dp = 0.0f;
+      if (rt * 32 >= valid) break;
+      const __bf16* Q = Qs[buf] + 32 * rt * D;
+      const __bf16* O = Os[buf] + 32 * rt * D;
+      f32x16 s[2], dp[2];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Q + qrd[k]), kreg[k], s);
-      if constexpr (PASS == 1)
-        dp = mfma32x32x16(*reinterpret_cast<const bf16x8*>(O + qrd[k]),
-                          *reinterpret_cast<const bf16x8*>(&Vt[wave * 32 * D + qrd[k]]), dp);
-    }
-    // accumulator row = query 32 rt + 8 (r/4) + 4 half + r%4 of the stage
-    bf16x8 pb[2], sb[2];
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Q + qrd[k]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(O + qrd[k]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (k == 0) {
+            mma_first(s[t], qa, kreg[t][k]);
+            mma_first(dp[t], oa, vreg[t][k]);
+          } else {
+            mma_v(s[t], qa, kreg[t][k]);
+            mma_v(dp[t], oa, vreg[t][k]);
+          }
+        }
+      }
+      asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(dp[0]), "+v"(dp[1]));
+      // accumulator row r = query 32 rt + 8 (r/4) + 4 half + r%4 of the stage, column = key
+      bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int q0 = rt * 32 + 8 * r4 + 4 * half;
         const float4 lv = *reinterpret_cast<const float4*>(&Ls[buf][q0]);
         const float4 dv4 = *reinterpret_cast<const float4*>(&Dl[buf][q0]);
         const float lq[4] = {lv.x, lv.y, lv.z, lv.w}, dq4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-        float p[4], ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          p[e] = q0 + e < valid ? __builtin_amdgcn_exp2f(s[r] * c2 - lq[e]) : 0.0f;
-          ds[e] = p[e] * (dp[r] - dq4[e]);
+        for (int t = 0; t < 2; ++t) {
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            p[e] = q0 + e < valid ? __builtin_amdgcn_exp2f(s[t][r] * c2 - lq[e]) : 0.0f;
+            ds[e] = p[e] * (dp[t][r] - dq4[e]);
+          }
+          uint4 wp = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
+          uint4 ws = __builtin_bit_cast(uint4, sb[t][r4 >> 1]);
+          if (r4 & 1) {
+            wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
+            ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
+          } else {
+            wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
+            ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
+          }
+          pb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, wp);
+          sb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, ws);
         }
-        uint4 wp = __builtin_bit_cast(uint4, pb[r4 >> 1]);
-        uint4 ws = __builtin_bit_cast(uint4, sb[r4 >> 1]);
-        if (r4 & 1) {
-          wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
-          ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
-        } else {
-          wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
-          ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
+      }
+      asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(sb[0][0]),
+                   "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x4 olo = lds_read_tr(O + 16 * G * D + trd[dt][0]);
+          const bf16x4 ohi = lds_read_tr(O + 16 * G * D + trd[dt][1]);
+          const bf16x8 oa = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
+          const bf16x4 qlo = lds_read_tr(Q + 16 * G * D + trd[dt][0]);
+          const bf16x4 qhi = lds_read_tr(Q + 16 * G * D + trd[dt][1]);
+          const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            mma_a(dv[dt][t], oa, pb[t][G]);  // dV^T += dO^T P
+            mma_a(dk[dt][t], qa, sb[t][G]);  // dK^T += Q^T dS
+          }
         }
-        pb[r4 >> 1] = __builtin_bit_cast(bf16x8, wp);
-        sb[r4 >> 1] = __builtin_bit_cast(bf16x8, ws);
-      }
-#pragma unroll
-    for (int G = 0; G < 2; ++G)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const __bf16* X = PASS == 0 ? O : Q;  // dV^T += dO^T P ; dK^T += Q^T dS
-        const bf16x4 lo = lds_read_tr(X + 16 * G * D + trd[dt][0]);
-        const bf16x4 hi = lds_read_tr(X + 16 * G * D + trd[dt][1]);
-        const bf16x8 xa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dt] = mfma32x32x16(xa, PASS == 0 ? pb[G] : sb[G], acc[dt]);
-      }
     }
-    if (j + 1 < nst) put_stats(buf ^ 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // stage j + 1 landed (stage j + 2's row copies may be outstanding); every wave is
+    // done with buffer j before stage j + 3 is copied into it
+    if (j + 2 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if (kok) {
-    float* dst = PASS == 0 ? (text ? a.dtv : a.dv) : (text ? a.dtk : a.dk);
-    dst += (size_t)ktok * rs + h * D;
-    const float f = PASS == 0 ? 1.0f : a.scale;
+  // the last MFMAs' results, before the vector unit reads them
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dv[dt][0]), "+a"(dv[dt][1]), "+a"(dk[dt][0]), "+a"(dk[dt][1]));
+  // lane holds channels 32 dt + 8 i + 4 half + e of keys ktok[t]
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (!kok[t]) continue;
+    float* pk = (text ? a.dtk : a.dk) + (size_t)ktok[t] * rs + h * D;
+    float* pv = (text ? a.dtv : a.dv) + (size_t)ktok[t] * rs + h * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * i + 4 * half) =
-            make_float4(f * acc[dt][4 * i], f * acc[dt][4 * i + 1], f * acc[dt][4 * i + 2], f * acc[dt][4 * i + 3]);
+      for (int i = 0; i < 4; ++i) {
+        const int c = 32 * dt + 8 * i + 4 * half;
+        *reinterpret_cast<float4*>(pk + c) = make_float4(a.scale * dk[dt][t][4 * i], a.scale * dk[dt][t][4 * i + 1],
+                                                         a.scale * dk[dt][t][4 * i + 2], a.scale * dk[dt][t][4 * i + 3]);
+        *reinterpret_cast<float4*>(pv + c) =
+            make_float4(dv[dt][t][4 * i], dv[dt][t][4 * i + 1], dv[dt][t][4 * i + 2], dv[dt][t][4 * i + 3]);
+      }
   }
 }
 
@@ -678,14 +732,9 @@ hipError_t launch_softmax_bwd(const SoftmaxBwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int per_head = (g.L + 255) / 256 + g.F * ((g.T + 255) / 256);
-  dim3 grid2(per_head * g.H), block2(512);
-  if (g.d == 128) {
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<128, 0>), grid2, block2, 0, stream, a);
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<128, 1>), grid2, block2, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<64, 0>), grid2, block2, 0, stream, a);
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_bwd_dkdv_kernel<64, 1>), grid2, block2, 0, stream, a);
-  }
+  dim3 grid2(per_head * g.H), block2(256);
+  if (g.d == 128) hipLaunchKernelGGL(softmax_bwd_kv_kernel<128>, grid2, block2, 0, stream, a);
+  else hipLaunchKernelGGL(softmax_bwd_kv_kernel<64>, grid2, block2, 0, stream, a);
   return hipGetLastError();
 }
 
