@@ -28,10 +28,10 @@ import tempfile
 VALU_TO_MFMA = 2
 MFMA_TO_VALU_READ = 12
 MFMA_SRCC_TO_VALU_WRITE = 11
-# (source file under csrc/, mangled-name prefix of the kernels written with asm MFMAs)
-TARGETS = (("softmax_bf16.hip", "_ZN3vdn17softmax_sw_kernel"),
-           ("backward.hip", "_ZN3vdn21softmax_bwd_kv_kernel"))
-PREFIXES = tuple(p for _, p in TARGETS)
+# (source file under csrc/, mangled-name prefixes of its kernels written with asm MFMAs)
+TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel",)),
+           ("backward.hip", ("_ZN3vdn21softmax_bwd_kv_kernel",)))
+PREFIXES = tuple(p for _, ps in TARGETS for p in ps)
 
 _REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
 _STORE = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store", "flat_store")
@@ -207,8 +207,8 @@ def check(src: str | None = None) -> list[str]:
         return check_asm(kernel_asm(src))
     from .build import CSRC
     problems = []
-    for name, prefix in TARGETS:
-        problems += check_asm(kernel_asm(os.path.join(CSRC, name)), (prefix,))
+    for name, prefixes in TARGETS:
+        problems += check_asm(kernel_asm(os.path.join(CSRC, name)), prefixes)
     return problems
 
 

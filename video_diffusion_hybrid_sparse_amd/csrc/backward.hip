@@ -15,6 +15,8 @@
 //      sum q^T du; each chunk's frame-state gradient is the sum of the group gradients of
 //      the chunks whose window excludes it, the text state's the sum of all of them;
 //      dk += v dS^T, dv += k dS per token.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace vdn {
@@ -423,13 +425,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // One workgroup = 256 keys of one frame (or of the text) and one head, 4 waves x 64 keys
 // (one wave per SIMD).  The wave keeps its keys' K and V rows in registers (MFMA B
 // operands, key lane-local) and its dK^T and dV^T accumulators (64 keys x D each) in the
-// matrix registers.  Queries stream through LDS in 64-query stages, three buffers deep,
+// matrix registers.  Queries stream through LDS in 64-query stages (double-buffered),
 // with their log-sum-exp and Delta; each stage runs as two 32-query halves.  Per half:
 // S = Q K^T and dP = dO V^T (Q and dO rows from LDS are the A operands, each feeding both
 // 32-key sub-tiles); P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and
 // dK^T += Q^T dS (dO^T and Q^T by the transposing LDS read, each feeding both sub-tiles).
 // Per (query, key) pair 8 d multiply-adds against 10 d for separate dV and dK passes,
-// and every LDS operand read feeds two MFMAs.
+// and every LDS operand read feeds two MFMAs.  The stage loop is unrolled over the two
+// buffers and the halves, so every LDS read is one per-lane base register plus an
+// immediate offset; queries past a ragged stage's end get log-sum-exp +inf (P = 0).
 // The kernel's MFMAs are inline asm so that the register classes are fixed: scores in
 // VGPRs (the vector unit reads them), dK^T and dV^T in AGPRs.  The compiler's hazard
 // recognizer does not see them, so the kernel places the wait states itself: 2 between
@@ -451,13 +455,15 @@ __device__ __forceinline__ void mma_a(f32x16& d, const bf16x8& a, const bf16x8& 
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_bwd_kv_kernel(SoftmaxBwdArgs a) {
-  constexpr int NW = 4, BK = 256, BQ = 64, NBUF = 3;
+  constexpr int NW = 4, BK = 256, BQ = 64;
   constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
   constexpr int NI = BQ * CPR / (64 * NW);  // 16-byte copies per lane per stage and tensor
+  constexpr int TB = BQ * D * 2;            // bytes of one tensor's stage
   static_assert(NI >= 1, "stage size");
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[NBUF][BQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Os[NBUF][BQ * D];
-  __shared__ __attribute__((aligned(16))) float Ls[NBUF][BQ], Dl[NBUF][BQ];
+  static_assert(3 * TB + 32 * D * 2 + 16 * D * 2 < 65536, "LDS offsets must fit the 16-bit immediate");
+  // [buffer][Q, dO][query][channel] and [buffer][lse, Delta][query]
+  __shared__ __attribute__((aligned(16))) __bf16 QO[2][2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float ST[2][2][BQ];
   const Geo g = a.geo;
   // key tiles of one head: anchor 0's tiles, anchor F-1's tiles, text tiles, then frames
   // 1 .. F-2 (the anchors' and the text's tiles see every query: largest first);
@@ -479,8 +485,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int end = text ? g.L : (kframe + 1) * g.T;
     kvalid = end - kstart;
   }
-  const KeySegs qs = group_keys(g, (text || kframe == 0 || kframe == g.F - 1) ? 0 : 2 + kframe / g.C);
-  const int n1 = (qs.l0 + BQ - 1) / BQ, n2 = (qs.l1 + BQ - 1) / BQ, n3 = (qs.l2 + BQ - 1) / BQ;
+  // the query segments as plain wave-uniform values (kept out of memory: selecting among
+  // struct fields otherwise becomes an indexed private-memory load, whose wait would also
+  // wait for the stage copies in flight)
+  int s0, l0, s1, l1, s2, l2;
+  {
+    const KeySegs qs = group_keys(g, (text || kframe == 0 || kframe == g.F - 1) ? 0 : 2 + kframe / g.C);
+    s0 = __builtin_amdgcn_readfirstlane(qs.s0);
+    l0 = __builtin_amdgcn_readfirstlane(qs.l0);
+    s1 = __builtin_amdgcn_readfirstlane(qs.s1);
+    l1 = __builtin_amdgcn_readfirstlane(qs.l1);
+    s2 = __builtin_amdgcn_readfirstlane(qs.s2);
+    l2 = __builtin_amdgcn_readfirstlane(qs.l2);
+  }
+  const int n1 = (l0 + BQ - 1) / BQ, n2 = (l1 + BQ - 1) / BQ, n3 = (l2 + BQ - 1) / BQ;
   const int nst = n1 + n2 + n3;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -489,71 +507,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // the wave's keys: 64 w + 32 t + l32 of the tile (t = 0, 1), clamped to the tile
   const __bf16* kbase = text ? a.tk : a.k;
   const __bf16* vbase = text ? a.tv : a.v;
+  // key t of the lane (0, 1): 64 w + 32 t + l32 of the tile, clamped to the tile
+  auto key_tok = [&](int t) __attribute__((always_inline)) {
+    return kstart + imin(wave * 64 + t * 32 + l32, kvalid - 1);
+  };
   bf16x8 kreg[2][KS], vreg[2][KS];
-  int ktok[2];
-  bool kok[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int kr = wave * 64 + t * 32 + l32;
-    kok[t] = kr < kvalid;
-    ktok[t] = kstart + imin(kr, kvalid - 1);
+    const size_t o = (size_t)key_tok(t) * rs + h * D + half * 8;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      kreg[t][s2] = load_bf16x8(kbase + (size_t)ktok[t] * rs + h * D + half * 8 + 16 * s2);
-      vreg[t][s2] = load_bf16x8(vbase + (size_t)ktok[t] * rs + h * D + half * 8 + 16 * s2);
+      kreg[t][s2] = load_bf16x8(kbase + o + 16 * s2);
+      vreg[t][s2] = load_bf16x8(vbase + o + 16 * s2);
     }
   }
 
   // stage copies (dma16/dma4, waited for explicitly): SGPR base per stage, per-lane offsets
   const uint32_t rs2 = (uint32_t)rs * 2;
-  int lrow[NI];
-  uint32_t loff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    loff[i] = (uint32_t)((lane % CPR) ^ swz<CPR>(lrow[i])) * 16;
-  }
-  const uint32_t m0q = lds_addr(&Qs[0][0], wave * NI * RPI * D * 2);
-  const uint32_t m0o = lds_addr(&Os[0][0], wave * NI * RPI * D * 2);
-  const uint32_t m0s = lds_addr(wave == 0 ? &Ls[0][0] : &Dl[0][0], 0);
+  const uint32_t m0q = lds_addr(&QO[0][0][0], wave * NI * RPI * D * 2);
+  const uint32_t m0s = lds_addr(&ST[0][0][0], (wave & 1) * BQ * 4);
+  // stage j's first query and valid count.  Written with selects between a computed
+  // value and 0: a select between two captured values becomes a load through a selected
+  // pointer, which keeps the captures in private memory (and its wait, on the vector
+  // memory counter, would also wait for the stage copies in flight).
+  const int ds01 = s0 - s1, ds12 = s1 - s2, dl01 = l0 - l1, dl12 = l1 - l2;
   auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
-    int len, base;
-    if (j < n1) { base = qs.s0; len = qs.l0; }
-    else if ((j -= n1) < n2) { base = qs.s1; len = qs.l1; }
-    else { j -= n2; base = qs.s2; len = qs.l2; }
-    start = base + BQ * j;
-    valid = len - BQ * j;
+    const bool in1 = j < n1, in2 = j < n1 + n2;
+    const int base = s2 + (in2 ? ds12 : 0) + (in1 ? ds01 : 0);
+    const int len = l2 + (in2 ? dl12 : 0) + (in1 ? dl01 : 0);
+    const int jj = j - (in1 ? 0 : n1) - (in2 ? 0 : n2);
+    start = base + BQ * jj;
+    valid = len - BQ * jj;
   };
-  // stage j into buffer buf: waves 0 and 1 first copy the 64 log-sum-exps / Deltas (one
-  // dword per lane), then every wave its share of the Q and dO rows (2 NI copies)
+  // stage j into buffer buf: waves 0 and 1 copy the 64 log-sum-exps / Deltas (one dword
+  // per lane), every wave its share of the Q and dO rows
+  const float* stat_src = wave == 0 ? a.lse : a.delta;
   auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     int start, valid;
     stage_at(j, start, valid);
     if (wave < 2) {
-      const float* sb = (wave == 0 ? a.lse : a.delta) + (size_t)start * g.H + h;
-      dma4(sb, (uint32_t)imin(lane, valid - 1) * (uint32_t)g.H * 4, m0s + (uint32_t)buf * (BQ * 4));
+      const float* sb = stat_src + (size_t)start * g.H + h;
+      dma4(sb, (uint32_t)imin(lane, valid - 1) * (uint32_t)g.H * 4, m0s + (uint32_t)buf * (2 * BQ * 4));
     }
     const size_t base = (size_t)start * rs + h * D;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint32_t off = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
-      dma16(a.q + base, off, m0q + (uint32_t)buf * (BQ * D * 2) + i * RPI * D * 2);
-      dma16(a.dO + base, off, m0o + (uint32_t)buf * (BQ * D * 2) + i * RPI * D * 2);
+      const int lrow = (wave * NI + i) * RPI + lane / CPR;
+      const uint32_t off = (uint32_t)imin(lrow, valid - 1) * rs2 + (uint32_t)((lane % CPR) ^ swz<CPR>(lrow)) * 16;
+      dma16(a.q + base, off, m0q + (uint32_t)buf * (2 * TB) + i * RPI * D * 2);
+      dma16(a.dO + base, off, m0q + (uint32_t)buf * (2 * TB) + TB + i * RPI * D * 2);
     }
   };
-  int qrd[KS];
-#pragma unroll
-  for (int k = 0; k < KS; ++k) qrd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
+  // per-lane LDS read addresses (buffer 0, Q, half 0), opaque to the compiler so that the
+  // buffer, tensor, half and k-group terms become the reads' immediate offsets:
+  //  rad[k]: row read of query l32, channels 16 k + 8 half .. +7 (A operand of S, dP);
+  //  tad[dt][c]: transposing read, 16-lane group grp16 covers queries 4 (grp16 >> 1) + 8 c
+  //  .. +3 and channels 32 dt + 16 (grp16 & 1) + 4 (i16 & 3) .. +3 (A operand of dV^T, dK^T);
+  //  sad: the statistics of queries 4 half .. 4 half + 3
+  using lds_b64 = __attribute__((address_space(3))) i16x4;
+  using lds_b128 = __attribute__((address_space(3))) const bf16x8;
+  using lds_f4 = __attribute__((address_space(3))) const f32x4;
+  const uint32_t qo0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&QO[0][0][0];
+  uint32_t rad[KS], tad[DT][2], sad;
   const int grp16 = lane >> 4, i16 = lane & 15;
-  int trd[DT][2];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    rad[k] = qo0 + 2 * (l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8));
+    asm volatile("" : "+v"(rad[k]));
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
       const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
-      trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
+      tad[dt][c] = qo0 + 2 * (row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7));
+      asm volatile("" : "+v"(tad[dt][c]));
     }
+  sad = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&ST[0][0][0] + 16 * half;
+  asm volatile("" : "+v"(sad));
 
   f32x16 dv[DT][2], dk[DT][2];
 #pragma unroll
@@ -570,105 +602,119 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     asm volatile("s_nop 1" : "+a"(dv[dt][0]), "+a"(dv[dt][1]), "+a"(dk[dt][0]), "+a"(dk[dt][1]));
   const float c2 = a.c2;
 
-  if (nst > 0) issue(0, 0);
-  if (nst > 1) issue(1, 1);
-  // stage 0 landed: at most the 2 NI row copies of stage 1 (issued after its dword copy)
-  // may still be outstanding
-  if (nst > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int j = 0; j < nst; ++j) {
-    const int buf = j % NBUF;
-    if (j + 2 < nst) issue(j + 2, (j + 2) % NBUF);
+  // one 32-query half RT of the stage in buffer BUF (`valid` queries in the stage)
+  auto half_body = [&](auto bufc, auto rtc, int valid) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value, RT = decltype(rtc)::value;
+    constexpr uint32_t QOFF = BUF * 2 * TB + RT * 32 * D * 2, OOFF = QOFF + TB;
+    constexpr uint32_t LOFF = BUF * 2 * BQ * 4 + RT * 32 * 4, DOFF = LOFF + BQ * 4;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const bf16x8 qa = *(lds_b128*)(uintptr_t)(rad[k] + QOFF);
+      const bf16x8 oa = *(lds_b128*)(uintptr_t)(rad[k] + OOFF);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (k == 0) {
+          mma_first(s[t], qa, kreg[t][k]);
+          mma_first(dp[t], oa, vreg[t][k]);
+        } else {
+          mma_v(s[t], qa, kreg[t][k]);
+          mma_v(dp[t], oa, vreg[t][k]);
+        }
+      }
+    }
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(dp[0]), "+v"(dp[1]));
+    // accumulator row r = query 32 RT + 8 (r/4) + 4 half + r%4 of the stage, column = key
+    bf16x8 pb[2][2], sb[2][2];
+    const bool ragged = valid < 32 * (RT + 1);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 lv = *(lds_f4*)(uintptr_t)(sad + LOFF + 32 * r4);
+      const f32x4 dv4 = *(lds_f4*)(uintptr_t)(sad + DOFF + 32 * r4);
+      if (__builtin_expect(ragged, 0)) {
+        // queries past the stage's end: P = exp2(-inf) = 0, dS = 0
+        const int q0 = RT * 32 + 8 * r4 + 4 * half;
+        const float inf = __builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lv[e] = q0 + e < valid ? lv[e] : inf;
+      }
+      const float lq[4] = {lv[0], lv[1], lv[2], lv[3]}, dq4[4] = {dv4[0], dv4[1], dv4[2], dv4[3]};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          p[e] = __builtin_amdgcn_exp2f(s[t][r] * c2 - lq[e]);
+          ds[e] = p[e] * (dp[t][r] - dq4[e]);
+        }
+        uint4 wp = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
+        uint4 ws = __builtin_bit_cast(uint4, sb[t][r4 >> 1]);
+        if (r4 & 1) {
+          wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
+          ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
+        } else {
+          wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
+          ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
+        }
+        pb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, wp);
+        sb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, ws);
+      }
+    }
+    asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(sb[0][0]),
+                 "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t go = 16 * G * D * 2;
+        const bf16x4 olo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                          (lds_b64*)(uintptr_t)(tad[dt][0] + OOFF + go)));
+        const bf16x4 ohi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                          (lds_b64*)(uintptr_t)(tad[dt][1] + OOFF + go)));
+        const bf16x8 oa = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
+        const bf16x4 qlo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                          (lds_b64*)(uintptr_t)(tad[dt][0] + QOFF + go)));
+        const bf16x4 qhi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                          (lds_b64*)(uintptr_t)(tad[dt][1] + QOFF + go)));
+        const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          mma_a(dv[dt][t], oa, pb[t][G]);  // dV^T += dO^T P
+          mma_a(dk[dt][t], qa, sb[t][G]);  // dK^T += Q^T dS
+        }
+      }
+  };
+  // stage j in buffer BUF: copy stage j + 1 into the other buffer (free since the last
+  // barrier), run the halves, wait for the copy, barrier
+  auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (j + 1 < nst) issue(j + 1, BUF ^ 1);
     int start, valid;
     stage_at(j, start, valid);
-#pragma unroll 1
-    for (int rt = 0; rt < 2; ++rt) {  // 32-query halves of the stage
-      if (rt * 32 >= valid) break;
-      const __bf16* Q = Qs[buf] + 32 * rt * D;
-      const __bf16* O = Os[buf] + 32 * rt * D;
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Q + qrd[k]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(O + qrd[k]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          if (k == 0) {
-            mma_first(s[t], qa, kreg[t][k]);
-            mma_first(dp[t], oa, vreg[t][k]);
-          } else {
-            mma_v(s[t], qa, kreg[t][k]);
-            mma_v(dp[t], oa, vreg[t][k]);
-          }
-        }
-      }
-      asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(dp[0]), "+v"(dp[1]));
-      // accumulator row r = query 32 rt + 8 (r/4) + 4 half + r%4 of the stage, column = key
-      bf16x8 pb[2][2], sb[2][2];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int q0 = rt * 32 + 8 * r4 + 4 * half;
-        const float4 lv = *reinterpret_cast<const float4*>(&Ls[buf][q0]);
-        const float4 dv4 = *reinterpret_cast<const float4*>(&Dl[buf][q0]);
-        const float lq[4] = {lv.x, lv.y, lv.z, lv.w}, dq4[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float p[4], ds[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            p[e] = q0 + e < valid ? __builtin_amdgcn_exp2f(s[t][r] * c2 - lq[e]) : 0.0f;
-            ds[e] = p[e] * (dp[t][r] - dq4[e]);
-          }
-          uint4 wp = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
-          uint4 ws = __builtin_bit_cast(uint4, sb[t][r4 >> 1]);
-          if (r4 & 1) {
-            wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
-            ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
-          } else {
-            wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
-            ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
-          }
-          pb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, wp);
-          sb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, ws);
-        }
-      }
-      asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(sb[0][0]),
-                   "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x4 olo = lds_read_tr(O + 16 * G * D + trd[dt][0]);
-          const bf16x4 ohi = lds_read_tr(O + 16 * G * D + trd[dt][1]);
-          const bf16x8 oa = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
-          const bf16x4 qlo = lds_read_tr(Q + 16 * G * D + trd[dt][0]);
-          const bf16x4 qhi = lds_read_tr(Q + 16 * G * D + trd[dt][1]);
-          const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            mma_a(dv[dt][t], oa, pb[t][G]);  // dV^T += dO^T P
-            mma_a(dk[dt][t], qa, sb[t][G]);  // dK^T += Q^T dS
-          }
-        }
-    }
-    // stage j + 1 landed (stage j + 2's row copies may be outstanding); every wave is
-    // done with buffer j before stage j + 3 is copied into it
-    if (j + 2 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    half_body(bufc, std::integral_constant<int, 0>{}, valid);
+    if (valid > 32) half_body(bufc, std::integral_constant<int, 1>{}, valid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  if (nst > 0) issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nst; j += 2) {
+    stage(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nst) stage(j + 1, std::integral_constant<int, 1>{});
   }
   // the last MFMAs' results, before the vector unit reads them
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
     asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dv[dt][0]), "+a"(dv[dt][1]), "+a"(dk[dt][0]), "+a"(dk[dt][1]));
-  // lane holds channels 32 dt + 8 i + 4 half + e of keys ktok[t]
+  // lane holds channels 32 dt + 8 i + 4 half + e of key t
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    if (!kok[t]) continue;
-    float* pk = (text ? a.dtk : a.dk) + (size_t)ktok[t] * rs + h * D;
-    float* pv = (text ? a.dtv : a.dv) + (size_t)ktok[t] * rs + h * D;
+    if (wave * 64 + t * 32 + l32 >= kvalid) continue;
+    float* pk = (text ? a.dtk : a.dk) + (size_t)key_tok(t) * rs + h * D;
+    float* pv = (text ? a.dtv : a.dv) + (size_t)key_tok(t) * rs + h * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
