@@ -258,18 +258,22 @@ __global__ __launch_bounds__(256) void token_state_kernel(TokenStateArgs<X> a) {
 }
 
 // ---- 3a. softmax backward, dQ -----------------------------------------------------------
-// Query tiles as in the forward (256 queries of one group and head, 8 waves x 32).  Per
-// 64-key sub-tile: S^T = K Q^T and dP^T = V dO^T (K and V rows are MFMA A operands);
-// P^T = exp2(S^T c2 - lse), dS^T = P^T (dP^T - Delta) (the query is lane-local);
-// dQ^T += K^T dS^T with K^T gathered by the transposing LDS read.  dq = scale dQ.
+// Query tiles as in the forward (256 queries of one group and head, 8 waves x 32, two
+// waves per SIMD).  Per 64-key stage (K and V rows double-buffered in LDS): S^T = K Q^T
+// and dP^T = V dO^T (K and V rows are MFMA A operands); P^T = exp2(S^T c2 - lse),
+// dS^T = P^T (dP^T - Delta) (the query is lane-local); dQ^T += K^T dS^T with K^T gathered
+// by the transposing LDS read.  dq = scale dQ.  The stage loop is unrolled over the two
+// buffers, so every LDS read is a per-lane base plus an immediate offset; keys past a
+// ragged stage's end get score -inf (P = 0).
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void softmax_bwd_dq_kernel(SoftmaxBwdArgs a) {
   constexpr int BM = 256, NW = 8, BN = 64;
   constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
   constexpr int NI = BN * CPR / (64 * NW);
+  constexpr int TB = BN * D * 2;  // bytes of one tensor's stage
   static_assert(NI >= 1, "stage size");
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * D];
+  static_assert(3 * TB + 48 * D * 2 < 65536, "LDS offsets must fit the 16-bit immediate");
+  __shared__ __attribute__((aligned(16))) __bf16 KV[2][2][BN * D];  // [buffer][K, V][key][channel]
   const Geo g = a.geo;
   const int per_head = count_tiles(g, BM);
   const int total = per_head * g.H;
@@ -278,10 +282,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int h = lid / per_head;
   int grp, t0, t1;
   if (!locate_tile(g, lid - h * per_head, BM, grp, t0, t1)) return;
-  const KeySegs sg = group_keys(g, grp);
-  const int n0 = (g.L + BN - 1) / BN, n1 = (sg.l0 + BN - 1) / BN, n2 = (sg.l1 + BN - 1) / BN, n3 = (sg.l2 + BN - 1) / BN;
+  // key segments (text first) as plain wave-uniform values
+  int s0, l0, s1, l1, s2, l2;
+  {
+    const KeySegs sg = group_keys(g, grp);
+    s0 = __builtin_amdgcn_readfirstlane(sg.s0);
+    l0 = __builtin_amdgcn_readfirstlane(sg.l0);
+    s1 = __builtin_amdgcn_readfirstlane(sg.s1);
+    l1 = __builtin_amdgcn_readfirstlane(sg.l1);
+    s2 = __builtin_amdgcn_readfirstlane(sg.s2);
+    l2 = __builtin_amdgcn_readfirstlane(sg.l2);
+  }
+  const int n0 = (g.L + BN - 1) / BN, n1 = (l0 + BN - 1) / BN, n2 = (l1 + BN - 1) / BN, n3 = (l2 + BN - 1) / BN;
   const int nst = n0 + n1 + n2 + n3;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t rs = (size_t)g.H * D;
 
   int qtok = t0 + wave * 32 + l32;
@@ -301,26 +316,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const float delta = a.delta[(size_t)qtok * g.H + h];
   __builtin_amdgcn_s_waitcnt(0);
 
-  // stage copies (dma16, not tracked by the compiler's waits): an SGPR base per stage and
-  // per-lane 32-bit offsets (row inside the stage, clamped to the segment; swizzled chunk)
+  // stage copies (dma16, waited for explicitly): SGPR base per stage, per-lane offsets.
+  // Stage j's first key and valid count, written with selects between a computed value
+  // and 0 (a select between two captured values becomes a load through a selected
+  // pointer, which keeps the captures in private memory).
   const uint32_t rs2 = (uint32_t)rs * 2;
-  int lrow[NI];
-  uint32_t loff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    lrow[i] = (wave * NI + i) * RPI + lane / CPR;
-    loff[i] = (uint32_t)((lane % CPR) ^ swz<CPR>(lrow[i])) * 16;
-  }
-  const uint32_t m0k = lds_addr(&Ks[0][0], wave * NI * RPI * D * 2);
-  const uint32_t m0v = lds_addr(&Vs[0][0], wave * NI * RPI * D * 2);
+  const uint32_t m0kv = lds_addr(&KV[0][0][0], wave * NI * RPI * D * 2);
+  const int e1 = n0 + n1, e2 = n0 + n1 + n2;
+  const int ds1 = s0 - s1, ds2 = s1 - s2, dl0 = g.L - l0, dl1 = l0 - l1, dl2 = l1 - l2;
   auto stage_at = [&](int j, int& start, int& valid) __attribute__((always_inline)) {
-    int len, base;
-    if (j < n0) { base = 0; len = g.L; }
-    else if ((j -= n0) < n1) { base = sg.s0; len = sg.l0; }
-    else if ((j -= n1) < n2) { base = sg.s1; len = sg.l1; }
-    else { j -= n2; base = sg.s2; len = sg.l2; }
-    start = base + BN * j;
-    valid = len - BN * j;
+    const bool in0 = j < n0, in1 = j < e1, in2 = j < e2;
+    // text: base 0; segments 0, 1, 2: s0, s1, s2
+    const int base = in0 ? 0 : s2 + (in2 ? ds2 : 0) + (in1 ? ds1 : 0);
+    const int len = l2 + (in2 ? dl2 : 0) + (in1 ? dl1 : 0) + (in0 ? dl0 : 0);
+    const int jj = j - (in0 ? 0 : n0) - (in1 ? 0 : n1) - (in2 ? 0 : n2);
+    start = base + BN * jj;
+    valid = len - BN * jj;
   };
   auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     int start, valid;
@@ -331,23 +342,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const __bf16* vb = (text ? a.tv : a.v) + base;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint32_t off = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
-      dma16(kb, off, m0k + (uint32_t)buf * (BN * D * 2) + i * RPI * D * 2);
-      dma16(vb, off, m0v + (uint32_t)buf * (BN * D * 2) + i * RPI * D * 2);
+      const int lrow = (wave * NI + i) * RPI + lane / CPR;
+      const uint32_t off = (uint32_t)imin(lrow, valid - 1) * rs2 + (uint32_t)((lane % CPR) ^ swz<CPR>(lrow)) * 16;
+      dma16(kb, off, m0kv + (uint32_t)buf * (2 * TB) + i * RPI * D * 2);
+      dma16(vb, off, m0kv + (uint32_t)buf * (2 * TB) + TB + i * RPI * D * 2);
     }
   };
-  int krd[KS];
-#pragma unroll
-  for (int k = 0; k < KS; ++k) krd[k] = l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8);
+  // per-lane LDS read addresses (buffer 0, K, key tile 0), opaque to the compiler so that
+  // the buffer, tensor, tile and key-group terms become immediate offsets:
+  //  kad[k]: row read of key l32, channels 16 k + 8 half .. +7 (A operand of S^T, dP^T);
+  //  tad[dt][c]: transposing read of K, keys 4 (grp16 >> 1) + 8 c .. +3, channels
+  //  32 dt + 16 (grp16 & 1) + 4 (i16 & 3) .. +3 (A operand of dQ^T)
+  using lds_b64 = __attribute__((address_space(3))) i16x4;
+  using lds_b128 = __attribute__((address_space(3))) const bf16x8;
+  const uint32_t kv0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&KV[0][0][0];
+  uint32_t kad[KS], tad[DT][2];
   const int grp16 = lane >> 4, i16 = lane & 15;
-  int trd[DT][2];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    kad[k] = kv0 + 2 * (l32 * D + (((2 * k + half) ^ swz<CPR>(l32)) * 8));
+    asm volatile("" : "+v"(kad[k]));
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
       const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
-      trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
+      tad[dt][c] = kv0 + 2 * (row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7));
+      asm volatile("" : "+v"(tad[dt][c]));
     }
 
   f32x16 dq[DT];
@@ -355,16 +378,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   for (int i = 0; i < DT; ++i) dq[i] = 0.0f;
   const float c2 = a.c2;
 
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int j = 0; j < nst; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nst) issue(j + 1, buf ^ 1);
+  auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr uint32_t KOFF = BUF * 2 * TB, VOFF = KOFF + TB;
+    if (j + 1 < nst) issue(j + 1, BUF ^ 1);
     int start, valid;
     stage_at(j, start, valid);
-    const __bf16* K = Ks[buf];
-    const __bf16* V = Vs[buf];
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -375,9 +394,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int k = 0; k < KS; ++k)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        s[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K + 32 * rt * D + krd[k]), qreg[k], s[rt]);
-        dp[rt] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(V + 32 * rt * D + krd[k]), doreg[k], dp[rt]);
+        s[rt] = mfma32x32x16(*(lds_b128*)(uintptr_t)(kad[k] + KOFF + rt * 32 * D * 2), qreg[k], s[rt]);
+        dp[rt] = mfma32x32x16(*(lds_b128*)(uintptr_t)(kad[k] + VOFF + rt * 32 * D * 2), doreg[k], dp[rt]);
       }
+    if (__builtin_expect(valid < BN, 0)) {
+      // keys past the stage's end: score -inf, P = 0
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          s[rt][r] = key < valid ? s[rt][r] : -__builtin_inff();
+        }
+    }
     bf16x8 pb[4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -386,8 +415,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         float ds2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int key = rt * 32 + 8 * ((r + e) >> 2) + 4 * half + ((r + e) & 3);
-          const float p = key < valid ? __builtin_amdgcn_exp2f(s[rt][r + e] * c2 - lse) : 0.0f;
+          const float p = __builtin_amdgcn_exp2f(s[rt][r + e] * c2 - lse);
           ds2[e] = p * (dp[rt][r + e] - delta);
         }
         uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
@@ -400,13 +428,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     for (int G = 0; G < 4; ++G)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 lo = lds_read_tr(K + 16 * G * D + trd[dt][0]);
-        const bf16x4 hi = lds_read_tr(K + 16 * G * D + trd[dt][1]);
+        const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                         (lds_b64*)(uintptr_t)(tad[dt][0] + KOFF + 16 * G * D * 2)));
+        const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                         (lds_b64*)(uintptr_t)(tad[dt][1] + KOFF + 16 * G * D * 2)));
         const bf16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dq[dt] = mfma32x32x16(ka, pb[G], dq[dt]);
       }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  if (nst > 0) issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = 0; j < nst; j += 2) {
+    stage(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nst) stage(j + 1, std::integral_constant<int, 1>{});
   }
   if (qok) {
     float* out = a.dq + (size_t)qtok * rs + h * D;
