@@ -36,65 +36,89 @@ __device__ __forceinline__ float sig(float x) { return 1.0f / (1.0f + __expf(-x)
 }  // namespace
 
 // ---- 2. epilogue backward -----------------------------------------------------------
-// One workgroup = 64 tokens of one head; 8 groups of 32 lanes, one token at a time per
-// group, D/32 channels per lane.
+// One workgroup = 64 tokens of one head; 8 groups of 32 lanes, two tokens at a time per
+// group (their loads in flight together), D/32 = 4 consecutive channels per lane moved
+// as 16-byte (float) and 8-byte (bf16) accesses.
 template <int D>
 __global__ __launch_bounds__(256) void epi_bwd_kernel(EpiBwdArgs a) {
-  constexpr int CPL = D / 32;
+  constexpr int CPL = D / 32, TPI = 2;
+  static_assert(CPL == 4 || CPL == 2, "channels per lane");
+  using FV = float __attribute__((ext_vector_type(CPL)));
+  using BV = __bf16 __attribute__((ext_vector_type(CPL)));
   __shared__ float red[8][D];
   const Geo g = a.geo;
   const int h = blockIdx.y, blk = blockIdx.x;
   const int tid = threadIdx.x, grp = tid >> 5, l = tid & 31;
   const int N = g.F * g.T;
   const size_t rs = (size_t)g.H * D, hd = rs;
-  float w[CPL], dwp[CPL];
+  const FV w = *reinterpret_cast<const FV*>(a.w + h * D + l * CPL);
+  FV dwp = 0.0f;
+  const int tend = imin(N, blk * 64 + 64);
+  for (int t0 = blk * 64 + grp; t0 < tend; t0 += 8 * TPI) {
+    FV O[TPI], U[TPI], DS[TPI], DL[TPI];
+    BV GS[TPI], GL[TPI];
+    bool ok[TPI];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    w[e] = a.w[h * D + l * CPL + e];
-    dwp[e] = 0.0f;
-  }
-  for (int t = blk * 64 + grp; t < imin(N, blk * 64 + 64); t += 8) {
-    const size_t o = (size_t)t * rs + h * D + l * CPL;
-    const float* das = a.dacat + (size_t)t * 2 * hd + h * D + l * CPL;
-    const float* dal = das + hd;
-    float dO[CPL], O[CPL], rh[CPL], dr[CPL], gl[CPL];
-    float delta = 0.0f, uu = 0.0f;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const float gs = (float)a.gs[o + e], ss = sig(gs);
-      O[e] = a.o[o + e];
-      dO[e] = das[e] * ss;
-      a.dgs[o + e] = das[e] * O[e] * ss * (1.0f - ss);
-      delta += dO[e] * O[e];
-      rh[e] = a.u[o + e];
-      uu += rh[e] * rh[e];
-      gl[e] = (float)a.gl[o + e];
+    for (int i = 0; i < TPI; ++i) {
+      const int t = t0 + 8 * i;
+      ok[i] = t < tend;
+      const int tt = ok[i] ? t : t0;
+      const size_t o = (size_t)tt * rs + h * D + l * CPL;
+      const size_t c = (size_t)tt * 2 * hd + h * D + l * CPL;
+      O[i] = *reinterpret_cast<const FV*>(a.o + o);
+      U[i] = *reinterpret_cast<const FV*>(a.u + o);
+      DS[i] = *reinterpret_cast<const FV*>(a.dacat + c);
+      DL[i] = *reinterpret_cast<const FV*>(a.dacat + c + hd);
+      GS[i] = *reinterpret_cast<const BV*>(a.gs + o);
+      GL[i] = *reinterpret_cast<const BV*>(a.gl + o);
     }
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) {
-      delta += __shfl_xor(delta, m, 32);
-      uu += __shfl_xor(uu, m, 32);
-    }
-    const float rho = 1.0f / sqrtf(uu / D + a.eps);
-    float sdr = 0.0f;  // sum over channels of (dr w) rhat
+    for (int i = 0; i < TPI; ++i) {
+      const int t = t0 + 8 * i;
+      const size_t o = (size_t)t * rs + h * D + l * CPL;
+      FV dO, dgs, rh, dr, dgl;
+      BV dOb, dub;
+      float delta = 0.0f, uu = 0.0f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      rh[e] *= rho;
-      const float sl = sig(gl[e]);
-      dr[e] = dal[e] * sl;
-      a.dgl[o + e] = dal[e] * rh[e] * w[e] * sl * (1.0f - sl);
-      dwp[e] += dr[e] * rh[e];
-      sdr += dr[e] * w[e] * rh[e];
-    }
+      for (int e = 0; e < CPL; ++e) {
+        const float ss = sig((float)GS[i][e]);
+        dO[e] = DS[i][e] * ss;
+        dgs[e] = DS[i][e] * O[i][e] * ss * (1.0f - ss);
+        delta += dO[e] * O[i][e];
+        uu += U[i][e] * U[i][e];
+      }
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) sdr += __shfl_xor(sdr, m, 32);
-    const float mean = sdr / D;
+      for (int m = 16; m >= 1; m >>= 1) {
+        delta += __shfl_xor(delta, m, 32);
+        uu += __shfl_xor(uu, m, 32);
+      }
+      const float rho = 1.0f / sqrtf(uu / D + a.eps);
+      float sdr = 0.0f;  // sum over channels of (dr w) rhat
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      a.du[o + e] = (__bf16)(rho * (dr[e] * w[e] - rh[e] * mean));
-      a.dO[o + e] = (__bf16)dO[e];
+      for (int e = 0; e < CPL; ++e) {
+        rh[e] = U[i][e] * rho;
+        const float sl = sig((float)GL[i][e]);
+        dr[e] = DL[i][e] * sl;
+        dgl[e] = DL[i][e] * rh[e] * w[e] * sl * (1.0f - sl);
+        sdr += dr[e] * w[e] * rh[e];
+      }
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) sdr += __shfl_xor(sdr, m, 32);
+      const float mean = sdr / D;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        dub[e] = (__bf16)(rho * (dr[e] * w[e] - rh[e] * mean));
+        dOb[e] = (__bf16)dO[e];
+      }
+      if (ok[i]) {
+        dwp += dr * rh;
+        *reinterpret_cast<FV*>(a.dgs + o) = dgs;
+        *reinterpret_cast<FV*>(a.dgl + o) = dgl;
+        *reinterpret_cast<BV*>(a.du + o) = dub;
+        *reinterpret_cast<BV*>(a.dO + o) = dOb;
+        if (l == 0) a.delta[(size_t)t * g.H + h] = delta;
+      }
     }
-    if (l == 0) a.delta[(size_t)t * g.H + h] = delta;
   }
 #pragma unroll
   for (int e = 0; e < CPL; ++e) red[grp][l * CPL + e] = dwp[e];
