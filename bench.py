@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
-PMC_TRAFFIC = {"source_sha256_16": "cc7faeb20d16f6a8", "bytes": 22.817e9}
+PMC_TRAFFIC = {"source_sha256_16": "579dfc2da4ca06a7", "bytes": 22.803e9}
 # the same for the MXFP8 GEMM (profiles/kernel_stats_768p_mxfp8_projections.md)
 PMC_TRAFFIC_MX = {"source_sha256_16": "cb0f1e10a0964a3b", "bytes": 25.021e9}
 MX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/mxfp8.hip", "video_diffusion_hybrid_sparse_amd/csrc/mxfp8.h",
