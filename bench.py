@@ -5,9 +5,12 @@ gate, block-sparse softmax + gate, both projections + residual) over the 768p la
 shape: 60 latent frames x 1008 tokens, 48 heads, head_dim 128, 512 text tokens, chunks
 of 5 frames, model dim 6144, bf16, on seeded synthetic inputs already resident in HBM.
 
-Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole layer; per-step
-kernel times come from HIP events the library records on its stream during the timed
-steps.  The CPU baseline times the fp64 oracle on a bounded sample of the same layer.
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole layer over the timed
+steps (20 by default, after 3 warm-ups); per-step kernel times come from HIP events the
+library records on its stream during those steps.  A second pass of as many calls,
+outside the timed region, reads the events after each call for the median and min of
+each step and of the whole call.  The CPU baseline times the fp64 oracle on a bounded
+sample of the same layer.
 
 With --linear-variant 1 the linear branch is the frame-wise delta rule (step size
 --delta-beta) instead of the additive states; the line then describes that layer.
@@ -55,6 +58,17 @@ def measured_traffic(sources, record):
 
 def softmax_traffic():
     return measured_traffic(SOFTMAX_SOURCES, PMC_TRAFFIC)
+
+
+def spread(per_call):
+    """Median and min over calls of each step's time and of their sum (one call)."""
+    import statistics
+    keys = list(per_call[0])
+    out = {k: {"median": round(statistics.median(pc[k] for pc in per_call), 4),
+               "min": round(min(pc[k] for pc in per_call), 4)} for k in keys}
+    calls = [sum(pc.values()) for pc in per_call]
+    out["call"] = {"median": round(statistics.median(calls), 4), "min": round(min(calls), 4)}
+    return out
 
 
 def log(*a):
@@ -106,7 +120,7 @@ def cpu_baseline(shape, inp, budget_s: float = 20.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--linear-variant", type=int, default=0, choices=(0, 1))
@@ -149,8 +163,16 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms, calls = binding.profile_read()
-    binding.profile_enable(False)
     assert calls == args.steps
+    # per-call spread, outside the timed loop: the library's step events read after each
+    # call (each read waits for that call), median and min per step and for the call
+    per_call = []
+    for _ in range(args.steps):
+        dl.run()
+        m, c = binding.profile_read()
+        assert c == 1
+        per_call.append(m)
+    binding.profile_enable(False)
     ms = (t1 - t0) * 1e3 / args.steps
     fl = workload.flops(shape)
     by = workload.bytes_moved(shape)
@@ -180,6 +202,7 @@ def main() -> int:
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": softmax_traffic()},
         "steps_ms": {k: round(v, 4) for k, v in per.items()},
+        "steps_ms_spread": spread(per_call),
         "steps_rate": {
             "softmax_tflops": round(achieved, 1),
             "projection_tflops": round(fl["projection"] / (per["projection"] * 1e-3) / 1e12, 1),
