@@ -1,7 +1,8 @@
 """GPU parity of the HIP layer against the CPU oracle, through the C ABI.
 
 Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16, ragged bf16 cases at
-both head dims, one without text, and a ragged fp8 case) are compared element by element
+both head dims, one without text, two with a short last chunk, and a ragged fp8 case)
+are compared element by element
 on every output and intermediate state; the 768p and 120-frame fp8 layers are compared
 on sampled tokens.  Tolerances: rel-L2 <= 1e-5 for the
 fp32 workloads and <= 1.5e-2 for bf16; index sets bit-exact everywhere.
@@ -27,7 +28,13 @@ NOTEXT = shapes.LayerShape("notext_f7_t70_c1_h1_d128_bf16", frames=7, tokens_per
 FP8_SMALL = shapes.LayerShape("fp8_f12_t100_c3_h3_d128", frames=12, tokens_per_frame=100, heads=3, head_dim=128,
                               text_len=40, chunk_frames=3, model_dim=200, qkv_dtype="fp8", act_dtype="bf16",
                               seed=2004)
-SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8_SMALL]
+# a short last chunk (F not a multiple of C: chunks {0-4} {5-9} {10-12}, and {0-3} {4-7}
+# {8-10}), with token and text counts off every tile size
+SHORT128 = shapes.LayerShape("shortchunk_f13_t45_c5_h2_d128_bf16", frames=13, tokens_per_frame=45, heads=2,
+                             head_dim=128, text_len=37, chunk_frames=5, model_dim=160, seed=2005)
+SHORT64 = shapes.LayerShape("shortchunk_f11_t29_c4_h2_d64_bf16", frames=11, tokens_per_frame=29, heads=2,
+                            head_dim=64, text_len=3, chunk_frames=4, model_dim=72, seed=2006)
+SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8_SMALL, SHORT128, SHORT64]
 TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 1.5e-2}
 
 
@@ -61,7 +68,7 @@ def oracle_for(shape):
     return _ORACLE[shape.name]
 
 
-@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768, shapes.LONG],
+@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, SHORT128, SHORT64, shapes.P768, shapes.LONG],
                          ids=lambda s: s.name)
 def test_membership_export_bit_exact(shape):
     cfg = binding.make_cfg(shape)
