@@ -2,7 +2,8 @@
 through the C ABI.
 
 Small bf16 workloads (ragged token, text and window sizes at both head dims, one
-without text, one with fp8 softmax inputs) are compared element by element on the
+without text, one with fp8 softmax inputs, two with a short last chunk) are compared
+element by element on the
 linear read u, the gated linear branch a_l, y = out - x, the text state and every
 chunk's forward and backward state; the 768p layer on sampled tokens of sampled heads.
 Tolerance: rel-L2 <= 1.5e-2 (bf16 inputs).
@@ -16,7 +17,7 @@ import torch
 import oracle
 from video_diffusion_hybrid_sparse_amd import runner, shapes, synth
 
-from .test_gpu_layer import FP8_SMALL, NOTEXT, RAGGED64, RAGGED128, _np, rel_l2
+from .test_gpu_layer import FP8_SMALL, NOTEXT, RAGGED64, RAGGED128, SHORT64, SHORT128, _np, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +29,7 @@ def delta(shape, beta):
 
 
 SMALL = [delta(shapes.MID, 0.5), delta(RAGGED128, 1.0), delta(RAGGED64, 0.3), delta(NOTEXT, 0.7),
-         delta(FP8_SMALL, 0.5)]
+         delta(FP8_SMALL, 0.5), delta(SHORT128, 0.6), delta(SHORT64, 0.9)]
 
 
 def oracle_delta(shape, inp, heads=None):
