@@ -13,12 +13,12 @@ import torch
 import oracle
 from video_diffusion_hybrid_sparse_amd import runner, shapes, synth
 
-from .test_gpu_layer import NOTEXT, RAGGED64, RAGGED128, SHORT64, SHORT128, _np, rel_l2
+from .test_gpu_layer import NOTEXT, ONECHUNK, RAGGED64, RAGGED128, SHORT64, SHORT128, WIDE, _np, rel_l2
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1.5e-2
-SHAPES = [shapes.MID, RAGGED128, RAGGED64, NOTEXT, SHORT128, SHORT64]
+SHAPES = [shapes.MID, RAGGED128, RAGGED64, NOTEXT, SHORT128, SHORT64, ONECHUNK, WIDE]
 
 
 def oracle_grads(shape, inp, dout):

@@ -2,7 +2,8 @@
 through the C ABI.
 
 Small bf16 workloads (ragged token, text and window sizes at both head dims, one
-without text, one with fp8 softmax inputs, two with a short last chunk) are compared
+without text, one with fp8 softmax inputs, two with a short last chunk, the single-chunk
+and two-neighbour-chunk cases) are compared
 element by element on the
 linear read u, the gated linear branch a_l, y = out - x, the text state and every
 chunk's forward and backward state; the 768p layer on sampled tokens of sampled heads.
@@ -17,7 +18,7 @@ import torch
 import oracle
 from video_diffusion_hybrid_sparse_amd import runner, shapes, synth
 
-from .test_gpu_layer import FP8_SMALL, NOTEXT, RAGGED64, RAGGED128, SHORT64, SHORT128, _np, rel_l2
+from .test_gpu_layer import FP8_SMALL, NOTEXT, ONECHUNK, RAGGED64, RAGGED128, SHORT64, SHORT128, WIDE, _np, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +30,8 @@ def delta(shape, beta):
 
 
 SMALL = [delta(shapes.MID, 0.5), delta(RAGGED128, 1.0), delta(RAGGED64, 0.3), delta(NOTEXT, 0.7),
-         delta(FP8_SMALL, 0.5), delta(SHORT128, 0.6), delta(SHORT64, 0.9)]
+         delta(FP8_SMALL, 0.5), delta(SHORT128, 0.6), delta(SHORT64, 0.9), delta(ONECHUNK, 0.4),
+         delta(WIDE, 0.8)]
 
 
 def oracle_delta(shape, inp, heads=None):

@@ -1,8 +1,9 @@
 """GPU parity of the HIP layer against the CPU oracle, through the C ABI.
 
 Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16, ragged bf16 cases at
-both head dims, one without text, two with a short last chunk, and a ragged fp8 case)
-are compared element by element
+both head dims, one without text, two with a short last chunk, one frame-3 single-chunk
+case, one with two neighbour chunks, and a ragged fp8 case) are compared element by
+element
 on every output and intermediate state; the 768p and 120-frame fp8 layers are compared
 on sampled tokens.  Tolerances: rel-L2 <= 1e-5 for the
 fp32 workloads and <= 1.5e-2 for bf16; index sets bit-exact everywhere.
@@ -34,7 +35,15 @@ SHORT128 = shapes.LayerShape("shortchunk_f13_t45_c5_h2_d128_bf16", frames=13, to
                              head_dim=128, text_len=37, chunk_frames=5, model_dim=160, seed=2005)
 SHORT64 = shapes.LayerShape("shortchunk_f11_t29_c4_h2_d64_bf16", frames=11, tokens_per_frame=29, heads=2,
                             head_dim=64, text_len=3, chunk_frames=4, model_dim=72, seed=2006)
-SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8_SMALL, SHORT128, SHORT64]
+# degenerate geometry: three frames of one token in a single (partial) chunk, so every
+# frame is in every window and both memories are empty; and a window of two neighbour
+# chunks on each side (R = 2)
+ONECHUNK = shapes.LayerShape("onechunk_f3_t1_c4_h1_d64_bf16", frames=3, tokens_per_frame=1, heads=1, head_dim=64,
+                             text_len=2, chunk_frames=4, model_dim=48, seed=2007)
+WIDE = shapes.LayerShape("r2_f9_t7_c1_h2_d128_bf16", frames=9, tokens_per_frame=7, heads=2, head_dim=128,
+                         text_len=6, chunk_frames=1, neighbor_chunks=2, model_dim=64, seed=2008)
+SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8_SMALL, SHORT128, SHORT64,
+         ONECHUNK, WIDE]
 TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 1.5e-2}
 
 
@@ -68,7 +77,8 @@ def oracle_for(shape):
     return _ORACLE[shape.name]
 
 
-@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, SHORT128, SHORT64, shapes.P768, shapes.LONG],
+@pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, SHORT128, SHORT64, ONECHUNK, WIDE,
+                                   shapes.P768, shapes.LONG],
                          ids=lambda s: s.name)
 def test_membership_export_bit_exact(shape):
     cfg = binding.make_cfg(shape)
