@@ -35,9 +35,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void copy_lds16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+// a pointer the wave agrees on, as a scalar value
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 
 // number of recurrence frames a chunk's forward / backward state has taken in
@@ -87,23 +89,35 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
       valid = imin(TT, g.T - tt * TT);
     }
   };
+  // Tile copies as untracked LDS DMA (dma16: the compiler does not wait for them before
+  // LDS reads; the walk waits for each tile itself): an SGPR base per tile (its first row,
+  // head h) and per-lane 32-bit offsets (row inside the tile, clamped to the block, and
+  // swizzled chunk).  Rows past the block are copies, zeroed in R'.
+  const uint32_t rs2 = (uint32_t)rs * 2;
+  const uint32_t m0k = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Kt[0][0] + wave * 64 * 16);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vt[0][0] + wave * 64 * 16);
   auto issue = [&](int j, int buf) __attribute__((always_inline)) {
     int first, valid;
     bool text;
     tile_at(j, first, valid, text);
-    const __bf16* kb = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.k) + (text ? tk_off : 0));
-    const __bf16* vb = reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.v) + (text ? tv_off : 0));
+    const size_t base = (size_t)first * rs + h * D;
+    const __bf16* kb = static_cast<const __bf16*>(uniform_ptr(
+        reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.k) + (text ? tk_off : 0)) + base));
+    const __bf16* vb = static_cast<const __bf16*>(uniform_ptr(
+        reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.v) + (text ? tv_off : 0)) + base + vcol0));
 #pragma unroll
     for (int i = 0; i < NKI; ++i) {
       const int q = i * 256 + tid, row = q / CPR, c = q % CPR;
-      const int src = first + imin(row, valid - 1);  // rows past the block: a copy, zeroed in R'
-      copy_lds16(kb + (size_t)src * rs + h * D + (c ^ swz<CPR>(row)) * 8, &Kt[buf][(i * 256 + wave * 64) * 8]);
+      dma16(kb, (uint32_t)imin(row, valid - 1) * rs2 + (uint32_t)(c ^ swz<CPR>(row)) * 16,
+            m0k + (uint32_t)buf * (TT * D * 2) + i * 256 * 16);
     }
 #pragma unroll
     for (int i = 0; i < NVI; ++i) {
       const int q = i * 256 + tid, row = q / 8, c = q % 8;
-      const int src = first + imin(row, valid - 1);
-      copy_lds16(vb + (size_t)src * rs + h * D + vcol0 + (c ^ swz<8>(row)) * 8, &Vt[buf][(i * 256 + wave * 64) * 8]);
+      dma16(vb, (uint32_t)imin(row, valid - 1) * rs2 + (uint32_t)(c ^ swz<8>(row)) * 16,
+            m0v + (uint32_t)buf * (TT * VC * 2) + i * 256 * 16);
     }
   };
 
