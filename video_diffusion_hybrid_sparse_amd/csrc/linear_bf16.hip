@@ -138,8 +138,9 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 
 // ---- state read: u = q.S_fwd + q.S_bwd, RMSNorm, gate --------------------------------
 //
-// One workgroup = up to 512 query tokens of one query group and one head; each of the 4
-// waves walks 32-token sub-tiles.  The group's two states are summed in float32 (the
+// One workgroup = up to 1024 query tokens of one query group and one head (the states'
+// load and split is paid once per 1024 tokens); each of the 4 waves walks 32-token
+// sub-tiles.  The group's two states are summed in float32 (the
 // identity feature map makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding
 // differs), split into bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled
 // 16-byte chunks) in LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes
@@ -149,7 +150,7 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 // loads and output stores are 16 bytes wide.
 template <int D>
 __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
-  constexpr int BM = 512, KS = D / 16, DT = D / 32, CPR = D / 8;
+  constexpr int BM = 1024, KS = D / 16, DT = D / 32, CPR = D / 8;
   __shared__ __attribute__((aligned(16))) __bf16 Shi[D * D];
   __shared__ __attribute__((aligned(16))) __bf16 Slo[D * D];
   const Geo g = a.geo;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
 }
 
 hipError_t launch_readout_bf16(const ReadoutArgs<__bf16>& a, hipStream_t stream) {
-  const int tiles = count_tiles(a.geo, 512);
+  const int tiles = count_tiles(a.geo, 1024);
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.geo.H), block(256);
   if (a.geo.d == 128)
