@@ -40,6 +40,13 @@ def test_agpr_write_then_mfma_accumulate_flagged():
     assert len(asm_check.check_asm(asm)) == 1
 
 
+def test_compiler_use_of_m0_flagged_outside_inline_asm():
+    plain = "\ts_mov_b32 m0, s4\n\tds_read_addtid_b32 v1\n"
+    assert len(asm_check.check_m0(plain)) == 1
+    in_asm = "\t;;#ASMSTART\n\ts_mov_b32 m0, s4\n\ts_nop 0\n\t;;#ASMEND\n\tv_mov_b32_e32 v1, v2\n"
+    assert asm_check.check_m0(in_asm) == []
+
+
 @pytest.mark.skipif(shutil.which("hipcc") is None and not __import__("os").path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not installed")
 def test_kernels_as_compiled_are_clean():

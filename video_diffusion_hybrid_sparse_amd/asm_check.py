@@ -15,8 +15,13 @@ to these instructions:
     store: at least 12 wait states (NumPasses + 3, plus one on gfx950);
   - an MFMA's C operand overwritten by the VALU: at least 11 wait states.
 
-A wait state is one issued instruction; s_nop N counts N + 1.  Used by build() and by a
-CPU test; the build fails on any violation.
+A wait state is one issued instruction; s_nop N counts N + 1.
+
+It also checks the sources whose kernels copy into LDS with the inline-asm DMA (which
+writes M0, a register the compiler reserves and does not protect around inline asm):
+no compiler-generated instruction there may use M0.
+
+Used by build() and by a CPU test; the build fails on any violation.
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ MFMA_SRCC_TO_VALU_WRITE = 11
 TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel",)),
            ("backward.hip", ("_ZN3vdn21softmax_bwd_kv_kernel",)))
 PREFIXES = tuple(p for _, ps in TARGETS for p in ps)
+# sources whose kernels write M0 in inline asm (the LDS DMA copies)
+M0_SOURCES = ("softmax_bf16.hip", "backward.hip", "delta_bf16.hip", "mxfp8.hip")
 
 _REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
 _STORE = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store", "flat_store")
@@ -187,6 +194,20 @@ def check_asm(asm: str, prefixes=PREFIXES) -> list[str]:
     return problems
 
 
+def check_m0(asm: str) -> list[str]:
+    """Compiler-generated instructions (outside inline-asm blocks) that name M0."""
+    problems, in_asm = [], False
+    for raw in asm.split("\n"):
+        t = raw.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif t.startswith(";;#ASMEND"):
+            in_asm = False
+        elif not in_asm and t and not t.startswith((".", ";")) and re.search(r"\bm0\b", t.split(";")[0]):
+            problems.append(f"compiler-generated use of M0 beside the inline-asm LDS copies: '{t}'")
+    return problems
+
+
 def kernel_asm(src: str) -> str:
     """gfx950 assembly of a source file, compiled with the library's flags."""
     from .build import FLAGS, HIPCC
@@ -207,13 +228,17 @@ def check(src: str | None = None) -> list[str]:
         return check_asm(kernel_asm(src))
     from .build import CSRC
     problems = []
+    asm = {}
     for name, prefixes in TARGETS:
-        problems += check_asm(kernel_asm(os.path.join(CSRC, name)), prefixes)
+        asm[name] = kernel_asm(os.path.join(CSRC, name))
+        problems += check_asm(asm[name], prefixes)
+    for name in M0_SOURCES:
+        problems += [f"{name}: {p}" for p in check_m0(asm.get(name) or kernel_asm(os.path.join(CSRC, name)))]
     return problems
 
 
 if __name__ == "__main__":
     import sys
     found = check(sys.argv[1] if len(sys.argv) > 1 else None)
-    print("\n".join(found) if found else "no MFMA wait-state violations")
+    print("\n".join(found) if found else "no MFMA wait-state violations, no compiler use of M0 beside the LDS copies")
     sys.exit(1 if found else 0)

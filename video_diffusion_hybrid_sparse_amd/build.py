@@ -53,11 +53,12 @@ def build(verbose: bool = False) -> str:
           "-lhipblaslt", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"])
     os.replace(tmp, LIB)
     # the bf16 softmax and the merged dK/dV backward write their MFMAs as inline asm:
-    # check the wait states around them
+    # check the wait states around them, and that no compiler-generated code uses M0 in
+    # the sources whose LDS copies write it from inline asm
     from .asm_check import check
     problems = check()
     if problems:
-        raise RuntimeError("MFMA wait-state violations:\n" + "\n".join(problems))
+        raise RuntimeError("static check of the compiled kernels failed:\n" + "\n".join(problems))
     return LIB
 
 
