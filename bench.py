@@ -14,9 +14,13 @@ sample of the same layer.
 
 With --linear-variant 1 the linear branch is the frame-wise delta rule (step size
 --delta-beta) instead of the additive states; the line then describes that layer.
+With --workload long the layer is the 120-frame long clip (120 x 1008 tokens, same
+heads and widths) with e4m3 softmax inputs and a bf16 linear branch; its softmax
+roofline is the mixed peak of e4m3 QK^T on the video keys and bf16 QK^T (text) and P V.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--linear-variant 0|1] [--delta-beta B]
+                       [--linear-variant 0|1] [--delta-beta B] [--workload 768p|long]
+                       [--backward] [--projections]
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ import sys
 import time
 
 METRIC = "hybrid-attn layer ms + TFLOP/s (% MFMA peak) at 768p 60-frame shape, 1 GPU"
+METRIC_LONG = "hybrid-attn layer ms + TFLOP/s (% MFMA peak) at 120-frame fp8 long-clip shape, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -75,46 +80,92 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(shape, inp, budget_s: float = 20.0) -> dict:
-    """Time the oracle (as it is) on a bounded sample of the layer: all four steps for a
-    subset of heads and the query tokens of a few frames, on the host cores."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, inp) -> dict:
+    """Time the oracle (as it is) on a bounded sample of the layer on the host cores: the
+    softmax and linear branches of a subset of heads for the query tokens of a few
+    frames, one head per task on a pool of as many threads as the process may use
+    (BLAS single-threaded inside each task), then the gates, RMSNorm and the projection
+    restricted to those heads' input columns (BLAS on all cores)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
 
     import oracle
-    from video_diffusion_hybrid_sparse_amd import synth
+    from video_diffusion_hybrid_sparse_amd import synth, workload
 
     F, T, C, R, H, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.neighbor_chunks, shape.heads, shape.head_dim
     frames = [0, 1, 5, 10, F // 2, F - 5, F - 2]
     rows = np.concatenate([np.arange(f * T, (f + 1) * T) for f in frames])
-    heads = list(range(24))
+    heads = list(range(min(24, H)))
     cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
+    hs = torch.tensor(heads)
 
-    def sub(t):
-        return np.ascontiguousarray(synth.f64(t)[:, heads, :])
+    def sub(t, scale=None):
+        """float64 values of the sampled heads (e4m3 codes times their scale)."""
+        t = t.index_select(1, hs)
+        a = synth.e4m3_values(t).double().numpy() * scale if scale is not None else synth.f64(t)
+        return np.ascontiguousarray(a)
 
-    q, k, v, tk, tv = (sub(t) for t in (inp.q, inp.k, inp.v, inp.text_k, inp.text_v))
+    fp8 = shape.qkv_dtype == "fp8"
+    q, k, v = (sub(t, sc if fp8 else None) for t, sc in ((inp.q, inp.q_scale), (inp.k, inp.k_scale),
+                                                         (inp.v, inp.v_scale)))
+    tk, tv = sub(inp.text_k), sub(inp.text_v)
+    ql, kl, vl = (sub(inp.q_lin), sub(inp.k_lin), sub(inp.v_lin)) if fp8 else (q, k, v)
     g_s, g_l = sub(inp.g_s)[rows], sub(inp.g_l)[rows]
     w = synth.f64(inp.w_rms)[heads]
     w_s, w_l = synth.f64(inp.w_s)[:, cols], synth.f64(inp.w_l)[:, cols]
     x = synth.f64(inp.x)[rows]
+    cores = len(os.sched_getaffinity(0))
+    nh = len(heads)
+
+    def one_head(i):
+        sl = slice(i, i + 1)
+        o = oracle.layer.softmax_branch(q[:, sl], k[:, sl], v[:, sl], tk[:, sl], tv[:, sl], F, C, R, rows=rows)
+        u = oracle.layer.linear_branch(ql[:, sl], kl[:, sl], vl[:, sl], tk[:, sl], tv[:, sl], F, C, R, rows=rows)
+        return o, u
+
     t0 = time.perf_counter()
-    o = oracle.layer.softmax_branch(q, k, v, tk, tv, F, C, R, rows=rows)
-    u = oracle.layer.linear_branch(q, k, v, tk, tv, F, C, R, rows=rows)
+    with threadpool_limits(1), ThreadPoolExecutor(cores) as ex:
+        parts = list(ex.map(one_head, range(nh)))
+    o = np.concatenate([p[0] for p in parts], axis=1)
+    u = np.concatenate([p[1] for p in parts], axis=1)
     a_s = oracle.layer.sigmoid(g_s) * o
     a_l = oracle.layer.sigmoid(g_l) * oracle.layer.rms_norm(u, w, shape.rms_eps)
     oracle.layer.project(a_s, a_l, w_s, w_l, x)
     dt = time.perf_counter() - t0
-    from video_diffusion_hybrid_sparse_amd import workload
     kpf = workload.keys_per_frame(shape)
-    nh = len(heads)
     fl = (4 * d * nh * sum(kpf[f] * T for f in frames) + 2 * d * d * nh * (T * (F - 2) + shape.text_len)
           + 2 * d * d * nh * len(rows) + 2 * len(rows) * 2 * nh * d * shape.dmodel)
-    cores = len(os.sched_getaffinity(0))
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu": cpu_model(), "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"fp64 oracle, all four steps for heads {heads} of {H} and the query tokens of frames "
-                      f"{frames} ({len(rows)} tokens); projection restricted to those heads' input columns; "
-                      f"{fl / 1e9:.1f} GFLOP of the layer's algorithmic work"}
+            "sample": f"fp64 oracle, all four steps for heads {heads[0]}..{heads[-1]} of {H} and the query tokens "
+                      f"of frames {frames} ({len(rows)} tokens), one head per task on {cores} threads; projection "
+                      f"restricted to those heads' input columns; {fl / 1e9:.1f} GFLOP of the layer's "
+                      f"algorithmic work"}
+
+
+# Figures the pages print, for context only: full-model denoising time per function
+# evaluation of a 768p, 14.4 s clip on NVIDIA GPUs (vdn-minimax-h3 model card, section
+# "Results").  They are not per-layer figures and are not the target of this bench.
+PAGES_CONTEXT = {
+    "unit": "s/NFE (full model, 768p 14.4 s clip)",
+    "B200": {"dense": 16.74, "vdn_fp8": 6.41},
+    "H200": {"dense": 32.7, "vdn_fp8": 11.2},
+    "source": "vdn-minimax-h3 model card, section Results",
+}
 
 
 def main() -> int:
@@ -128,6 +179,8 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true", help="time the layer backward instead of the forward")
     ap.add_argument("--projections", action="store_true",
                     help="time the MXFP8 input-side projections (quantise x, block-scaled GEMM) instead")
+    ap.add_argument("--workload", default="768p", choices=("768p", "long"),
+                    help="768p: the 60-frame bf16 layer; long: the 120-frame layer with e4m3 softmax inputs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the layer is not sharded across GPUs (asked for --gpus {args.gpus})",
@@ -138,7 +191,7 @@ def main() -> int:
 
     from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth, workload
 
-    shape = shapes.P768
+    shape = shapes.P768 if args.workload == "768p" else shapes.LONG
     if args.projections:
         return bench_projections(args, shape)
     if args.linear_variant == 1:
@@ -179,8 +232,22 @@ def main() -> int:
     per = {k: v / args.steps for k, v in step_ms.items()}
     sm_ms = per["softmax"]
     achieved = fl["softmax"] / (sm_ms * 1e-3) / 1e12
+    fp8 = shape.qkv_dtype == "fp8"
+    if fp8:
+        # e4m3 QK^T of the video keys at the fp8 MFMA rate, text QK^T and P V at the bf16 rate
+        sm_peak = workload.softmax_mixed_peak(shape, PEAK_FP8_TFLOPS, PEAK_BF16_TFLOPS)
+        kernel, traffic = "softmax_fp8_kernel<128>", None
+        metric = METRIC_LONG
+        dtype = "fp8 e4m3 QK^T + bf16 PV, linear branch, projections"
+        data = "synthetic: seeded N(0,1) activations (per-tensor e4m3 q/k/v) and gate logits, scaled N(0,1) weights"
+    else:
+        sm_peak = PEAK_BF16_TFLOPS
+        kernel, traffic = "softmax_sw_kernel<128>", softmax_traffic()
+        metric = METRIC
+        dtype = "bf16"
+        data = "synthetic: seeded N(0,1) activations and gate logits, scaled N(0,1) weights, 768p layer shape"
     res = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(fl["total"] / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -190,17 +257,17 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) activations and gate logits, scaled N(0,1) weights, 768p layer shape",
+        "dtype": dtype,
+        "data": data,
         "config": {"workload": shape.name, "frames": shape.frames, "tokens_per_frame": shape.tokens_per_frame,
                    "heads": shape.heads, "head_dim": shape.head_dim, "text_len": shape.text_len,
                    "chunk_frames": shape.chunk_frames, "model_dim": shape.dmodel,
                    "linear_variant": shape.linear_variant,
                    "layer_tflop": round(fl["total"] / 1e12, 3)},
         "pct_mfma_peak": round(100 * fl["total"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"kernel": "softmax_sw_kernel<128>", "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": softmax_traffic()},
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": round(sm_peak, 1), "unit": "TFLOP/s", "frac": round(achieved / sm_peak, 4),
+                     "traffic": traffic},
         "steps_ms": {k: round(v, 4) for k, v in per.items()},
         "steps_ms_spread": spread(per_call),
         "steps_rate": {
@@ -211,6 +278,7 @@ def main() -> int:
             "state_scan_gbs": round(by["state_scan"] / max(per["state_scan"], 1e-6) / 1e6, 1),
             "linear_read_gbs": round(by["linear_read"] / (per["linear_read"] * 1e-3) / 1e9, 1),
         },
+        "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline and shape.linear_variant == 0:
         log("bench: cpu baseline (oracle on a sample)")

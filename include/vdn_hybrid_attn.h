@@ -36,9 +36,10 @@
  *
  * Conventions for every entry point:
  *   - All tensors are dense, row-major, 16-byte aligned device pointers owned by the
- *     caller.  The library allocates no tensor memory; scratch space comes from the
+ *     caller.  The library allocates no device memory; scratch space comes from the
  *     caller's workspace.  (The projection GEMM library handle is created once per
- *     device on first use.)
+ *     device on first use, and the membership export uses a small buffer the library
+ *     holds per device.)
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream) of the current HIP device; no entry point except
  *     vdn_hybrid_attn_membership synchronises.
@@ -216,7 +217,9 @@ vdn_status vdn_hybrid_attn_bwd_saved(const void* q, const void* k, const void* v
  * Membership export: runs, on the current device, the same index functions the kernels
  * use and writes codes_host[f * F + g] (host memory, F*F bytes) = how query frame f reads
  * key frame g: 1 softmax, 2 forward state, 3 backward state, 0 not at all.
- * Synchronises the device.
+ * The codes pass through a 1 MiB device buffer that the library holds on every device it
+ * runs on (F <= 1024, else VDN_ERR_UNSUPPORTED); nothing is allocated.  Calls are
+ * serialised inside the process.  Runs on the null stream and synchronises the device.
  */
 vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_host);
 

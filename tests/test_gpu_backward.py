@@ -3,8 +3,11 @@ are pinned to finite differences), through the C ABI.
 
 bf16 workloads with ragged token, text and window sizes at both head dims and one
 without text: every gradient (q, k, v, text keys and values, both gate logits, the
-RMSNorm weight, both projections) element by element at rel-L2 <= 1.5e-2, and the
-backward is bitwise repeatable.
+RMSNorm weight, both projections) element by element at rel-L2 <= 1.5e-2 over the whole
+tensor and <= 5e-2 over every (token, head) row of head_dim gradients (projection
+weights: every (output channel, head) row; tests/parity.py), and the backward is
+bitwise repeatable.  Peaky-logit inputs (synth.peaky_inputs: scores that rise along the
+key walk, up to 44 log2 units above the rest) are checked the same way.
 """
 import numpy as np
 import pytest
@@ -13,7 +16,8 @@ import torch
 import oracle
 from video_diffusion_hybrid_sparse_amd import runner, shapes, synth
 
-from .test_gpu_layer import NOTEXT, ONECHUNK, RAGGED64, RAGGED128, SHORT64, SHORT128, WIDE, _np, rel_l2
+from .parity import ROW_TOL, check, fmt
+from .test_gpu_layer import NOTEXT, ONECHUNK, RAGGED64, RAGGED128, SHORT64, SHORT128, WIDE, _np
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +33,7 @@ def oracle_grads(shape, inp, dout):
                                        shape.chunk_frames, shape.neighbor_chunks, shape.rms_eps)
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s.name)
-def test_backward_parity(shape):
-    inp = synth.make_inputs(shape)
+def check_grads(shape, inp):
     dout = synth.upstream_grad(shape)
     ref = oracle_grads(shape, inp, dout)
     dl = runner.upload(inp)
@@ -40,11 +42,20 @@ def test_backward_parity(shape):
     names = ["dq", "dk", "dv", "dg_s", "dg_l", "dw_rms", "dw_s", "dw_l"]
     if shape.text_len:
         names += ["dtext_k", "dtext_v"]
-    errs = {n: rel_l2(_np(got[n]), ref[n]) for n in names}
-    print(shape.name, {n: f"{e:.2e}" for n, e in errs.items()}, flush=True)
-    for n, e in errs.items():
-        assert np.isfinite(_np(got[n])).all(), n
-        assert e <= TOL, (n, e)
+    rep = {}
+    for n in names:
+        check(n, _np(got[n]), ref[n], TOL, ROW_TOL["bf16"], shape.head_dim, rep)
+    print(shape.name, fmt(rep), flush=True)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: s.name)
+def test_backward_parity(shape):
+    check_grads(shape, synth.make_inputs(shape))
+
+
+@pytest.mark.parametrize("shape", [shapes.MID, RAGGED128, SHORT64], ids=lambda s: s.name)
+def test_backward_parity_peaky(shape):
+    check_grads(shape, synth.peaky_inputs(shape))
 
 
 def test_backward_is_deterministic():
@@ -90,11 +101,10 @@ def test_768p_backward_sampled():
                     dtext_v=got["dtext_v"][:, h], dg_s=got["dg_s"].index_select(0, qi)[:, h],
                     dg_l=got["dg_l"].index_select(0, qi)[:, h], dw_rms=got["dw_rms"][h],
                     dw_s=got["dw_s"][:, cols], dw_l=got["dw_l"][:, cols])
-        errs = {n: rel_l2(_np(t), want[n]) for n, t in have.items()}
-        print("768p head", h, {n: f"{e:.2e}" for n, e in errs.items()}, flush=True)
-        for n, e in errs.items():
-            assert np.isfinite(_np(have[n])).all(), n
-            assert e <= TOL, (n, e)
+        rep = {}
+        for n, t in have.items():
+            check(n, _np(t), want[n], TOL, ROW_TOL["bf16"], d, rep)
+        print("768p head", h, fmt(rep), flush=True)
 
 
 @pytest.mark.parametrize("shape", [shapes.MID, RAGGED128], ids=lambda s: s.name)

@@ -7,7 +7,8 @@ and two-neighbour-chunk cases) are compared
 element by element on the
 linear read u, the gated linear branch a_l, y = out - x, the text state and every
 chunk's forward and backward state; the 768p layer on sampled tokens of sampled heads.
-Tolerance: rel-L2 <= 1.5e-2 (bf16 inputs).
+Tolerance: rel-L2 <= 1.5e-2 (bf16 inputs) over each whole tensor and 5e-2 over each
+(token, head), output-token or state row (tests/parity.py).
 """
 import dataclasses
 
@@ -18,7 +19,10 @@ import torch
 import oracle
 from video_diffusion_hybrid_sparse_amd import runner, shapes, synth
 
-from .test_gpu_layer import FP8_SMALL, NOTEXT, ONECHUNK, RAGGED64, RAGGED128, SHORT64, SHORT128, WIDE, _np, rel_l2
+from .parity import ROW_TOL, check, fmt
+from .test_gpu_layer import FP8_SMALL, NOTEXT, ONECHUNK, RAGGED64, RAGGED128, SHORT64, SHORT128, WIDE, _np
+
+ROW = ROW_TOL["bf16"]
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +60,7 @@ def check_chunk_states(shape, ws, fwd, bwd, heads=slice(None)):
             if np.linalg.norm(want_s) == 0:
                 assert np.abs(got_s).max() == 0, c
             else:
-                assert rel_l2(got_s, want_s) <= TOL, (c, rel_l2(got_s, want_s))
+                check(f"state[{c}]", got_s, want_s, TOL, ROW, shape.head_dim)
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
@@ -80,13 +84,14 @@ def test_delta_layer_parity(shape):
                out=_np(dl.out), o_soft=_np(dl.o_soft_dbg))
     got["y"] = got["out"] - x
     ref = dict(ref, y=ref["out"] - x)
-    errs = {k: rel_l2(got[k], ref[k]) for k in ("u", "a_l", "y", "out", "o_soft")}
-    print(shape.name, {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
-    for key, e in errs.items():
-        assert e <= TOL, (key, e)
-    assert np.isfinite(got["u"]).all()
+    rep = {}
+    for key in ("u", "a_l", "o_soft"):
+        check(key, got[key], ref[key], TOL, ROW, shape.head_dim, rep)
+    for key in ("y", "out"):
+        check(key, got[key], ref[key], TOL, ROW, shape.dmodel, rep)
+    print(shape.name, fmt(rep), flush=True)
     if shape.text_len:
-        assert rel_l2(_np(ws["text_state"]), Tx) <= TOL
+        check("Tx", _np(ws["text_state"]), Tx, TOL, ROW, shape.head_dim)
     else:
         assert np.abs(_np(ws["text_state"])).max() == 0
     check_chunk_states(shape, ws, fwd, bwd)
@@ -119,7 +124,7 @@ def test_768p_delta_sampled_parity():
     rows = np.array(sorted({f * T + o for f in frames for o in (0, 333, T - 1)}))
     want = oracle.layer.linear_read(oracle.layer.phi(ql), fwd, bwd, F, rows)
     got = _np(dl.u_lin_dbg.index_select(0, torch.from_numpy(rows).cuda()))[:, heads]
-    e = rel_l2(got, want)
-    print("768p delta u rel-L2", e, flush=True)
-    assert e <= TOL
+    rep = {}
+    check("u", got, want, TOL, ROW, shape.head_dim, rep)
+    print("768p delta", fmt(rep), flush=True)
     check_chunk_states(shape, dl.workspace_tensors(), fwd, bwd, heads)

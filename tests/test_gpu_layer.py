@@ -3,10 +3,17 @@
 Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16, ragged bf16 cases at
 both head dims, one without text, two with a short last chunk, one frame-3 single-chunk
 case, one with two neighbour chunks, and a ragged fp8 case) are compared element by
-element
-on every output and intermediate state; the 768p and 120-frame fp8 layers are compared
-on sampled tokens.  Tolerances: rel-L2 <= 1e-5 for the
-fp32 workloads and <= 1.5e-2 for bf16; index sets bit-exact everywhere.
+element on every output and intermediate state: the whole-tensor rel-L2 (<= 1e-5 for
+fp32, <= 1.5e-2 for bf16 and fp8) and, for every (token, head) row, output-token row and
+state row, the row rel-L2 (tests/parity.py).  Index sets are bit-exact everywhere.
+
+Peaky-logit cases (synth.peaky_inputs) put the largest scores of every query late in
+its key walk, so the softmax kernels must raise their reference maximum, rescale the
+partial output and redo the exponentials of the block; with a planted score 200 (log2
+units) above the rest, an exponential against the unraised reference overflows float32,
+so a finite, matching result shows that the rescale ran.
+
+The 768p and 120-frame fp8 layers are compared on sampled tokens.
 """
 import numpy as np
 import pytest
@@ -14,6 +21,8 @@ import torch
 
 import oracle
 from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth
+
+from .parity import ROW_TOL, check, fmt, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -47,12 +56,6 @@ SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8
 TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 1.5e-2}
 
 
-def rel_l2(got, want):
-    got = np.asarray(got, np.float64)
-    want = np.asarray(want, np.float64)
-    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
-
-
 def _np(t):
     return t.detach().float().cpu().double().numpy()
 
@@ -60,20 +63,24 @@ def _np(t):
 _ORACLE = {}
 
 
+def oracle_of(shape, inp):
+    q, k, v = inp.qkv_values()
+    ql, kl, vl = inp.linear_qkv_values()
+    f = synth.f64
+    ref = oracle.layer.layer(q, k, v, f(inp.text_k), f(inp.text_v), f(inp.g_s), f(inp.g_l), f(inp.w_rms),
+                             f(inp.w_s), f(inp.w_l), f(inp.x), shape.frames, shape.chunk_frames,
+                             shape.neighbor_chunks, shape.rms_eps, q_lin=ql, k_lin=kl, v_lin=vl)
+    S = oracle.layer.frame_states(kl, vl, shape.frames)
+    Tx = oracle.layer.text_state(f(inp.text_k), f(inp.text_v))
+    fwd, bwd = oracle.layer.side_states(S, Tx, shape.frames, shape.chunk_frames, shape.neighbor_chunks)
+    ref.update(S=S, Tx=Tx, fwd=fwd, bwd=bwd)
+    return ref
+
+
 def oracle_for(shape):
     if shape.name not in _ORACLE:
         inp = synth.make_inputs(shape)
-        q, k, v = inp.qkv_values()
-        ql, kl, vl = inp.linear_qkv_values()
-        f = synth.f64
-        ref = oracle.layer.layer(q, k, v, f(inp.text_k), f(inp.text_v), f(inp.g_s), f(inp.g_l), f(inp.w_rms),
-                                 f(inp.w_s), f(inp.w_l), f(inp.x), shape.frames, shape.chunk_frames,
-                                 shape.neighbor_chunks, shape.rms_eps, q_lin=ql, k_lin=kl, v_lin=vl)
-        S = oracle.layer.frame_states(kl, vl, shape.frames)
-        Tx = oracle.layer.text_state(f(inp.text_k), f(inp.text_v))
-        fwd, bwd = oracle.layer.side_states(S, Tx, shape.frames, shape.chunk_frames, shape.neighbor_chunks)
-        ref.update(S=S, Tx=Tx, fwd=fwd, bwd=bwd)
-        _ORACLE[shape.name] = (inp, ref)
+        _ORACLE[shape.name] = (inp, oracle_of(shape, inp))
     return _ORACLE[shape.name]
 
 
@@ -87,14 +94,14 @@ def test_membership_export_bit_exact(shape):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
-def test_layer_parity(shape):
-    inp, ref = oracle_for(shape)
+def check_layer(shape, inp, ref, states=True):
+    """Run the layer on `inp` and compare every output (and, with states, every
+    intermediate state) with the oracle's `ref`, whole-tensor and row by row."""
     dl = runner.upload(inp, debug=True, sentinel=float("nan"))
     dl.run()
     torch.cuda.synchronize()
-    tol = TOL[shape.qkv_dtype]
-    hd = shape.hd
+    tol, row_tol = TOL[shape.qkv_dtype], ROW_TOL[shape.qkv_dtype]
+    hd, d, D = shape.hd, shape.head_dim, shape.dmodel
     ws = dl.workspace_tensors()
     x = synth.f64(inp.x)
     got = dict(o_soft=_np(dl.o_soft_dbg), u=_np(dl.u_lin_dbg),
@@ -102,20 +109,20 @@ def test_layer_parity(shape):
                a_l=_np(ws["branch_out"][:, hd:]).reshape(ref["a_l"].shape),
                out=_np(dl.out))
     got["y"] = got["out"] - x
-    ref = dict(ref, y=ref["out"] - x)
-    errs = {k: rel_l2(got[k], ref[k]) for k in ("o_soft", "u", "a_s", "a_l", "y", "out")}
-    print(shape.name, {k: f"{e:.2e}" for k, e in errs.items()}, flush=True)
-    for k, e in errs.items():
-        assert e <= tol, (k, e)
-    for k in ("o_soft", "u", "out"):
-        assert np.isfinite(got[k]).all(), k
-
+    want = dict(ref, y=ref["out"] - x)
+    rep = {}
+    for key in ("o_soft", "u", "a_s", "a_l"):
+        check(key, got[key], want[key], tol, row_tol, d, rep)
+    for key in ("y", "out"):
+        check(key, got[key], want[key], tol, row_tol, D, rep)
+    print(shape.name, fmt(rep), flush=True)
+    if not states:
+        return
     # per-step states: frame states, text state, and each chunk's forward/backward state
     F, C = shape.frames, shape.chunk_frames
-    S = _np(ws["frame_states"])
-    assert rel_l2(S, ref["S"]) <= tol
+    check("S", _np(ws["frame_states"]), ref["S"], tol, row_tol, d)
     if shape.text_len:
-        assert rel_l2(_np(ws["text_state"]), ref["Tx"]) <= tol
+        check("Tx", _np(ws["text_state"]), ref["Tx"], tol, row_tol, d)
     else:
         assert np.abs(_np(ws["text_state"])).max() == 0
     fw, bw = _np(ws["fwd_states"]), _np(ws["bwd_states"])
@@ -124,11 +131,40 @@ def test_layer_parity(shape):
         if not frames:
             continue
         f = frames[0]
-        for got_s, want_s in ((fw[c], ref["fwd"][f]), (bw[c], ref["bwd"][f])):
+        for name, got_s, want_s in (("fwd", fw[c], ref["fwd"][f]), ("bwd", bw[c], ref["bwd"][f])):
             if np.linalg.norm(want_s) == 0:
-                assert np.abs(got_s).max() == 0
+                assert np.abs(got_s).max() == 0, (name, c)
             else:
-                assert rel_l2(got_s, want_s) <= tol, c
+                check(f"{name}[{c}]", got_s, want_s, tol, row_tol, d)
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
+def test_layer_parity(shape):
+    inp, ref = oracle_for(shape)
+    check_layer(shape, inp, ref)
+
+
+PEAKY = [shapes.TOY, shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT64, WIDE]
+
+
+@pytest.mark.parametrize("shape", PEAKY, ids=lambda s: s.name)
+def test_layer_parity_peaky(shape):
+    """Scores that rise several times along the key walk, the last time at the final key
+    of the walk (levels 14, 24, 34 and 44 in log2 units above the query's typical
+    score): the reference maximum moves up to four times per query."""
+    inp = synth.peaky_inputs(shape)
+    check_layer(shape, inp, oracle_of(shape, inp), states=False)
+
+
+@pytest.mark.parametrize("shape", [shapes.TOY, RAGGED128, RAGGED64, FP8_SMALL, SHORT64],
+                         ids=lambda s: s.name)
+def test_rescale_branch_runs(shape):
+    """One planted key, the last key of every walk, scores 200 (log2 units) above the
+    rest.  An exponential against a reference maximum that was never raised is 2^190 or
+    more: inf in float32, and the output NaN.  A finite output that matches the oracle
+    therefore shows that the rescale branch ran, and ran correctly."""
+    inp = synth.peaky_inputs(shape, last_level=200.0)
+    check_layer(shape, inp, oracle_of(shape, inp), states=False)
 
 
 @pytest.mark.parametrize("shape", SMALL + [shapes.P768, shapes.LONG], ids=lambda s: s.name)
@@ -192,6 +228,32 @@ def test_runs_on_a_side_stream():
     assert rel_l2(_np(dl.out), ref["out"]) <= TOL["f32"]
 
 
+def test_side_stream_with_the_default_workspace():
+    """Workspace left to the binding on a side stream: the binding's block must stay
+    reserved for that stream's kernels even though the call returns at once.  A block of
+    the same size taken and overwritten on the current stream right after the call must
+    not be the workspace."""
+    shape = shapes.MID
+    inp, _ = oracle_for(shape)
+    dl = runner.upload(inp)
+    dl.run()
+    torch.cuda.synchronize()
+    want = dl.out.clone()
+    dl.out.fill_(float("nan"))
+    nbytes = binding.workspace_bytes(dl.cfg)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        binding.hybrid_attn_fwd(dl.q, dl.k, dl.v, dl.text_kv, dl.gates, dl.rms_weight, dl.w_out, dl.residual,
+                                dl.out, dl.cfg, stream=s)
+        junk = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xFF)
+        del junk
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(dl.out, want)
+
+
 def test_768p_sampled_parity():
     """The 768p layer in the bench's launch configuration, checked against the oracle on
     sampled query tokens: o_soft and u on 8 heads for tokens of 13 frames (anchors, chunk
@@ -219,9 +281,10 @@ def test_768p_sampled_parity():
     print("768p: oracle softmax rows done", flush=True)
     u_ref = oracle.layer.linear_branch(q, k, v, tk, tv, F, C, rows=rows)
     del q, k, v
-    e_o, e_u = rel_l2(o_gpu, o_ref), rel_l2(u_gpu, u_ref)
-    print(f"768p sampled rel-L2: o_soft {e_o:.2e} u {e_u:.2e}", flush=True)
-    assert e_o <= TOL["bf16"] and e_u <= TOL["bf16"]
+    rep = {}
+    check("o_soft", o_gpu, o_ref, TOL["bf16"], ROW_TOL["bf16"], shape.head_dim, rep)
+    check("u", u_gpu, u_ref, TOL["bf16"], ROW_TOL["bf16"], shape.head_dim, rep)
+    print("768p sampled", fmt(rep), flush=True)
 
     # y on all heads for a few tokens
     yrows = np.array([0 * T + 3, 5 * T + 100, 5 * T + 900, 30 * T + 500, 59 * T + 7, 57 * T + 1000])
@@ -235,9 +298,9 @@ def test_768p_sampled_parity():
     x = f(inp.x)[yrows]
     y_ref = oracle.layer.project(a_s, a_l, f(inp.w_s), f(inp.w_l), x) - x
     y_gpu = _np(dl.out.index_select(0, torch.from_numpy(yrows).cuda())) - x
-    e_y = rel_l2(y_gpu, y_ref)
-    print(f"768p sampled rel-L2: y {e_y:.2e}", flush=True)
-    assert e_y <= TOL["bf16"]
+    rep = {}
+    check("y", y_gpu, y_ref, TOL["bf16"], ROW_TOL["bf16"], shape.dmodel, rep)
+    print("768p sampled", fmt(rep), flush=True)
 
 
 def test_long_fp8_sampled_parity():
@@ -263,6 +326,7 @@ def test_long_fp8_sampled_parity():
     ql, kl, vl = (np.ascontiguousarray(a[:, heads]) for a in inp.linear_qkv_values())
     u_ref = oracle.layer.linear_branch(ql, kl, vl, tk, tv, F, C, rows=rows)
     del ql, kl, vl
-    e_o, e_u = rel_l2(o_gpu, o_ref), rel_l2(u_gpu, u_ref)
-    print(f"long fp8 sampled rel-L2: o_soft {e_o:.2e} u {e_u:.2e}", flush=True)
-    assert e_o <= TOL["fp8"] and e_u <= TOL["fp8"]
+    rep = {}
+    check("o_soft", o_gpu, o_ref, TOL["fp8"], ROW_TOL["fp8"], shape.head_dim, rep)
+    check("u", u_gpu, u_ref, TOL["fp8"], ROW_TOL["fp8"], shape.head_dim, rep)
+    print("long fp8 sampled", fmt(rep), flush=True)

@@ -55,3 +55,40 @@ def test_membership_probe_inputs():
     frame = torch.arange(s.tokens) // s.tokens_per_frame
     assert torch.equal(p.v[:, 0, :].float().argmax(-1), frame)
     assert float(p.text_v[:, :, s.frames].float().min()) == 1.0
+
+
+def _log2_scores(inp, n, h):
+    """log2-domain scaled scores d^-1/2 log2(e) q_n.k_j of query n against its key set,
+    split into (text and first video frame of the set, the rest)."""
+    import oracle
+
+    s = inp.shape
+    F, T, C, R, d = s.frames, s.tokens_per_frame, s.chunk_frames, s.neighbor_chunks, s.head_dim
+    q, k, _ = inp.qkv_values()
+    frames = oracle.sets.softmax_frames(n // T, F, C, R)
+    c2 = d ** -0.5 * np.log2(np.e)
+    early_keys = np.concatenate([synth.f64(inp.text_k)[:, h], k[frames[0] * T:(frames[0] + 1) * T, h]])
+    late_keys = np.concatenate([k[g * T:(g + 1) * T, h] for g in frames[1:]])
+    return c2 * early_keys @ q[n, h], c2 * late_keys @ q[n, h]
+
+
+def test_peaky_inputs_peak_late():
+    """Every sampled query's largest score lies past its text keys and its first video
+    frame, more than 8 (log2 units) above all of those; with last_level = 200 the gap
+    exceeds 128, so exponentials against any early reference overflow float32."""
+    from video_diffusion_hybrid_sparse_amd.shapes import LayerShape
+
+    shape = LayerShape("peaky_f12_t40_c3_h2_d128_bf16", frames=12, tokens_per_frame=40, heads=2, head_dim=128,
+                       text_len=16, chunk_frames=3, model_dim=64, seed=3)
+    for last, gap in ((44.0, 8.0), (200.0, 128.0)):
+        inp = synth.peaky_inputs(shape, last_level=last)
+        for n in range(0, shape.tokens, 7):
+            for h in range(shape.heads):
+                early, late = _log2_scores(inp, n, h)
+                assert late.max() - early.max() > gap, (last, n, h)
+    # the chunk plants alone already rise above the first keys
+    inp = synth.peaky_inputs(shape, last_level=0.0)
+    T = shape.tokens_per_frame
+    n = 4 * T + 3  # chunk 1: window chunks 0..2, plants in frames 2, 5, 8
+    early, late = _log2_scores(inp, n, 0)
+    assert late.max() - early.max() > 8.0

@@ -166,6 +166,26 @@ def _expect(t: Optional[torch.Tensor], name: str, shape: tuple, dtypes: tuple) -
 _TORCH = {F32: (torch.float32,), BF16: (torch.bfloat16,), FP8_E4M3: (torch.uint8, torch.float8_e4m3fn)}
 
 
+def _torch_stream(stream, device):
+    """(torch stream object, raw hipStream_t handle) for `stream`: None = torch's current
+    stream, a torch stream as is, a raw handle (int) wrapped as an external stream."""
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    elif not hasattr(stream, "cuda_stream"):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return stream, stream.cuda_stream
+
+
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace the library call on `stream` owns until that stream's work ends: torch's
+    caching allocator would otherwise hand the block to new work on the current stream as
+    soon as this function returns, while the kernels still use it."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
+
+
 def hybrid_attn_fwd(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg: Cfg, qkv_lin=None,
                     o_soft_dbg=None, u_lin_dbg=None, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Enqueue one layer forward on `stream` (default: torch's current stream).
@@ -188,11 +208,9 @@ def hybrid_attn_fwd(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, c
     _expect(qkv_lin, "qkv_lin", (3, N, H, d), ad)
     _expect(o_soft_dbg, "o_soft_dbg", (N, H, d), (torch.float32,))
     _expect(u_lin_dbg, "u_lin_dbg", (N, H, d), (torch.float32,))
+    stream, handle = _torch_stream(stream, q.device)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        workspace = _scratch(workspace_bytes(cfg), q.device, stream)
     _check(lib().vdn_hybrid_attn_fwd(
         _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None, _ptr(gates, "gates"),
         _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(residual, "residual"), _ptr(out, "out"),
@@ -230,11 +248,9 @@ def hybrid_attn_fwd_train(q, k, v, text_kv, gates, rms_weight, w_out, residual, 
     _expect(out, "out", (N, D), ad)
     if saved.numel() < saved_bytes(cfg):
         raise ValueError("saved is smaller than saved_bytes(cfg)")
+    stream, handle = _torch_stream(stream, q.device)
     if workspace is None:
-        workspace = torch.empty(workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        workspace = _scratch(workspace_bytes(cfg), q.device, stream)
     _check(lib().vdn_hybrid_attn_fwd_train(
         _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None, _ptr(gates, "gates"),
         _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(residual, "residual"), _ptr(out, "out"),
@@ -267,11 +283,9 @@ def hybrid_attn_bwd(q, k, v, text_kv, gates, rms_weight, w_out, dout, cfg: Cfg, 
     _expect(dgates, "dgates", (2, N, H, d), f32)
     _expect(drms_weight, "drms_weight", (H, d), f32)
     _expect(dw_out, "dw_out", (D, 2 * H * d), f32)
+    stream, handle = _torch_stream(stream, q.device)
     if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        workspace = _scratch(bwd_workspace_bytes(cfg), q.device, stream)
     if saved is not None:
         if saved.numel() < saved_bytes(cfg):
             raise ValueError("saved is smaller than saved_bytes(cfg)")

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -167,6 +168,15 @@ void bwd_layout_of(const vdn_hybrid_cfg* c, BwdLayout* B) {
   B->dw_part = off; off = align_up(off + ((N + 63) / 64) * H * d * 4);
   B->total = off;
 }
+
+// ---- membership export buffer ----------------------------------------------------------
+// F*F codes for F <= kMaxMembershipFrames, held by the library on every device it runs on
+// (1 MiB), so the export allocates nothing.  Host code uses the address that
+// hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr int kMaxMembershipFrames = 1024;
+__device__ __align__(256) int8_t g_membership_codes[kMaxMembershipFrames * kMaxMembershipFrames];
+std::mutex g_membership_mu;
+std::map<int, int8_t*> g_membership_ptr;
 
 // ---- profiling ----------------------------------------------------------------------
 constexpr int kProfSlots = 4096;
@@ -389,12 +399,23 @@ vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_h
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
   const Geo g = make_geo(cfg);
+  if (g.F > kMaxMembershipFrames)
+    return fail(VDN_ERR_UNSUPPORTED, "membership export holds at most %d frames (got %d)", kMaxMembershipFrames, g.F);
   const size_t bytes = (size_t)g.F * g.F;
-  int8_t* dev = nullptr;
-  if (hipMalloc(&dev, bytes) != hipSuccess) return fail(VDN_ERR_HIP, "hipMalloc of %zu bytes failed", bytes);
-  hipError_t e = launch_membership(g, dev, nullptr);
-  if (e == hipSuccess) e = hipMemcpy(codes_host, dev, bytes, hipMemcpyDeviceToHost);
-  hipFree(dev);
+  // one call at a time per process: the device buffer is shared
+  std::lock_guard<std::mutex> lock(g_membership_mu);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(VDN_ERR_NO_DEVICE, "hipGetDevice failed");
+  int8_t*& buf = g_membership_ptr[dev];
+  if (!buf) {
+    const hipError_t se = hipGetSymbolAddress(reinterpret_cast<void**>(&buf), HIP_SYMBOL(g_membership_codes));
+    if (se != hipSuccess) {
+      buf = nullptr;
+      return fail(VDN_ERR_HIP, "hipGetSymbolAddress of the membership buffer: %s", hipGetErrorString(se));
+    }
+  }
+  hipError_t e = launch_membership(g, buf, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(codes_host, buf, bytes, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(VDN_ERR_HIP, "membership kernel: %s", hipGetErrorString(e));
   return VDN_OK;
 }

@@ -122,7 +122,24 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.double().numpy()
 
 
-def make_inputs(shape: LayerShape, seed: Optional[int] = None) -> LayerInputs:
+def _store_qkv(shape: LayerShape, qkv: dict) -> dict:
+    """Round float32 q/k/v arrays to the softmax branch's storage type (fp8: per-tensor
+    e4m3 codes of the bf16-rounded tensor, whose bf16 values also feed the linear branch)."""
+    kw = {}
+    if shape.qkv_dtype == "fp8":
+        lin = {n: _round(a, "bf16") for n, a in qkv.items()}
+        for n in ("q", "k", "v"):
+            kw[n], kw[n + "_scale"] = quantize_e4m3(lin[n])
+        kw.update(q_lin=lin["q"], k_lin=lin["k"], v_lin=lin["v"])
+    else:
+        for n in ("q", "k", "v"):
+            kw[n] = _round(qkv[n], shape.qkv_dtype)
+    return kw
+
+
+def make_inputs(shape: LayerShape, seed: Optional[int] = None, edit_qkv=None) -> LayerInputs:
+    """Seeded inputs of `shape` (module recipe).  edit_qkv, if given, may change the float32
+    q/k/v arrays (dict of [N,H,d]) in place before they are rounded to storage."""
     seed = shape.seed if seed is None else seed
     N, H, d, L, D = shape.tokens, shape.heads, shape.head_dim, shape.text_len, shape.dmodel
     act = shape.act_dtype
@@ -147,21 +164,52 @@ def make_inputs(shape: LayerShape, seed: Optional[int] = None) -> LayerInputs:
     wl = draw("w_l", D, H * d) * np.float32((H * d) ** -0.5)
     x = draw("x", N, D)
 
-    kw = {}
-    if shape.qkv_dtype == "fp8":
-        lin = {n: _round(a, "bf16") for n, a in qkv.items()}
-        for n in ("q", "k", "v"):
-            kw[n], kw[n + "_scale"] = quantize_e4m3(lin[n])
-        kw.update(q_lin=lin["q"], k_lin=lin["k"], v_lin=lin["v"])
-    else:
-        for n in ("q", "k", "v"):
-            kw[n] = _round(qkv[n], shape.qkv_dtype)
+    if edit_qkv is not None:
+        edit_qkv(qkv)
+    kw = _store_qkv(shape, qkv)
     return LayerInputs(
         shape=shape,
         text_k=_round(tk, act), text_v=_round(tv, act),
         g_s=_round(g_s, act), g_l=_round(g_l, act),
         w_rms=torch.from_numpy(w_rms.astype(np.float32)),
         w_s=_round(ws, act), w_l=_round(wl, act), x=_round(x, act), **kw)
+
+
+def peaky_inputs(shape: LayerShape, levels=(14.0, 24.0, 34.0), last_level: float = 44.0,
+                 q_shift: float = 1.0, seed: Optional[int] = None) -> LayerInputs:
+    """Inputs whose softmax scores peak late in each query's key walk.
+
+    The seeded inputs of `shape`, with two changes made before rounding:
+      * every query channel is shifted by q_shift, so all queries share a component
+        along the all-ones direction;
+      * planted key rows are constant in every channel: token T // 2 of the last frame of
+        chunk c (when that frame is not an anchor) and token T - 1 of the last frame
+        F - 1.  A constant row c_k has q.k = c_k * sum(q); its level is set so that
+        d^-1/2 log2(e) q.k is about `levels[c % len(levels)]` (chunk plants) or
+        `last_level` (the last frame's plant) in log2 units, i.e. c_k = level /
+        (q_shift sqrt(d) log2 e).
+    Random keys then score about sqrt(q_shift^2 + 1) log2 e in log2 units (one standard
+    deviation), so each plant lies well above the maximum of the first keys a query
+    meets, and a window that covers chunks c-1, c, c+1 meets rising plants: a
+    flash-softmax kernel has to raise its reference maximum several times, the last time
+    at the final key of the walk.  With last_level beyond 128, an exponential taken
+    against a reference that was never raised overflows float32.
+    """
+    F, T, C, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.head_dim
+    unit = q_shift * float(np.sqrt(d)) * float(np.log2(np.e))
+    plants = []
+    for c in range(shape.n_chunks):
+        f = min(F - 1, c * C + C - 1)
+        if f not in (0, F - 1):
+            plants.append((f * T + T // 2, levels[c % len(levels)]))
+    plants.append(((F - 1) * T + T - 1, last_level))
+
+    def edit(qkv):
+        qkv["q"] += np.float32(q_shift)
+        for tok, level in plants:
+            qkv["k"][tok] = np.float32(level / unit)
+
+    return make_inputs(shape, seed, edit_qkv=edit)
 
 
 def upstream_grad(shape: LayerShape, seed: Optional[int] = None) -> torch.Tensor:

@@ -38,6 +38,16 @@ def pairs_per_head(s: LayerShape) -> int:
     return sum(k * s.tokens_per_frame for k in keys_per_frame(s))
 
 
+def softmax_mixed_peak(s: LayerShape, peak_fp8: float, peak_bf16: float) -> float:
+    """Ceiling of the softmax branch when q.k of the video keys runs at the fp8 rate and
+    q.k of the text keys and every p.v run at the bf16 rate (the e4m3 workload's kernel):
+    4 d FLOPs per pair over the time the three parts take at their peaks."""
+    pairs = pairs_per_head(s)
+    text = s.text_len * s.tokens
+    t = (pairs - text) / peak_fp8 + text / peak_bf16 + pairs / peak_bf16  # each part 2 d FLOPs per pair
+    return 2 * pairs / t
+
+
 def flops(s: LayerShape) -> dict:
     H, d, T, L, N, D, F = s.heads, s.head_dim, s.tokens_per_frame, s.text_len, s.tokens, s.dmodel, s.frames
     if s.linear_variant == 1:
