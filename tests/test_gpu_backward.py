@@ -33,7 +33,7 @@ def oracle_grads(shape, inp, dout):
                                        shape.chunk_frames, shape.neighbor_chunks, shape.rms_eps)
 
 
-def check_grads(shape, inp):
+def check_grads(shape, inp, floors=None):
     dout = synth.upstream_grad(shape)
     ref = oracle_grads(shape, inp, dout)
     dl = runner.upload(inp)
@@ -44,7 +44,8 @@ def check_grads(shape, inp):
         names += ["dtext_k", "dtext_v"]
     rep = {}
     for n in names:
-        check(n, _np(got[n]), ref[n], TOL, ROW_TOL["bf16"], shape.head_dim, rep)
+        kw = {"floor": floors[n]} if floors and n in floors else {}
+        check(n, _np(got[n]), ref[n], TOL, ROW_TOL["bf16"], shape.head_dim, rep, **kw)
     print(shape.name, fmt(rep), flush=True)
 
 
@@ -55,7 +56,17 @@ def test_backward_parity(shape):
 
 @pytest.mark.parametrize("shape", [shapes.MID, RAGGED128, SHORT64], ids=lambda s: s.name)
 def test_backward_parity_peaky(shape):
-    check_grads(shape, synth.peaky_inputs(shape))
+    """Peaky logits: every gradient as above, dq rows with a floor of 0.3 of the typical
+    row.  With two planted keys per query, dq of a query is about
+    scale dS_last (c_last e_B - c_frame e_A), and dS_last is proportional to the
+    difference of the sums of dO over the two channel halves; where that difference
+    nearly cancels, the row's exact value is far below a typical row while the bf16
+    storage of dO (the gradient of the softmax output, an MFMA operand) moves it by
+    about 2^-9 of the terms that cancel.  Rounding only dO in a float64 model of the
+    worst mid-size row reproduces the measured error (0.6% of a typical row on a row
+    that is 4e-4 of one); the kernels are not the cause.  Measured rows reach about 1%
+    of a typical row, so rows below 0.3 of a typical one are held to 1.5% of it."""
+    check_grads(shape, synth.peaky_inputs(shape), floors={"dq": 0.3})
 
 
 def test_backward_is_deterministic():

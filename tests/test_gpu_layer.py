@@ -9,8 +9,8 @@ state row, the row rel-L2 (tests/parity.py).  Index sets are bit-exact everywher
 
 Peaky-logit cases (synth.peaky_inputs) put the largest scores of every query late in
 its key walk, so the softmax kernels must raise their reference maximum, rescale the
-partial output and redo the exponentials of the block; with a planted score 200 (log2
-units) above the rest, an exponential against the unraised reference overflows float32,
+partial output and redo the exponentials of the block; with a planted score at least 128
+(log2 units) above the rest, an exponential against the unraised reference overflows float32,
 so a finite, matching result shows that the rescale ran.
 
 The 768p and 120-frame fp8 layers are compared on sampled tokens.
@@ -22,7 +22,7 @@ import torch
 import oracle
 from video_diffusion_hybrid_sparse_amd import binding, runner, shapes, synth
 
-from .parity import ROW_TOL, check, fmt, rel_l2
+from .parity import ROW_TOL, check, fmt, rel_l2, half_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -113,8 +113,8 @@ def check_layer(shape, inp, ref, states=True):
     rep = {}
     for key in ("o_soft", "u", "a_s", "a_l"):
         check(key, got[key], want[key], tol, row_tol, d, rep)
-    for key in ("y", "out"):
-        check(key, got[key], want[key], tol, row_tol, D, rep)
+    check("y", got["y"], want["y"], tol, row_tol, D, rep, slack=half_ulp(got["out"], shape.act_dtype))
+    check("out", got["out"], want["out"], tol, row_tol, D, rep)
     print(shape.name, fmt(rep), flush=True)
     if not states:
         return
@@ -150,8 +150,10 @@ PEAKY = [shapes.TOY, shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT
 @pytest.mark.parametrize("shape", PEAKY, ids=lambda s: s.name)
 def test_layer_parity_peaky(shape):
     """Scores that rise several times along the key walk, the last time at the final key
-    of the walk (levels 14, 24, 34 and 44 in log2 units above the query's typical
-    score): the reference maximum moves up to four times per query."""
+    of the walk (whole frames at levels 14, 23 and 32 in log2 units above the query's
+    typical score, then one key at 41): the reference maximum moves up to four times
+    per query, and the two halves of the output carry the weights of the frame plants
+    and of the last plant, which the rescaling sets."""
     inp = synth.peaky_inputs(shape)
     check_layer(shape, inp, oracle_of(shape, inp), states=False)
 
@@ -159,11 +161,12 @@ def test_layer_parity_peaky(shape):
 @pytest.mark.parametrize("shape", [shapes.TOY, RAGGED128, RAGGED64, FP8_SMALL, SHORT64],
                          ids=lambda s: s.name)
 def test_rescale_branch_runs(shape):
-    """One planted key, the last key of every walk, scores 200 (log2 units) above the
-    rest.  An exponential against a reference maximum that was never raised is 2^190 or
-    more: inf in float32, and the output NaN.  A finite output that matches the oracle
-    therefore shows that the rescale branch ran, and ran correctly."""
-    inp = synth.peaky_inputs(shape, last_level=200.0)
+    """One planted key, the last key of every walk, scores about 400 (log2 units; at
+    least 128 above everything before it for every query, tests/test_synth.py) above
+    the rest.  An exponential against a reference maximum that was never raised is then
+    2^128 or more: inf in float32, and the output NaN.  A finite output that matches the
+    oracle therefore shows that the rescale branch ran, and ran correctly."""
+    inp = synth.peaky_inputs(shape, last_level=400.0)
     check_layer(shape, inp, oracle_of(shape, inp), states=False)
 
 
@@ -299,7 +302,8 @@ def test_768p_sampled_parity():
     y_ref = oracle.layer.project(a_s, a_l, f(inp.w_s), f(inp.w_l), x) - x
     y_gpu = _np(dl.out.index_select(0, torch.from_numpy(yrows).cuda())) - x
     rep = {}
-    check("y", y_gpu, y_ref, TOL["bf16"], ROW_TOL["bf16"], shape.dmodel, rep)
+    check("y", y_gpu, y_ref, TOL["bf16"], ROW_TOL["bf16"], shape.dmodel, rep,
+          slack=half_ulp(y_gpu + x, "bf16"))
     print("768p sampled", fmt(rep), flush=True)
 
 

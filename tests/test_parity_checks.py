@@ -65,3 +65,38 @@ def test_non_finite_fails():
     got[0, 0, 0] = np.nan
     with pytest.raises(AssertionError, match="non-finite"):
         check("o", got, ref, 1.5e-2, ROW_TOL["bf16"], D)
+
+
+def test_half_ulp_bounds_bf16_rounding():
+    import torch
+
+    from .parity import half_ulp
+
+    g = np.random.default_rng(1)
+    v = g.standard_normal(200000) * np.exp(g.uniform(-20, 20, 200000))
+    stored = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    assert (np.abs(stored - v) <= half_ulp(stored, "bf16")).all()
+    assert half_ulp(np.array([1.0, 1.99, 2.0, -0.75]), "bf16").tolist() == [2 ** -8, 2 ** -8, 2 ** -7, 2 ** -9]
+
+
+def test_small_sum_on_a_large_residual():
+    """y = out - x with out = bf16(x + y): y of order 1e-2 on x of order 1 keeps only a few
+    bits, so y rows pass only with the storage slack; a wrong y row still fails."""
+    import torch
+
+    from .parity import half_ulp
+
+    g = np.random.default_rng(2)
+    n, D = 400, 64
+    x = torch.from_numpy(g.standard_normal((n, D))).to(torch.bfloat16).double().numpy()
+    y_ref = 0.02 * g.standard_normal((n, D))
+    y_dev = y_ref * (1 + g.uniform(-1e-3, 1e-3, y_ref.shape))  # a kernel's small error
+    out = torch.from_numpy(x + y_dev).to(torch.bfloat16).double().numpy()
+    y = out - x
+    with pytest.raises(AssertionError, match="row"):
+        check("y", y, y_ref, 1.5e-1, ROW_TOL["bf16"], D)  # storage rounding alone fails rows
+    check("y", y, y_ref, 1.5e-1, ROW_TOL["bf16"], D, slack=half_ulp(out, "bf16"))
+    bad = out.copy()
+    bad[7] = torch.from_numpy(x[7] - y_dev[7]).to(torch.bfloat16).double().numpy()  # y of row 7 negated
+    with pytest.raises(AssertionError, match="row 7"):
+        check("y", bad - x, y_ref, 1.5e-1, ROW_TOL["bf16"], D, slack=half_ulp(bad, "bf16"))

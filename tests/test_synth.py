@@ -74,18 +74,19 @@ def _log2_scores(inp, n, h):
 
 def test_peaky_inputs_peak_late():
     """Every sampled query's largest score lies past its text keys and its first video
-    frame, more than 8 (log2 units) above all of those; with last_level = 200 the gap
+    frame, more than 8 (log2 units) above all of those; with last_level = 400 the gap
     exceeds 128, so exponentials against any early reference overflow float32."""
     from video_diffusion_hybrid_sparse_amd.shapes import LayerShape
 
     shape = LayerShape("peaky_f12_t40_c3_h2_d128_bf16", frames=12, tokens_per_frame=40, heads=2, head_dim=128,
                        text_len=16, chunk_frames=3, model_dim=64, seed=3)
-    for last, gap in ((44.0, 8.0), (200.0, 128.0)):
-        inp = synth.peaky_inputs(shape, last_level=last)
-        for n in range(0, shape.tokens, 7):
-            for h in range(shape.heads):
-                early, late = _log2_scores(inp, n, h)
-                assert late.max() - early.max() > gap, (last, n, h)
+    for sh in (shape, shape.with_(name="peaky_d64", head_dim=64, seed=4)):
+        for last, gap in ((41.0, 8.0), (400.0, 128.0)):
+            inp = synth.peaky_inputs(sh, last_level=last)
+            for n in range(0, sh.tokens, 7):
+                for h in range(sh.heads):
+                    early, late = _log2_scores(inp, n, h)
+                    assert late.max() - early.max() > gap, (sh.head_dim, last, n, h)
     # the chunk plants alone already rise above the first keys
     inp = synth.peaky_inputs(shape, last_level=0.0)
     T = shape.tokens_per_frame

@@ -122,7 +122,7 @@ void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
 // backward's intermediates.
 struct BwdLayout {
   vdn_workspace_layout fwd;
-  size_t o, u, lse, delta, dacat, dO, du, G, dS, dTx, dw_part, total;
+  size_t o, u, lse, delta, dacat, dO, du, qs, G, dS, dTx, dw_part, total;
 };
 
 vdn_status check_bwd_cfg(const vdn_hybrid_cfg* c) {
@@ -162,6 +162,7 @@ void bwd_layout_of(const vdn_hybrid_cfg* c, BwdLayout* B) {
   B->dacat = off; off = align_up(off + 2 * nhd * 4);
   B->dO = off; off = align_up(off + nhd * 2);
   B->du = off; off = align_up(off + nhd * 2);
+  B->qs = off; off = align_up(off + nhd * 2);
   B->G = off; off = align_up(off + ng * st);
   B->dS = off; off = align_up(off + nC * st);
   B->dTx = off; off = align_up(off + st);
@@ -350,8 +351,11 @@ static vdn_status bwd_impl(const void* q, const void* k, const void* v, const vo
   EpiBwdArgs ea{dacat, gs, gl, O, U, rms_weight, dO, du, dgates, dgates + nhd, delta, dw_part, drms_weight, g,
                 cfg->rms_eps};
   VDN_LAUNCH("epilogue backward", launch_epi_bwd(ea, stream));
-  // softmax branch: dq, dk, dv, text (stored)
-  SoftmaxBwdArgs sb{qb, kb, vb, tk, tv, dO, lse, delta, dq, dk, dv, dtk, dtv, g, c2, scale};
+  // softmax branch: dq, dk, dv, text (stored), with the forward's score operand bf16(c2 q)
+  __bf16* qs = reinterpret_cast<__bf16*>(ws + B.qs);
+  VDN_LAUNCH("query prescale", launch_prescale_q(qb, qs, (int64_t)nhd, c2, stream));
+  SoftmaxBwdArgs sb{qb, kb, vb, tk, tv, dO, lse, delta, dq, dk, dv, dtk, dtv, g, c2, scale, qs,
+                    1.0f / 1.4426950408889634f};
   VDN_LAUNCH("softmax backward", launch_softmax_bwd(sb, stream));
   // linear branch (accumulated)
   BuildArgs<__bf16> ga{qb, du, tk, tv, G, nullptr, g, 1};

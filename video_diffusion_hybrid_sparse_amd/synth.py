@@ -175,39 +175,54 @@ def make_inputs(shape: LayerShape, seed: Optional[int] = None, edit_qkv=None) ->
         w_s=_round(ws, act), w_l=_round(wl, act), x=_round(x, act), **kw)
 
 
-def peaky_inputs(shape: LayerShape, levels=(14.0, 24.0, 34.0), last_level: float = 44.0,
+def peaky_inputs(shape: LayerShape, levels=(14.0, 23.0, 32.0), last_level: float = 41.0,
                  q_shift: float = 1.0, seed: Optional[int] = None) -> LayerInputs:
     """Inputs whose softmax scores peak late in each query's key walk.
 
-    The seeded inputs of `shape`, with two changes made before rounding:
-      * every query channel is shifted by q_shift, so all queries share a component
-        along the all-ones direction;
-      * planted key rows are constant in every channel: token T // 2 of the last frame of
-        chunk c (when that frame is not an anchor) and token T - 1 of the last frame
-        F - 1.  A constant row c_k has q.k = c_k * sum(q); its level is set so that
-        d^-1/2 log2(e) q.k is about `levels[c % len(levels)]` (chunk plants) or
-        `last_level` (the last frame's plant) in log2 units, i.e. c_k = level /
-        (q_shift sqrt(d) log2 e).
-    Random keys then score about sqrt(q_shift^2 + 1) log2 e in log2 units (one standard
-    deviation), so each plant lies well above the maximum of the first keys a query
-    meets, and a window that covers chunks c-1, c, c+1 meets rising plants: a
-    flash-softmax kernel has to raise its reference maximum several times, the last time
-    at the final key of the walk.  With last_level beyond 128, an exponential taken
-    against a reference that was never raised overflows float32.
+    The seeded inputs of `shape`, with these changes made before rounding (A = the first
+    half of the head_dim channels, B = the second half):
+      * every query channel is shifted by q_shift, so every query has a large positive
+        sum over A and over B;
+      * frame plants: every token of the last frame of chunk c (when that frame is not
+        an anchor) gets the key row c_k on A and 0 on B, at level
+        `levels[c % len(levels)]`, and the value row 1 on A, 0 on B;
+      * the last plant: token T - 1 of the last frame F - 1 gets the key row c_k on B
+        and 0 on A, at `last_level`, and the value row 0 on A, 1 on B.
+    A level is the target of d^-1/2 log2(e) q.k in log2 units; with q.k = c_k times the
+    sum of q over one half (about q_shift d / 2), c_k = 2 level / (q_shift sqrt(d) log2 e).
+    Unit-variance random keys score about sqrt(q_shift^2 + 1) log2(e) (one standard
+    deviation), so each plant lies well above the first keys a query meets, and a window
+    over chunks c-1, c, c+1 meets rising plants: a flash-softmax kernel has to raise its
+    reference maximum several times, the last time at the final key of the walk.  With
+    the default levels the last plant is about 9 above the highest frame plant, so the T
+    keys of that frame keep a share of about T 2^-9 of its weight; the output's A and B
+    halves measure the two weights separately, and the key directions of the two kinds
+    of plant are orthogonal, so no result is a small difference of large terms.  With
+    last_level beyond 128, an exponential taken against a reference that was never
+    raised overflows float32.
     """
     F, T, C, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.head_dim
-    unit = q_shift * float(np.sqrt(d)) * float(np.log2(np.e))
-    plants = []
+    half = d // 2
+    unit = q_shift * float(np.sqrt(d)) * float(np.log2(np.e)) / 2.0
+    frame_plants = []
     for c in range(shape.n_chunks):
         f = min(F - 1, c * C + C - 1)
         if f not in (0, F - 1):
-            plants.append((f * T + T // 2, levels[c % len(levels)]))
-    plants.append(((F - 1) * T + T - 1, last_level))
+            frame_plants.append((f, levels[c % len(levels)]))
+    last = (F - 1) * T + T - 1
 
     def edit(qkv):
         qkv["q"] += np.float32(q_shift)
-        for tok, level in plants:
-            qkv["k"][tok] = np.float32(level / unit)
+        for f, level in frame_plants:
+            rows = slice(f * T, (f + 1) * T)
+            qkv["k"][rows, :, :half] = np.float32(level / unit)
+            qkv["k"][rows, :, half:] = 0.0
+            qkv["v"][rows, :, :half] = 1.0
+            qkv["v"][rows, :, half:] = 0.0
+        qkv["k"][last, :, :half] = 0.0
+        qkv["k"][last, :, half:] = np.float32(last_level / unit)
+        qkv["v"][last, :, :half] = 0.0
+        qkv["v"][last, :, half:] = 1.0
 
     return make_inputs(shape, seed, edit_qkv=edit)
 
