@@ -157,6 +157,23 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
                                float* o_soft_dbg, float* u_lin_dbg,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The layer's last step alone: out = residual + a_cat w_out^T, i.e. both output
+ * projections added into the residual stream (the article's section
+ * "独立门控，融合两条注意力分支"), on the library's hand-written bf16 GEMM.
+ *
+ *   a_cat     [n_tokens, k] bf16: per token the gated softmax output (heads concatenated)
+ *             followed by the gated linear output (k = 2*H*d); the layout of the
+ *             workspace's branch_out.
+ *   w_out     [model_dim, k] bf16: W_s then W_l per output row, as for the forward.
+ *   residual, out  [n_tokens, model_dim] bf16; may alias.
+ * Needs model_dim % 4 == 0, k a positive multiple of 128 and each operand below 4 GiB
+ * (VDN_ERR_UNSUPPORTED otherwise).  float32 accumulation, one bf16 rounding of the sum.
+ * Enqueued on `stream`; allocates nothing.
+ */
+vdn_status vdn_hybrid_attn_projection(const void* a_cat, const void* w_out, const void* residual, void* out,
+                                      int64_t n_tokens, int64_t model_dim, int64_t k, void* stream);
+
 /* Workspace of one vdn_hybrid_attn_bwd call, or 0 if cfg is invalid or the backward is not
  * built for it (then vdn_last_error() says why). */
 size_t vdn_hybrid_attn_bwd_workspace_bytes(const vdn_hybrid_cfg* cfg);

@@ -262,3 +262,17 @@ def test_training_record_entry_points():
         assert L.vdn_hybrid_attn_bwd_saved(*good[:8], None, ctypes.byref(cfg), *grads, 0x200000, bws, None) == INVALID
         assert L.vdn_hybrid_attn_bwd_saved(*good[:8], 0x300000, ctypes.byref(cfg), *grads, 0x200000, bws,
                                            None) == NO_DEVICE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check: fake pointers must never reach a GPU")
+def test_projection_argument_checks_launch_nothing():
+    L = binding.lib()
+    a, w, x, o = 0x10000, 0x20000, 0x30000, 0x40000
+    assert L.vdn_hybrid_attn_projection(a, w, x, o, 300, 512, 1024, None) == NO_DEVICE
+    assert L.vdn_hybrid_attn_projection(a, w, x, o, 0, 512, 1024, None) == OK  # nothing to do
+    assert L.vdn_hybrid_attn_projection(a, w, x, o, 300, 510, 1024, None) == UNSUPPORTED  # model_dim % 4
+    assert L.vdn_hybrid_attn_projection(a, w, x, o, 300, 512, 1000, None) == UNSUPPORTED  # k % 128
+    assert L.vdn_hybrid_attn_projection(a, w, x, o, 1 << 21, 512, 1024, None) == UNSUPPORTED  # a over 4 GiB
+    assert L.vdn_hybrid_attn_projection(None, w, x, o, 300, 512, 1024, None) == INVALID
+    assert L.vdn_hybrid_attn_projection(a, w + 8, x, o, 300, 512, 1024, None) == INVALID
+    assert L.vdn_hybrid_attn_projection(a, w, x, o, -1, 512, 1024, None) == INVALID

@@ -26,7 +26,7 @@ EXPORTS = ("vdn_hybrid_attn_workspace_bytes", "vdn_hybrid_attn_workspace_layout"
            "vdn_hybrid_attn_bwd_workspace_bytes", "vdn_hybrid_attn_bwd",
            "vdn_hybrid_attn_saved_bytes", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
            "vdn_hybrid_attn_membership", "vdn_profile_enable", "vdn_profile_read", "vdn_last_error",
-           "vdn_mxfp8_quantize", "vdn_mxfp8_quantize_lora", "vdn_mxfp8_linear")
+           "vdn_mxfp8_quantize", "vdn_mxfp8_quantize_lora", "vdn_mxfp8_linear", "vdn_hybrid_attn_projection")
 
 
 class VdnError(RuntimeError):
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_mxfp8_quantize_lora.restype = i32
         L.vdn_mxfp8_linear.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, ctypes.POINTER(vp), vp]
         L.vdn_mxfp8_linear.restype = i32
+        L.vdn_hybrid_attn_projection.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        L.vdn_hybrid_attn_projection.restype = i32
         L.vdn_last_error.argtypes = []
         L.vdn_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -308,6 +310,21 @@ def _stream_handle(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def projection(a_cat: torch.Tensor, w_out: torch.Tensor, residual: torch.Tensor, out: torch.Tensor,
+               stream=None) -> None:
+    """Enqueue out = residual + a_cat @ w_out.T on the library's bf16 GEMM: a_cat [N, K],
+    w_out [D, K], residual and out [N, D] (bf16; out may be residual)."""
+    n, k = a_cat.shape
+    d = w_out.shape[0]
+    bf = (torch.bfloat16,)
+    _expect(a_cat, "a_cat", (n, k), bf)
+    _expect(w_out, "w_out", (d, k), bf)
+    _expect(residual, "residual", (n, d), bf)
+    _expect(out, "out", (n, d), bf)
+    _check(lib().vdn_hybrid_attn_projection(_ptr(a_cat, "a_cat"), _ptr(w_out, "w_out"), _ptr(residual, "residual"),
+                                            _ptr(out, "out"), n, d, k, _stream_handle(stream, a_cat.device)))
 
 
 def mxfp8_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, lora_b=None, lora_a=None,

@@ -12,6 +12,7 @@
 
 #include "gemm.h"
 #include "kernels.h"
+#include "proj_gemm.h"
 #include "mxfp8.h"
 #include "vdn_hybrid_attn.h"
 #include "vdn_mxfp8.h"
@@ -426,11 +427,18 @@ vdn_status vdn_hybrid_attn_membership(const vdn_hybrid_cfg* cfg, int8_t* codes_h
 
 // The forward; lse (softmax log-sum-exp, log2 domain) and acat_out (branch outputs in
 // place of the workspace's) are set only by the training forward.
+// How the forward runs its projection GEMM: the library's choice for the configuration,
+// or always the hand-written bf16 kernel (no GEMM library call, no library scratch).
+enum ProjMode { kProjDefault = 0, kProjOwn = 1 };
+
+// Whether the hand-written bf16 kernel runs the projection of a bf16 forward by default.
+constexpr bool kOwnProjectionDefault = false;
+
 static vdn_status fwd_impl(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
                            const float* rms_weight, const void* w_out, const void* residual, void* out,
                            const vdn_hybrid_cfg* cfg, const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg,
                            void* workspace, size_t workspace_bytes, void* stream_ptr, float* lse_out,
-                           void* acat_out) {
+                           void* acat_out, ProjMode proj = kProjDefault) {
   vdn_status s = check_cfg(cfg);
   if (s != VDN_OK) return s;
   const struct { const void* p; const char* name; } req[] = {
@@ -449,8 +457,17 @@ static vdn_status fwd_impl(const void* q, const void* k, const void* v, const vo
     if (opt[i] && !aligned16(opt[i])) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", optn[i]);
   vdn_workspace_layout L;
   layout_of(cfg, &L);
-  if (workspace_bytes < L.total)
-    return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, L.total);
+  const bool bf16_act = cfg->act_dtype == VDN_BF16;
+  const int64_t Nt = (int64_t)cfg->frames * cfg->tokens_per_frame, K2 = 2 * (int64_t)cfg->heads * cfg->head_dim;
+  const bool own_ok = bf16_act && proj_gemm_supported(Nt, cfg->model_dim, K2);
+  if (proj == kProjOwn && !own_ok)
+    return fail(VDN_ERR_UNSUPPORTED, "the hand-written projection GEMM needs bf16 activations and model_dim a "
+                                     "multiple of 4 (got model_dim %d)", cfg->model_dim);
+  const bool own = proj == kProjOwn || (own_ok && kOwnProjectionDefault);
+  // the hand-written GEMM needs no library scratch, which the layout puts last
+  const size_t need = own ? L.gemm_ws : L.total;
+  if (workspace_bytes < need)
+    return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
 
@@ -547,10 +564,18 @@ static vdn_status fwd_impl(const void* q, const void* k, const void* v, const vo
   }
   if (e != hipSuccess) return fail(VDN_ERR_HIP, "softmax launch: %s", hipGetErrorString(e));
   mark(4);
-  const char* gerr = nullptr;
-  if (projection_gemm(bf16, (int64_t)N, cfg->model_dim, (int64_t)(2 * row), acat, w_out, residual, out,
-                      ws + L.gemm_ws, L.gemm_ws_bytes, stream, &gerr) != 0)
-    return fail(VDN_ERR_HIP, "projection: %s", gerr);
+  if (own) {
+    ProjGemmArgs pa{static_cast<const __bf16*>(acat), static_cast<const __bf16*>(w_out),
+                    static_cast<const __bf16*>(residual), static_cast<__bf16*>(out), (int)N, cfg->model_dim,
+                    (int)(2 * row)};
+    e = launch_proj_gemm(pa, stream);
+    if (e != hipSuccess) return fail(VDN_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  } else {
+    const char* gerr = nullptr;
+    if (projection_gemm(bf16, (int64_t)N, cfg->model_dim, (int64_t)(2 * row), acat, w_out, residual, out,
+                        ws + L.gemm_ws, L.gemm_ws_bytes, stream, &gerr) != 0)
+      return fail(VDN_ERR_HIP, "projection: %s", gerr);
+  }
   mark(5);
   return VDN_OK;
 }
@@ -562,6 +587,31 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, cons
                                size_t workspace_bytes, void* stream_ptr) {
   return fwd_impl(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg, qkv_lin, o_soft_dbg, u_lin_dbg,
                   workspace, workspace_bytes, stream_ptr, nullptr, nullptr);
+}
+
+vdn_status vdn_hybrid_attn_projection(const void* a_cat, const void* w_out, const void* residual, void* out,
+                                      int64_t n_tokens, int64_t model_dim, int64_t k, void* stream) {
+  if (n_tokens < 0 || model_dim < 1 || k < 1)
+    return fail(VDN_ERR_INVALID_ARG, "need n_tokens >= 0, model_dim >= 1, k >= 1");
+  if (!proj_gemm_supported(n_tokens, model_dim, k))
+    return fail(VDN_ERR_UNSUPPORTED, "projection GEMM needs model_dim %% 4 == 0, k a positive multiple of 128 and "
+                                     "operands below 4 GiB (got %lld x %lld, k %lld)",
+                (long long)n_tokens, (long long)model_dim, (long long)k);
+  if (n_tokens == 0) return VDN_OK;
+  const struct { const void* p; const char* name; } req[] = {
+      {a_cat, "a_cat"}, {w_out, "w_out"}, {residual, "residual"}, {out, "out"}};
+  for (const auto& r : req) {
+    if (!r.p) return fail(VDN_ERR_INVALID_ARG, "%s is NULL", r.name);
+    if (!aligned16(r.p)) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", r.name);
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+  ProjGemmArgs pa{static_cast<const __bf16*>(a_cat), static_cast<const __bf16*>(w_out),
+                  static_cast<const __bf16*>(residual), static_cast<__bf16*>(out), (int)n_tokens, (int)model_dim,
+                  (int)k};
+  const hipError_t e = launch_proj_gemm(pa, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VDN_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  return VDN_OK;
 }
 
 size_t vdn_hybrid_attn_saved_bytes(const vdn_hybrid_cfg* cfg) {

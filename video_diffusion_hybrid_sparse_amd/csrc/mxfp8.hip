@@ -30,6 +30,7 @@
 // 4 row tiles by all column tiles: the 32 tiles one XCD runs at a time share 4 token
 // panels (x does not fit in the 256 MB last-level cache) and 8 weight panels in its L2.
 #include "mxfp8.h"
+#include "tile.h"
 
 namespace vdn {
 namespace {
@@ -102,21 +103,7 @@ constexpr int kGroupM = 4;                 // row tiles per tile group
 
 // Stage copies use dma16 (inline asm) so that the compiler, which cannot tell the four
 // stage buffers apart, does not wait for every copy in flight before each LDS read; the
-// waits are explicit (wait_barrier).
-
-// Wait until at most N of this wave's copies are in flight and its LDS reads are done,
-// then meet the other waves.
-template <int N>
-__device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-template <int V>
-struct IC {
-  static constexpr int value = V;
-};
-
-__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+// waits are explicit (wait_barrier, tile.h).
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_kernel(MxGemmArgs a) {
   // four stage buffers (A tile then B tile), then two scale windows (A rows then B rows)
