@@ -174,6 +174,24 @@ vdn_status vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
 vdn_status vdn_hybrid_attn_projection(const void* a_cat, const void* w_out, const void* residual, void* out,
                                       int64_t n_tokens, int64_t model_dim, int64_t k, void* stream);
 
+/*
+ * vdn_hybrid_attn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same layer
+ * and the same arguments without the workspace, which comes from a 64 MiB array that the
+ * library holds on every device it runs on until the process ends.  Configurations whose
+ * workspace (vdn_hybrid_attn_workspace_layout's gemm_ws offset: everything before the
+ * GEMM library's scratch) exceeds 64 MiB are rejected with VDN_ERR_WORKSPACE before
+ * anything is enqueued; act_dtype must be BF16 (VDN_ERR_UNSUPPORTED otherwise), as the
+ * projection runs on the library's hand-written GEMM (vdn_hybrid_attn_projection's
+ * kernel: model_dim % 4 == 0).  Calls no allocating routine.  Every call on one device
+ * uses that device's one array, so calls that overlap on one device (on different
+ * streams, or from several threads) race; nothing in it needs to start at zero.
+ */
+vdn_status vdn_hybrid_attn_fwd_noalloc(const void* q, const void* k, const void* v, const void* text_kv,
+                                       const void* gates, const float* rms_weight, const void* w_out,
+                                       const void* residual, void* out, const vdn_hybrid_cfg* cfg,
+                                       const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg, void* stream);
+
 /* Workspace of one vdn_hybrid_attn_bwd call, or 0 if cfg is invalid or the backward is not
  * built for it (then vdn_last_error() says why). */
 size_t vdn_hybrid_attn_bwd_workspace_bytes(const vdn_hybrid_cfg* cfg);

@@ -265,6 +265,33 @@ def test_training_record_entry_points():
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check: fake pointers must never reach a GPU")
+def test_noalloc_forward_checks_launch_nothing():
+    """The forward without allocation: every host check runs before the device is touched;
+    configurations whose workspace exceeds its 64 MiB array, float32 activations and
+    model widths the hand-written GEMM does not take are rejected."""
+    L = binding.lib()
+    good = [0x10000 * (i + 1) for i in range(9)]
+
+    def call(cfg, ptrs=good, lin=None):
+        return L.vdn_hybrid_attn_fwd_noalloc(*ptrs, ctypes.byref(cfg), lin, None, None, None)
+
+    mid = binding.make_cfg(shapes.MID)
+    assert call(mid) == NO_DEVICE  # every check passed
+    for i in range(9):
+        bad = list(good)
+        bad[i] = None
+        assert call(mid, bad) == INVALID, i
+    big = binding.make_cfg(shapes.P768)
+    assert call(big) == WORKSPACE
+    assert "holds" in binding.last_error()
+    assert call(binding.make_cfg(shapes.TOY)) == UNSUPPORTED  # float32 activations
+    odd = binding.make_cfg(shapes.MID)
+    odd.model_dim = 1022
+    assert call(odd) == UNSUPPORTED
+    assert "multiple of 4" in binding.last_error()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="host-only check: fake pointers must never reach a GPU")
 def test_projection_argument_checks_launch_nothing():
     L = binding.lib()
     a, w, x, o = 0x10000, 0x20000, 0x30000, 0x40000

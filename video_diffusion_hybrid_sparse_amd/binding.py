@@ -26,7 +26,8 @@ EXPORTS = ("vdn_hybrid_attn_workspace_bytes", "vdn_hybrid_attn_workspace_layout"
            "vdn_hybrid_attn_bwd_workspace_bytes", "vdn_hybrid_attn_bwd",
            "vdn_hybrid_attn_saved_bytes", "vdn_hybrid_attn_fwd_train", "vdn_hybrid_attn_bwd_saved",
            "vdn_hybrid_attn_membership", "vdn_profile_enable", "vdn_profile_read", "vdn_last_error",
-           "vdn_mxfp8_quantize", "vdn_mxfp8_quantize_lora", "vdn_mxfp8_linear", "vdn_hybrid_attn_projection")
+           "vdn_mxfp8_quantize", "vdn_mxfp8_quantize_lora", "vdn_mxfp8_linear", "vdn_hybrid_attn_projection",
+           "vdn_hybrid_attn_fwd_noalloc")
 
 
 class VdnError(RuntimeError):
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.vdn_mxfp8_quantize_lora.restype = i32
         L.vdn_mxfp8_linear.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int32, ctypes.POINTER(vp), vp]
         L.vdn_mxfp8_linear.restype = i32
+        L.vdn_hybrid_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Cfg), vp, vp,
+                                                  vp, vp]
+        L.vdn_hybrid_attn_fwd_noalloc.restype = i32
         L.vdn_hybrid_attn_projection.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
         L.vdn_hybrid_attn_projection.restype = i32
         L.vdn_last_error.argtypes = []
@@ -218,6 +222,31 @@ def hybrid_attn_fwd(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, c
         _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(residual, "residual"), _ptr(out, "out"),
         ctypes.byref(cfg), _ptr(qkv_lin, "qkv_lin"), _ptr(o_soft_dbg, "o_soft_dbg"), _ptr(u_lin_dbg, "u_lin_dbg"),
         _ptr(workspace, "workspace"), workspace.numel(), handle))
+
+
+def hybrid_attn_fwd_noalloc(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg: Cfg, qkv_lin=None,
+                            o_soft_dbg=None, u_lin_dbg=None, stream=None) -> None:
+    """Enqueue hybrid_attn_fwd's layer with no workspace: the library's own per-device
+    scratch array serves instead (configurations that fit it, bf16 activations).  Calls
+    that overlap on one device race on that array."""
+    N, H, d, L, D = cfg.frames * cfg.tokens_per_frame, cfg.heads, cfg.head_dim, cfg.text_len, cfg.model_dim
+    qd, ad = _TORCH[cfg.qkv_dtype], _TORCH[cfg.act_dtype]
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, n, (N, H, d), qd)
+    _expect(text_kv, "text_kv", (2, L, H, d), ad)
+    _expect(gates, "gates", (2, N, H, d), ad)
+    _expect(rms_weight, "rms_weight", (H, d), (torch.float32,))
+    _expect(w_out, "w_out", (D, 2 * H * d), ad)
+    _expect(residual, "residual", (N, D), ad)
+    _expect(out, "out", (N, D), ad)
+    _expect(qkv_lin, "qkv_lin", (3, N, H, d), ad)
+    _expect(o_soft_dbg, "o_soft_dbg", (N, H, d), (torch.float32,))
+    _expect(u_lin_dbg, "u_lin_dbg", (N, H, d), (torch.float32,))
+    _check(lib().vdn_hybrid_attn_fwd_noalloc(
+        _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(text_kv, "text_kv") if L > 0 else None, _ptr(gates, "gates"),
+        _ptr(rms_weight, "rms_weight"), _ptr(w_out, "w_out"), _ptr(residual, "residual"), _ptr(out, "out"),
+        ctypes.byref(cfg), _ptr(qkv_lin, "qkv_lin"), _ptr(o_soft_dbg, "o_soft_dbg"), _ptr(u_lin_dbg, "u_lin_dbg"),
+        _stream_handle(stream, q.device)))
 
 
 def bwd_workspace_bytes(cfg: Cfg) -> int:

@@ -180,6 +180,16 @@ __device__ __align__(256) int8_t g_membership_codes[kMaxMembershipFrames * kMaxM
 std::mutex g_membership_mu;
 std::map<int, int8_t*> g_membership_ptr;
 
+// ---- scratch of the forward that allocates nothing -----------------------------------
+// vdn_hybrid_attn_fwd_noalloc carves its workspace out of this array: kNoAllocScratchBytes
+// held on every device the library runs on until the process ends.  Host code uses the
+// address hipGetSymbolAddress returns for the current device (taken once per device, on
+// the entry point's first call there), never the array's name.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
 // ---- profiling ----------------------------------------------------------------------
 constexpr int kProfSlots = 4096;
 struct Prof {
@@ -434,16 +444,44 @@ enum ProjMode { kProjDefault = 0, kProjOwn = 1 };
 // Whether the hand-written bf16 kernel runs the projection of a bf16 forward by default.
 constexpr bool kOwnProjectionDefault = false;
 
+// The library's scratch array for the forward without allocation on the current device
+// (its address taken once per device, with that device current).
+static vdn_status noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(VDN_ERR_NO_DEVICE, "no HIP device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return VDN_OK;
+  }
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(VDN_ERR_HIP, "hipGetSymbolAddress of the scratch array: %s", hipGetErrorString(e));
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
+  return VDN_OK;
+}
+
+// noalloc: the workspace is the library's scratch array (workspace and workspace_bytes
+// are ignored), and the projection runs on the hand-written GEMM.
 static vdn_status fwd_impl(const void* q, const void* k, const void* v, const void* text_kv, const void* gates,
                            const float* rms_weight, const void* w_out, const void* residual, void* out,
                            const vdn_hybrid_cfg* cfg, const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg,
                            void* workspace, size_t workspace_bytes, void* stream_ptr, float* lse_out,
-                           void* acat_out, ProjMode proj = kProjDefault) {
+                           void* acat_out, ProjMode proj = kProjDefault, bool noalloc = false) {
   vdn_status s = check_cfg(cfg);
   if (s != VDN_OK) return s;
+  if (noalloc) {
+    proj = kProjOwn;
+    if (cfg->act_dtype != VDN_BF16)
+      return fail(VDN_ERR_UNSUPPORTED, "the forward without allocation needs bf16 activations (its projection "
+                                       "runs on the hand-written bf16 GEMM)");
+  }
   const struct { const void* p; const char* name; } req[] = {
       {q, "q"}, {k, "k"}, {v, "v"}, {gates, "gates"}, {rms_weight, "rms_weight"}, {w_out, "w_out"},
-      {residual, "residual"}, {out, "out"}, {workspace, "workspace"}};
+      {residual, "residual"}, {out, "out"}, {noalloc ? out : workspace, "workspace"}};
   for (const auto& r : req) {
     if (!r.p) return fail(VDN_ERR_INVALID_ARG, "%s is NULL", r.name);
     if (!aligned16(r.p)) return fail(VDN_ERR_INVALID_ARG, "%s is not 16-byte aligned", r.name);
@@ -466,6 +504,15 @@ static vdn_status fwd_impl(const void* q, const void* k, const void* v, const vo
   const bool own = proj == kProjOwn || (own_ok && kOwnProjectionDefault);
   // the hand-written GEMM needs no library scratch, which the layout puts last
   const size_t need = own ? L.gemm_ws : L.total;
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes)
+      return fail(VDN_ERR_WORKSPACE, "this configuration needs %zu bytes of scratch; the forward without "
+                                     "allocation holds %zu per device (use vdn_hybrid_attn_fwd with a workspace)",
+                  need, kNoAllocScratchBytes);
+    const vdn_status ss = noalloc_scratch(&workspace);
+    if (ss != VDN_OK) return ss;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (workspace_bytes < need)
     return fail(VDN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
   int ndev = 0;
@@ -612,6 +659,14 @@ vdn_status vdn_hybrid_attn_projection(const void* a_cat, const void* w_out, cons
   const hipError_t e = launch_proj_gemm(pa, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VDN_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
   return VDN_OK;
+}
+
+vdn_status vdn_hybrid_attn_fwd_noalloc(const void* q, const void* k, const void* v, const void* text_kv,
+                                       const void* gates, const float* rms_weight, const void* w_out,
+                                       const void* residual, void* out, const vdn_hybrid_cfg* cfg,
+                                       const void* qkv_lin, float* o_soft_dbg, float* u_lin_dbg, void* stream) {
+  return fwd_impl(q, k, v, text_kv, gates, rms_weight, w_out, residual, out, cfg, qkv_lin, o_soft_dbg, u_lin_dbg,
+                  nullptr, 0, stream, nullptr, nullptr, kProjOwn, true);
 }
 
 size_t vdn_hybrid_attn_saved_bytes(const vdn_hybrid_cfg* cfg) {
