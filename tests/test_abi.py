@@ -35,11 +35,22 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(binding.Cfg) == 17 * 4
-    assert ctypes.sizeof(binding.WorkspaceLayout) == 9 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(binding.WorkspaceLayout) == 10 * ctypes.sizeof(ctypes.c_size_t)
 
 
 def _align(x):
     return (x + 255) // 256 * 256
+
+
+def _group_sizes(shape):
+    """Query tokens of each softmax query group: the two anchor frames, then each chunk
+    without them."""
+    F, T, C = shape.frames, shape.tokens_per_frame, shape.chunk_frames
+    sizes = [T, T]
+    for c in range(shape.n_chunks):
+        frames = [f for f in range(c * C, min(F, (c + 1) * C)) if f not in (0, F - 1)]
+        sizes.append(len(frames) * T)
+    return sizes
 
 
 @pytest.mark.parametrize("shape", [shapes.TOY, shapes.WORKED, shapes.MID, shapes.P768, shapes.LONG], ids=lambda s: s.name)
@@ -56,7 +67,11 @@ def test_workspace_layout(shape):
     assert L.branch_out == _align(L.bwd_states + shape.n_chunks * st)
     assert L.value_stage == _align(L.branch_out + N * 2 * H * d * ab)
     stage = (N + shape.text_len) * H * d * 2 if shape.qkv_dtype == "fp8" else 0
-    assert L.gemm_ws == _align(L.value_stage + stage)
+    assert L.tile_flags == _align(L.value_stage + stage)
+    # bf16: one int per (256-query tile, wave) of every head, for the softmax's second pass
+    tiles = sum(-(-n // 256) for n in _group_sizes(shape))
+    flags = 4 * tiles * H * 4 if shape.qkv_dtype == "bf16" else 0
+    assert L.gemm_ws == _align(L.tile_flags + flags)
     assert L.total == _align(L.gemm_ws + L.gemm_ws_bytes) == binding.workspace_bytes(cfg)
 
 

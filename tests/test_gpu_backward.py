@@ -69,6 +69,13 @@ def test_backward_parity_peaky(shape):
     check_grads(shape, synth.peaky_inputs(shape), floors={"dq": 0.3})
 
 
+@pytest.mark.parametrize("shape", [RAGGED128, SHORT64], ids=lambda s: s.name)
+def test_backward_parity_peaky_high(shape):
+    """Plants high enough that the recomputed forward's softmax goes through its second
+    pass (see the forward test of the same inputs)."""
+    check_grads(shape, synth.peaky_inputs(shape, levels=(64.0, 73.0, 82.0), last_level=91.0), floors={"dq": 0.3})
+
+
 def test_backward_is_deterministic():
     shape = RAGGED128
     inp = synth.make_inputs(shape)

@@ -158,6 +158,18 @@ def test_layer_parity_peaky(shape):
     check_layer(shape, inp, oracle_of(shape, inp), states=False)
 
 
+@pytest.mark.parametrize("shape", [shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT64],
+                         ids=lambda s: s.name)
+def test_layer_parity_peaky_high(shape):
+    """The same plants 50 log2 units higher (64, 73, 82, then 91): far enough above every
+    query's first keys that the bf16 kernel's first pass, which keeps the reference its
+    first keys set, flags every tile and its second pass recomputes them with the
+    reference raised along the walk (four times per query); the mixture of the frame
+    plants and the last plant still checks each rescaling."""
+    inp = synth.peaky_inputs(shape, levels=(64.0, 73.0, 82.0), last_level=91.0)
+    check_layer(shape, inp, oracle_of(shape, inp), states=False)
+
+
 @pytest.mark.parametrize("shape", [shapes.TOY, RAGGED128, RAGGED64, FP8_SMALL, SHORT64],
                          ids=lambda s: s.name)
 def test_rescale_branch_runs(shape):

@@ -115,6 +115,8 @@ void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
   const size_t L_txt = c->text_len;
   L->value_stage = off;
   if (c->qkv_dtype == VDN_FP8_E4M3) off = align_up(off + (N + L_txt) * H * d * 2);
+  L->tile_flags = off;
+  if (c->qkv_dtype == VDN_BF16) off = align_up(off + (size_t)softmax_bf16_flag_count(make_geo(c)) * 4);
   L->gemm_ws = off; L->gemm_ws_bytes = kGemmWs; off = align_up(off + kGemmWs);
   L->total = off;
 }
@@ -123,7 +125,7 @@ void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
 // backward's intermediates.
 struct BwdLayout {
   vdn_workspace_layout fwd;
-  size_t o, u, lse, delta, dacat, dO, du, qs, G, dS, dTx, dw_part, total;
+  size_t o, u, lse, delta, dacat, dO, du, G, dS, dTx, dw_part, total;
 };
 
 vdn_status check_bwd_cfg(const vdn_hybrid_cfg* c) {
@@ -163,7 +165,6 @@ void bwd_layout_of(const vdn_hybrid_cfg* c, BwdLayout* B) {
   B->dacat = off; off = align_up(off + 2 * nhd * 4);
   B->dO = off; off = align_up(off + nhd * 2);
   B->du = off; off = align_up(off + nhd * 2);
-  B->qs = off; off = align_up(off + nhd * 2);
   B->G = off; off = align_up(off + ng * st);
   B->dS = off; off = align_up(off + nC * st);
   B->dTx = off; off = align_up(off + st);
@@ -344,7 +345,8 @@ static vdn_status bwd_impl(const void* q, const void* k, const void* v, const vo
   if (!saved) {
     ReadoutArgs<__bf16> ra{qb, Sf, Sb, St, gl, rms_weight, acat, U, g, cfg->rms_eps, 0};
     VDN_LAUNCH("linear read", launch_readout_bf16(ra, stream));
-    SoftmaxArgs sm{q, k, vb, tk, tv, gs, acat, O, g, c2, c2, 1.0f, lse};
+    SoftmaxArgs sm{q, k, vb, tk, tv, gs, acat, O, g, c2, c2, 1.0f, lse,
+                   reinterpret_cast<int*>(ws + L.tile_flags)};
     VDN_LAUNCH("softmax", launch_softmax_bf16(sm, stream));
   }
 
@@ -362,11 +364,8 @@ static vdn_status bwd_impl(const void* q, const void* k, const void* v, const vo
   EpiBwdArgs ea{dacat, gs, gl, O, U, rms_weight, dO, du, dgates, dgates + nhd, delta, dw_part, drms_weight, g,
                 cfg->rms_eps};
   VDN_LAUNCH("epilogue backward", launch_epi_bwd(ea, stream));
-  // softmax branch: dq, dk, dv, text (stored), with the forward's score operand bf16(c2 q)
-  __bf16* qs = reinterpret_cast<__bf16*>(ws + B.qs);
-  VDN_LAUNCH("query prescale", launch_prescale_q(qb, qs, (int64_t)nhd, c2, stream));
-  SoftmaxBwdArgs sb{qb, kb, vb, tk, tv, dO, lse, delta, dq, dk, dv, dtk, dtv, g, c2, scale, qs,
-                    1.0f / 1.4426950408889634f};
+  // softmax branch: dq, dk, dv, text (stored)
+  SoftmaxBwdArgs sb{qb, kb, vb, tk, tv, dO, lse, delta, dq, dk, dv, dtk, dtv, g, c2, scale};
   VDN_LAUNCH("softmax backward", launch_softmax_bwd(sb, stream));
   // linear branch (accumulated)
   BuildArgs<__bf16> ga{qb, du, tk, tv, G, nullptr, g, 1};
@@ -598,11 +597,12 @@ static vdn_status fwd_impl(const void* q, const void* k, const void* v, const vo
     e = launch_dequant_values(da, stream);
     if (e != hipSuccess) return fail(VDN_ERR_HIP, "value staging launch: %s", hipGetErrorString(e));
     SoftmaxArgs sm{q, k, vst, (const __bf16*)tk, tvst, (const __bf16*)gs, (__bf16*)acat, o_soft_dbg, g,
-                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale, nullptr};
+                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale, nullptr, nullptr};
     e = launch_softmax_fp8(sm, stream);
   } else if (bf16) {
     SoftmaxArgs sm{q, k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv, (const __bf16*)gs, (__bf16*)acat,
-                   o_soft_dbg, g, c2, c2, 1.0f, lse_out};
+                   o_soft_dbg, g, c2, c2, 1.0f, lse_out,
+                   reinterpret_cast<int*>(ws + L.tile_flags)};
     e = launch_softmax_bf16(sm, stream);
   } else {
     SoftmaxF32Args sm{(const float*)q, (const float*)k, (const float*)v, (const float*)tk, (const float*)tv,

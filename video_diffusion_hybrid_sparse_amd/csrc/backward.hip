@@ -285,34 +285,10 @@ __global__ __launch_bounds__(256) void token_state_kernel(TokenStateArgs<X> a) {
   }
 }
 
-// ---- 3. softmax backward: the forward's score operand ----------------------------------
-// The forward multiplies q by c2 = scale log2(e) and rounds it to bf16 before its score
-// MFMAs, so its probabilities are those of the scores bf16(c2 q).k.  The backward forms
-// its scores from the same operand (written here once per call), so that its P matches
-// the forward's log-sum-exp and output exactly up to the forward's bf16 P: with the
-// exact scores instead, P and the forward's Delta = dO.o disagree by the rounding of q,
-// which shows in the gradient of a key that holds most of a query's weight.
-__global__ __launch_bounds__(256) void prescale_q_kernel(const __bf16* q, __bf16* qs, int64_t n, float c2) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= n) return;
-  const bf16x8 x = load_bf16x8(q + i);
-  bf16x8 y;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * c2);
-  *reinterpret_cast<uint4*>(qs + i) = __builtin_bit_cast(uint4, y);
-}
-
-hipError_t launch_prescale_q(const __bf16* q, __bf16* qs, int64_t n, float c2, hipStream_t stream) {
-  const int64_t units = n / 8;
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(prescale_q_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream, q, qs, n, c2);
-  return hipGetLastError();
-}
-
 // ---- 3a. softmax backward, dQ -----------------------------------------------------------
 // Query tiles as in the forward (256 queries of one group and head, 8 waves x 32, two
-// waves per SIMD).  Per 64-key stage (K and V rows double-buffered in LDS): S^T = K Qs^T
-// and dP^T = V dO^T (K and V rows are MFMA A operands); P^T = exp2(S^T - lse),
+// waves per SIMD).  Per 64-key stage (K and V rows double-buffered in LDS): S^T = K Q^T
+// and dP^T = V dO^T (K and V rows are MFMA A operands); P^T = exp2(S^T c2 - lse),
 // dS^T = P^T (dP^T - Delta) (the query is lane-local); dQ^T += K^T dS^T with K^T gathered
 // by the transposing LDS read.  dq = scale dQ.  The stage loop is unrolled over the two
 // buffers, so every LDS read is a per-lane base plus an immediate offset; keys past a
@@ -356,7 +332,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   qtok = qok ? qtok : t1 - 1;
   bf16x8 qreg[KS], doreg[KS];
   {
-    const __bf16* qp = a.qs + (size_t)qtok * rs + h * D + half * 8;
+    const __bf16* qp = a.q + (size_t)qtok * rs + h * D + half * 8;
     const __bf16* dp = a.dO + (size_t)qtok * rs + h * D + half * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -428,6 +404,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   f32x16 dq[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) dq[i] = 0.0f;
+  const float c2 = a.c2;
 
   auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
@@ -466,7 +443,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         float ds2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[rt][r + e] - lse);
+          const float p = __builtin_amdgcn_exp2f(s[rt][r + e] * c2 - lse);
           ds2[e] = p * (dp[rt][r + e] - delta);
         }
         uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
@@ -516,10 +493,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // operands, key lane-local) and its dK^T and dV^T accumulators (64 keys x D each) in the
 // matrix registers.  Queries stream through LDS in 64-query stages (double-buffered),
 // with their log-sum-exp and Delta; each stage runs as two 32-query halves.  Per half:
-// S = Qs K^T and dP = dO V^T (Qs = bf16(c2 q) and dO rows from LDS are the A operands,
-// each feeding both 32-key sub-tiles); P = exp2(S - lse), dS = P (dP - Delta);
-// dV^T += dO^T P and dK^T += Qs^T dS (dO^T and Qs^T by the transposing LDS read, each
-// feeding both sub-tiles), dk = dK / log2(e).
+// S = Q K^T and dP = dO V^T (Q and dO rows from LDS are the A operands, each feeding both
+// 32-key sub-tiles); P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and
+// dK^T += Q^T dS (dO^T and Q^T by the transposing LDS read, each feeding both sub-tiles).
 // Per (query, key) pair 8 d multiply-adds against 10 d for separate dV and dK passes,
 // and every LDS operand read feeds two MFMAs.  The stage loop is unrolled over the two
 // buffers and the halves, so every LDS read is one per-lane base register plus an
@@ -644,7 +620,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < NI; ++i) {
       const int lrow = (wave * NI + i) * RPI + lane / CPR;
       const uint32_t off = (uint32_t)imin(lrow, valid - 1) * rs2 + (uint32_t)((lane % CPR) ^ swz<CPR>(lrow)) * 16;
-      dma16(a.qs + base, off, m0q + (uint32_t)buf * (2 * TB) + i * RPI * D * 2);
+      dma16(a.q + base, off, m0q + (uint32_t)buf * (2 * TB) + i * RPI * D * 2);
       dma16(a.dO + base, off, m0q + (uint32_t)buf * (2 * TB) + TB + i * RPI * D * 2);
     }
   };
@@ -690,6 +666,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
     asm volatile("s_nop 1" : "+a"(dv[dt][0]), "+a"(dv[dt][1]), "+a"(dk[dt][0]), "+a"(dk[dt][1]));
+  const float c2 = a.c2;
 
   // one 32-query half RT of the stage in buffer BUF (`valid` queries in the stage)
   auto half_body = [&](auto bufc, auto rtc, int valid) __attribute__((always_inline)) {
@@ -734,7 +711,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          p[e] = __builtin_amdgcn_exp2f(s[t][r] - lq[e]);
+          p[e] = __builtin_amdgcn_exp2f(s[t][r] * c2 - lq[e]);
           ds[e] = p[e] * (dp[t][r] - dq4[e]);
         }
         uint4 wp = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
@@ -809,8 +786,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 32 * dt + 8 * i + 4 * half;
-        *reinterpret_cast<float4*>(pk + c) = make_float4(a.kscale * dk[dt][t][4 * i], a.kscale * dk[dt][t][4 * i + 1],
-                                                         a.kscale * dk[dt][t][4 * i + 2], a.kscale * dk[dt][t][4 * i + 3]);
+        *reinterpret_cast<float4*>(pk + c) = make_float4(a.scale * dk[dt][t][4 * i], a.scale * dk[dt][t][4 * i + 1],
+                                                         a.scale * dk[dt][t][4 * i + 2], a.scale * dk[dt][t][4 * i + 3]);
         *reinterpret_cast<float4*>(pv + c) =
             make_float4(dv[dt][t][4 * i], dv[dt][t][4 * i + 1], dv[dt][t][4 * i + 2], dv[dt][t][4 * i + 3]);
       }

@@ -147,7 +147,10 @@ __host__ __device__ inline int count_tiles(const Geo& g, int bm) {
 
 // ---- device helpers ---------------------------------------------------------------
 
-__device__ inline float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// The gates' sigmoid, with the hardware reciprocal (within one ulp of 1 / y; a correctly
+// rounded division would cost a dozen instructions per element in the epilogues, whose
+// results are rounded to bf16).  A large negative x gives 1 / inf = 0.
+__device__ inline float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ inline f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -24,8 +24,13 @@ struct SoftmaxArgs {
   float c2_text, c2_video;
   float out_scale;
   float* lse;    // nullable [N,H]: m + log2(l), the log2-domain log-sum-exp of each query's
-                 // scaled scores (the backward rebuilds P = exp2(bf16(c2 q).k - lse))
+                 // scaled scores (the backward rebuilds P = exp2(c2 q.k - lse))
+  int* flags;    // bf16 kernel: softmax_bf16_flag_count(geo) ints of scratch, one per
+                 // (query tile, wave): written by the first pass, read by the second
 };
+
+// Ints of scratch the bf16 softmax needs for its tile flags.
+int softmax_bf16_flag_count(const Geo& g);
 
 // fp8 value staging: vout[n] = bf16(code value of v8[n]) for the video values and
 // tvout[n] = bf16(tv[n] / v_scale) for the text values.
@@ -158,15 +163,7 @@ struct SoftmaxBwdArgs {
   float* dtv;
   Geo geo;
   float c2, scale;     // scale * log2(e), scale
-  // the forward's score operand bf16(c2 q) [N,H,d] (prescale_q): scores are qs.k in log2
-  // units, as in the forward; dq = scale dS k, dk = kscale dS qs with kscale = 1 / log2(e)
-  const __bf16* qs;
-  float kscale;
 };
-
-// qs[i] = bf16(float(q[i]) * c2) for i < n (n a multiple of 8): the softmax forward's
-// score operand, written out for the backward.
-hipError_t launch_prescale_q(const __bf16* q, __bf16* qs, int64_t n, float c2, hipStream_t stream);
 
 hipError_t launch_epi_bwd(const EpiBwdArgs& a, hipStream_t stream);
 hipError_t launch_lin_mix(const float* G, float* dS, float* dTx, const Geo& g, hipStream_t stream);

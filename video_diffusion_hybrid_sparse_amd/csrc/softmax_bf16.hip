@@ -27,9 +27,13 @@
 // matrix cores).
 //
 // bf16 inputs (softmax_sw_kernel): four waves, 64 queries each, one wave per SIMD, with
-// the matrix and vector work of each wave software-pipelined (see the kernel).  Q^T is
-// pre-multiplied by c2 = scale log2 e (one extra bf16 rounding of q) and every score
-// accumulator starts at -m, so the MFMA hands the exponent c2 s - m straight to v_exp.
+// the matrix and vector work of each wave software-pipelined (see the kernel).  The
+// scores are q.k of the bf16 inputs summed in float32, and each exponent is one fused
+// multiply-add, c2 s - m with c2 = scale log2 e.  (Pre-multiplying q by c2 in bf16
+// instead would round q once more: about 1e-3 of a score, a 6% error in the weights of
+// scores near 90 in log2 units.)  The bf16 kernel runs twice: the first pass keeps the
+// reference its first keys set and flags the tiles whose row sums show a later score
+// far above it; the second pass redoes only those, raising the reference as it goes.
 //
 // fp8 inputs (softmax_fp8_kernel): eight waves, 32 queries each, two per SIMD, 128-key
 // stages double-buffered.  Video keys stay e4m3 in LDS and S^T uses
@@ -364,13 +368,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // ---- bf16 inputs: software-pipelined kernel, one wave per SIMD --------------------------
 // Four waves, each owning two blocks of 32 queries, so that every K and V operand read
 // from LDS feeds two MFMAs.  Keys advance in 32-key sub-tiles.  The work on sub-tile t+1
-// is one block: a single stream of 32 MFMAs (O += V^T P_t^T, then S_{t+2} = K Q^T - m)
-// with the vector work of sub-tile t+1 between them (its row maxima beside the P V
-// MFMAs, P_{t+1} = 2^{S_{t+1}} and its row sums beside the score MFMAs), one MFMA per
-// slot so that the matrix cores and the VALU of the wave run side by side.  The
-// exponentials are taken before the maxima are checked; in the rare block whose maximum
-// exceeds m by more than 8, m moves at the end of the block and that block's
-// exponentials are redone.  Operand reads from LDS run LA operands ahead of their MFMAs.
+// is one block: a single stream of 32 MFMAs (O += V^T P_t^T, then S_{t+2} = K Q^T)
+// with the vector work of sub-tile t+1 between them (in the second pass its row maxima
+// beside the P V MFMAs; P_{t+1} = 2^{c2 S_{t+1} - m} and its row sums beside the score
+// MFMAs), one MFMA per slot so that the matrix cores and the VALU of the wave run side by
+// side.  First pass (SAFE = false): m is the maximum of the first sub-tile and never
+// moves; at the end a wave whose row sum is not below 2^60 (so some exponent reached
+// 2^60 or overflowed) flags its tile.  Second pass (SAFE = true, flagged tiles only): the
+// exponentials are taken before the maxima are checked; in the block whose maximum exceeds
+// m by more than 8, m moves at the end of the block and that block's exponentials are
+// redone.  Operand reads from LDS run LA operands ahead of their MFMAs.
 //
 // Key and value stages hold 64 keys, four LDS buffers deep.  One barrier per stage: after
 // it, stage j + 3 is copied into the buffer of stage j - 1 (every wave is done with it),
@@ -396,6 +403,10 @@ namespace {
 __device__ __forceinline__ void mfma_qk(f32x16& d, const bf16x8& k, const bf16x8& q) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
 }
+// the first k-step of a sub-tile's scores: accumulator input 0 (d's old value is not read)
+__device__ __forceinline__ void mfma_qk0(f32x16& d, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "+v"(d) : "v"(k), "a"(q));
+}
 __device__ __forceinline__ void mfma_pv(f32x16& d, const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(v), "v"(p));
 }
@@ -407,7 +418,7 @@ __device__ __forceinline__ void mfma_sum(f32x4& d, const bf16x8& a, const bf16x8
 }
 }  // namespace
 
-template <int D>
+template <int D, bool SAFE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_sw_kernel(SoftmaxArgs a) {
   constexpr int QB = 2, NW = 4, BM = 256;
   constexpr int BN = 64, BC = 32, NBUF = 4;  // keys per stage, keys per sub-tile, stage buffers
@@ -433,6 +444,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int h = lid / per_head;
   int grp, t0, t1;
   if (!locate_tile(g, lid - h * per_head, BM, grp, t0, t1)) return;
+  if constexpr (SAFE) {
+    // the second pass redoes only the tiles the first pass flagged
+    const int4 f = *reinterpret_cast<const int4*>(a.flags + 4 * (size_t)lid);
+    if ((f.x | f.y | f.z | f.w) == 0) return;
+  }
   const KeyWalk<BN> kw(g.L, group_keys(g, grp));
   const int nst = kw.stages();
 
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   int qtok[QB];
   bool qok[QB];
-  bf16x8 qreg[QB][KS];  // Q^T pre-multiplied by c2 = scale log2 e, kept in AGPRs
+  bf16x8 qreg[QB][KS];  // Q^T as given (bf16), kept in AGPRs
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int t = t0 + (wave * QB + qb) * 32 + l32;
@@ -450,9 +466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const __bf16* qp = static_cast<const __bf16*>(a.q) + (size_t)qtok[qb] * rs + h * D + half * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      const bf16x8 raw = load_bf16x8(qp + 16 * k);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[qb][k][e] = (__bf16)((float)raw[e] * a.c2_text);
+      qreg[qb][k] = load_bf16x8(qp + 16 * k);
       asm volatile("" : "+a"(qreg[qb][k]));
     }
   }
@@ -494,7 +508,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     c.kb = (text ? k_text : k_video) + base;
     c.vb = (text ? v_text : v_video) + base;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) c.off[i] = (uint32_t)imin(lrow[i], valid - 1) * rs2 + loff[i];
+    // (24-bit products: the row is below 64 and the row stride H d 2 below 2^24)
+    for (int i = 0; i < NI; ++i) c.off[i] = __umul24((uint32_t)imin(lrow[i], valid - 1), rs2) + loff[i];
     c.m0k = lds_k + (uint32_t)buf * (BN * D * 2);
     c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
     return c;
@@ -559,13 +574,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // formed by the matrix cores over the same bf16 P that multiplies V (AGPRs)
   f32x16 o[QB][DT];
   f32x4 lsum[QB];
-  float m[QB];
+  float m[QB], nm[QB];  // the reference and its negative (the exponent is fma(s, c2, -m))
+  const float c2 = a.c2_text;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qb][dt] = 0.0f;
     lsum[qb] = 0.0f;
     m[qb] = 0.0f;
+    nm[qb] = 0.0f;
   }
   // Row-sum selector for the 16x16x32 MFMA.  P^T as its B operand: lane l holds 8 keys of
   // query l % 32, so lane groups 0 and 2 (lanes j, j + 32) hold the 16 keys of query j and
@@ -604,7 +621,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // exponential pair u = (qb, u % 8) of s into pb (bf16)
   auto expo_unit = [&](const f32x16 (&s)[QB], bf16x8 (&pb)[QB][2], int u) __attribute__((always_inline)) {
     const int qb = u / 8, r = 2 * (u % 8);
-    const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(s[qb][r]), __builtin_amdgcn_exp2f(s[qb][r + 1]));
+    const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, nm[qb])),
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r + 1], c2, nm[qb])));
     uint4 w = __builtin_bit_cast(uint4, pb[qb][r >> 3]);
     const int e = (r & 7) >> 1;
     if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
@@ -651,11 +669,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float mx[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
-    if constexpr (NEXT_S && NMP < 2) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sn[qb] = -m[qb];
-      asm volatile("s_nop 1" : "+v"(sn[0]), "+v"(sn[1]));  // VALU write, then MFMA read
-    }
 
     // (one v_max3 per pair: fmaxf would first quiet each operand, the scores come out of asm)
     auto max_item = [&](int u) __attribute__((always_inline)) {
@@ -677,20 +690,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // scores: operand n = NOPV + k of the stream
         const int k = (sl - NMP) / QB, n = NOPV + k;
         if (qb == 0) fetch(n + LA);
-        mfma_qk(sn[qb], op[n], qreg[qb][k]);
+        if (k == 0) mfma_qk0(sn[qb], op[n], qreg[qb][k]);
+        else mfma_qk(sn[qb], op[n], qreg[qb][k]);
       }
-      if (sl == 0) fence_s(sc);
-      // the next scores start at -m: their accumulators (the registers of the sub-tile
-      // before the current one, done with) are filled by the VALU two slots before the
-      // first score MFMA reads them (a block without P V fills them before its first slot)
-      if constexpr (NEXT_S && NMP >= 2) {
-        if (sl == NMP - 2) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sn[qb] = -m[qb];
-          // (all sixteen moves here: else the compiler sinks copies to just before the MFMA)
-          asm volatile("" : "+v"(sn[0]), "+v"(sn[1]));
-        }
-      }
+      // the second pass reads the current scores (their maxima) from the first slot on;
+      // the first pass reads them only beside the score MFMAs, after this block's P V
+      // MFMAs (asm_check verifies the wait states either way)
+      if (SAFE && sl == 0) fence_s(sc);
       if constexpr (CP != 0) {
         constexpr int GAP = NMF / NI;  // MFMA slots per copy instruction
         if (sl % GAP == GAP / 2) {
@@ -702,16 +708,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // read of P); a block without one of the two spreads both kinds over its MFMAs
       if constexpr (NMP > 0 && NMP < NMF) {
         if (sl < NMP) {
+          if constexpr (SAFE) {
 #pragma unroll
-          for (int it = sl * NIT / NMP; it < (sl + 1) * NIT / NMP; ++it) max_item(it);
+            for (int it = sl * NIT / NMP; it < (sl + 1) * NIT / NMP; ++it) max_item(it);
+          }
         } else {
 #pragma unroll
           for (int it = (sl - NMP) * NIT / (NMF - NMP); it < (sl - NMP + 1) * NIT / (NMF - NMP); ++it)
             expo_unit(sc, pc, it);
         }
       } else {
+        if constexpr (SAFE) {
 #pragma unroll
-        for (int it = sl * NIT / NMF; it < (sl + 1) * NIT / NMF; ++it) max_item(it);
+          for (int it = sl * NIT / NMF; it < (sl + 1) * NIT / NMF; ++it) max_item(it);
+        }
         if (NMP == 0 || sl == NMF - 1) {
           // no P V to wait for (NMP == 0), or the last P V issued: the exponentials
 #pragma unroll
@@ -730,15 +740,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     bool up = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) up |= mx[qb] > 8.0f;
-    if (__builtin_expect(__any(up), 0)) {  // rare: keep it out of the block's straight line
+    for (int qb = 0; qb < QB; ++qb) up |= __builtin_fmaf(mx[qb], c2, nm[qb]) > 8.0f;
+    if (SAFE && __builtin_expect(__any(up), 0)) {  // rare: keep it out of the block's straight line
       fence_o();
-      if constexpr (NEXT_S) fence_s(sn);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float shift = fmaxf(pair_max(mx[qb]), 0.0f);
+        const float shift = fmaxf(__builtin_fmaf(pair_max(mx[qb]), c2, nm[qb]), 0.0f);
         const float alpha = __builtin_amdgcn_exp2f(-shift);
         m[qb] += shift;
+        nm[qb] = -m[qb];
         // one 16-register tile at a time through the VALU, each put back into AGPRs
         // before the next (else the compiler stages all of O in VGPRs at once)
         // lane j < 16 holds the sums of queries j and j + 16 (alpha of query q: lane q)
@@ -751,8 +761,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           o[qb][dt] *= alpha;
           asm volatile("" : "+a"(o[qb][dt]));
         }
-        sc[qb] -= shift;
-        if constexpr (NEXT_S) sn[qb] -= shift;
       }
 #pragma unroll
       for (int u = 0; u < 8 * QB; ++u) expo_unit(sc, pc, u);
@@ -804,14 +812,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * NI) : "memory");
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) S[0][qb] = 0.0f;
-  asm volatile("s_nop 1" : "+v"(S[0][0]), "+v"(S[0][1]));  // VALU write, then MFMA read
-#pragma unroll
   for (int k = 0; k < KS; ++k) {
     const bf16x8 kop = rdk(0, 0, k);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      mfma_qk(S[0][qb], kop, qreg[qb][k]);
+      if (k == 0) mfma_qk0(S[0][qb], kop, qreg[qb][k]);
+      else mfma_qk(S[0][qb], kop, qreg[qb][k]);
     }
   }
   fence_s(S[0]);
@@ -820,8 +826,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[0][qb][r]);
-    m[qb] = pair_max(mx);  // keys past a segment repeat its last key: no mask needed
-    S[0][qb] -= m[qb];
+    m[qb] = pair_max(mx) * c2;  // keys past a segment repeat its last key: no mask needed
+    nm[qb] = -m[qb];
   }
   bf16x8 va[LA], vb[LA];
   int vj = valid_of(0);
@@ -834,17 +840,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Stage j (LDS buffer B = j % 4): sub-tiles 2 j + 1 and 2 j + 2.  The main loop takes
   // four stages at a time, so that the buffers are constants; the rest go one by one.
+  // The copy of stage j + 3 (into the buffer of stage j - 1, which every wave is done with
+  // once past stage j's barrier) and the valid count of stage j + 1 are computed in the
+  // iteration before, after its blocks' MFMAs have been issued: the scalar work of picking
+  // the segment then overlaps those MFMAs instead of holding the next ones after the
+  // barrier.
+  auto pin = [&](const Copy& c, int v) __attribute__((always_inline)) {
+    asm volatile("" ::"s"(c.kb), "s"(c.vb), "s"(c.m0k), "s"(c.m0v), "s"(v));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) asm volatile("" ::"v"(c.off[i]));
+  };
+  Copy cp = prep(imin(3, nst - 1), 3);
+  int vn = valid_of(1);
   auto iter = [&](int j, int B) __attribute__((always_inline)) {
     const int B1 = (B + 1) & (NBUF - 1);
     barrier_wait();
-    // stage j + 3 into the buffer of stage j - 1, which every wave is done with
-    const Copy cp = prep(imin(j + 3, nst - 1), (B + 3) & (NBUF - 1));
-    const int vn = valid_of(j + 1);
     // P V of sub-tile 2 j; sub-tile 2 j + 1 (stage j, keys 32..63); scores of 2 j + 2
     block(T{}, T{}, T{}, CK{}, cp, B, 0, va, S[1], vj - BC, B1, 0, S[0], B, 1, vb);
     // P V of sub-tile 2 j + 1; sub-tile 2 j + 2 (stage j + 1, keys 0..31); scores of 2 j + 3
     block(T{}, T{}, T{}, CV{}, cp, B, 1, vb, S[0], vn, B1, 1, S[1], B1, 0, va);
     vj = vn;
+    // the next iteration's: stage j + 4 into buffer (B + 4) % 4 = B, valid count of j + 2
+    cp = prep(imin(j + 4, nst - 1), B);
+    vn = valid_of(j + 2);
+    pin(cp, vn);
   };
   int j = 0;
   for (; j + 4 < nst; j += 4) {
@@ -876,11 +895,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   fence_o();
 
+  bool overflow = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     // the sum of query l32: lane l32 % 16, element l32 / 16
     const float s0 = __shfl(lsum[qb][0], l32 & 15), s1 = __shfl(lsum[qb][1], l32 & 15);
     const float lq = l32 < 16 ? s0 : s1;
+    // every probability is at most the row sum: below 2^60 none overflowed (nor did O)
+    overflow |= !(lq <= 0x1p60f);
     if (a.lse && qok[qb] && half == 0) a.lse[(size_t)qtok[qb] * g.H + h] = m[qb] + __log2f(lq);
     const float inv = 1.0f / lq;
     const size_t orow = (size_t)qtok[qb] * rs + h * D;
@@ -914,18 +936,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
   }
+  if constexpr (!SAFE) {
+    // this wave's verdict for the tile (the second pass redoes flagged tiles)
+    const bool any = __any(overflow);
+    if (lane == 0) a.flags[4 * (size_t)lid + wave] = any ? 1 : 0;
+  }
 }
+
+int softmax_bf16_flag_count(const Geo& g) { return 4 * count_tiles(g, 256) * g.H; }
 
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream) {
   const int tiles = count_tiles(a.geo, 256);
   if (tiles == 0) return hipSuccess;
+  if (!a.flags) return hipErrorInvalidValue;
   dim3 grid(tiles * a.geo.H), block(256);
-  if (a.geo.d == 128)
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128>), grid, block, 0, stream, a);
-  else if (a.geo.d == 64)
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64>), grid, block, 0, stream, a);
-  else
+  // first pass: every tile against the reference its first keys set; second pass: the
+  // tiles whose row sums showed a later score far above it, with the reference raised
+  // as the walk goes
+  if (a.geo.d == 128) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128, true>), grid, block, 0, stream, a);
+  } else if (a.geo.d == 64) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64, true>), grid, block, 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
