@@ -429,6 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int RPI = 64 / CPR;              // rows one wave-wide 16-byte load covers
   constexpr int NI = BN * CPR / (64 * NW);   // loads per lane per stage (per tensor)
   constexpr int LA = 2;                      // operand reads in flight ahead of their MFMAs
+  constexpr int kExpSlot = 4;                // first MFMA slot of a first-pass block's exponentials
   constexpr int EMAX = 16 * QB / NV;         // max operations per P V slot
   constexpr int EEXP = 8 * QB / KS;          // exponential pairs per score slot
   static_assert(NI >= 1 && NW * QB * 32 == BM && NV >= LA && KS >= LA, "shape");
@@ -597,7 +598,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (!((lr == 0 && (lg & 1) == 0) || (lr == 1 && (lg & 1) == 1))) ones = bf16x8{};
   asm volatile("" : "+v"(ones));
   f32x16 S[2][QB];  // scores of two consecutive sub-tiles
-  bf16x8 P[QB][2];  // probabilities of one sub-tile (MFMA B-operand order)
+  // probabilities of two consecutive sub-tiles (MFMA B-operand order): a block reads one
+  // (P V, row sums) while its exponentials fill the other
+  bf16x8 PP[2][QB][2];
 
   auto fence_s = [&](f32x16 (&s)[QB]) __attribute__((always_inline)) {
     asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
@@ -641,18 +644,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // and the scores are shifted and pc is redone.  Keys past the end of a segment (vc < BC)
   // repeat its last key, so they leave the maxima unchanged; they are dropped from pc.
   // CP: 0 none, 1 the K rows of copy cp, 2 its V rows, spread over the MFMA slots.
-  auto block = [&](auto prev, auto next_s, auto next_v, auto cpk, const Copy& cp, int pbuf, int psub,
+  auto block = [&](auto prev, auto next_s, auto next_v, auto cpk, auto pbi, const Copy& cp, int pbuf, int psub,
                    const bf16x8 (&vin)[LA], f32x16 (&sc)[QB], int vc, int nbuf, int nsub, f32x16 (&sn)[QB],
                    int xbuf, int xsub, bf16x8 (&vout)[LA]) __attribute__((always_inline)) {
     constexpr int CP = decltype(cpk)::value;
-    bf16x8 (&pc)[QB][2] = P;
+    constexpr int PI = decltype(pbi)::value;  // P of the previous sub-tile in PP[PI]
+    bf16x8 (&P)[QB][2] = PP[PI];
+    bf16x8 (&pc)[QB][2] = PP[1 - PI];
     constexpr bool PREV = decltype(prev)::value, NEXT_S = decltype(next_s)::value;
     constexpr bool NEXT_V = decltype(next_v)::value;
     constexpr int NOPV = PREV ? NV : 0, NOP = NOPV + (NEXT_S ? KS : 0);
     constexpr int NMP = QB * (NOPV + (PREV ? 2 : 0));  // P V and row-sum MFMAs (they read P)
     constexpr int NMF = NMP + QB * (NOP - NOPV);      // MFMAs
     constexpr int NIT = 8 * QB;            // items of each kind: maxima of pairs, exponential pairs
-    static_assert(NMF > 0, "a block issues MFMAs");
+    // first slot of the exponentials: the first pass has no fence before them, so they
+    // wait kExpSlot slots in a block that follows the one that computed their scores (the
+    // wait states an MFMA result needs before a VALU read; asm_check verifies them)
+    constexpr int E0 = (SAFE || !PREV) ? 0 : kExpSlot;
+    static_assert(NMF > 0 && NMF > E0, "a block issues MFMAs");
     bf16x8 op[NOP + LA];
     auto fetch = [&](int n) __attribute__((always_inline)) {
       if (n < NOPV) op[n] = rdv(pbuf, psub, n);
@@ -704,30 +713,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           else copy_v(cp, sl / GAP);
         }
       }
-      // maxima beside the P V MFMAs, exponentials beside the score MFMAs (after every
-      // read of P); a block without one of the two spreads both kinds over its MFMAs
-      if constexpr (NMP > 0 && NMP < NMF) {
-        if (sl < NMP) {
-          if constexpr (SAFE) {
+      // the vector work spread over all the block's MFMA slots (the exponentials write the
+      // other P buffer, so they need not wait for the P V MFMAs): the second pass's maxima
+      // from the first slot (after its fence), the exponentials from slot E0 on
+      if constexpr (SAFE) {
 #pragma unroll
-            for (int it = sl * NIT / NMP; it < (sl + 1) * NIT / NMP; ++it) max_item(it);
-          }
-        } else {
+        for (int it = sl * NIT / NMF; it < (sl + 1) * NIT / NMF; ++it) max_item(it);
+      }
+      if (sl >= E0) {
 #pragma unroll
-          for (int it = (sl - NMP) * NIT / (NMF - NMP); it < (sl - NMP + 1) * NIT / (NMF - NMP); ++it)
-            expo_unit(sc, pc, it);
-        }
-      } else {
-        if constexpr (SAFE) {
-#pragma unroll
-          for (int it = sl * NIT / NMF; it < (sl + 1) * NIT / NMF; ++it) max_item(it);
-        }
-        if (NMP == 0 || sl == NMF - 1) {
-          // no P V to wait for (NMP == 0), or the last P V issued: the exponentials
-#pragma unroll
-          for (int it = (NMP == 0 ? sl * NIT / NMF : 0); it < (NMP == 0 ? (sl + 1) * NIT / NMF : NIT); ++it)
-            expo_unit(sc, pc, it);
-        }
+        for (int it = (sl - E0) * NIT / (NMF - E0); it < (sl - E0 + 1) * NIT / (NMF - E0); ++it)
+          expo_unit(sc, pc, it);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -836,7 +832,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using C0 = std::integral_constant<int, 0>;
   using CK = std::integral_constant<int, 1>;
   using CV = std::integral_constant<int, 2>;
-  block(F{}, T{}, T{}, C0{}, none, 0, 0, va, S[0], vj, 0, 1, S[1], 0, 0, va);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  block(F{}, T{}, T{}, C0{}, P1{}, none, 0, 0, va, S[0], vj, 0, 1, S[1], 0, 0, va);
 
   // Stage j (LDS buffer B = j % 4): sub-tiles 2 j + 1 and 2 j + 2.  The main loop takes
   // four stages at a time, so that the buffers are constants; the rest go one by one.
@@ -856,9 +854,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int B1 = (B + 1) & (NBUF - 1);
     barrier_wait();
     // P V of sub-tile 2 j; sub-tile 2 j + 1 (stage j, keys 32..63); scores of 2 j + 2
-    block(T{}, T{}, T{}, CK{}, cp, B, 0, va, S[1], vj - BC, B1, 0, S[0], B, 1, vb);
+    block(T{}, T{}, T{}, CK{}, P0{}, cp, B, 0, va, S[1], vj - BC, B1, 0, S[0], B, 1, vb);
     // P V of sub-tile 2 j + 1; sub-tile 2 j + 2 (stage j + 1, keys 0..31); scores of 2 j + 3
-    block(T{}, T{}, T{}, CV{}, cp, B, 1, vb, S[0], vn, B1, 1, S[1], B1, 0, va);
+    block(T{}, T{}, T{}, CV{}, P1{}, cp, B, 1, vb, S[0], vn, B1, 1, S[1], B1, 0, va);
     vj = vn;
     // the next iteration's: stage j + 4 into buffer (B + 4) % 4 = B, valid count of j + 2
     cp = prep(imin(j + 4, nst - 1), B);
@@ -875,7 +873,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (; j + 1 < nst; ++j) iter(j, j & (NBUF - 1));
   // last stage: P V of sub-tile 2 j; sub-tile 2 j + 1; then its P V
   const int bl = j & (NBUF - 1);
-  block(T{}, F{}, T{}, C0{}, none, bl, 0, va, S[1], vj - BC, 0, 0, S[0], bl, 1, vb);
+  block(T{}, F{}, T{}, C0{}, P0{}, none, bl, 0, va, S[1], vj - BC, 0, 0, S[0], bl, 1, vb);
   {
     bf16x8 op[NV + LA];
 #pragma unroll
@@ -884,12 +882,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < NV; ++i) {
       if (i + LA < NV) op[i + LA] = rdv(bl, 1, i + LA);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) mfma_pv(o[qb][i % DT], op[i], P[qb][i / DT]);
+      for (int qb = 0; qb < QB; ++qb) mfma_pv(o[qb][i % DT], op[i], PP[1][qb][i / DT]);
     }
 #pragma unroll
     for (int G = 0; G < 2; ++G)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) mfma_sum(lsum[qb], ones, P[qb][G]);
+      for (int qb = 0; qb < QB; ++qb) mfma_sum(lsum[qb], ones, PP[1][qb][G]);
   }
   // the repeated copies issued for stages past the last may still be landing
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
