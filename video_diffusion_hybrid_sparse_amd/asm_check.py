@@ -34,7 +34,7 @@ VALU_TO_MFMA = 2
 MFMA_TO_VALU_READ = 12
 MFMA_SRCC_TO_VALU_WRITE = 11
 # (source file under csrc/, mangled-name prefixes of its kernels written with asm MFMAs)
-TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel",)),
+TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel", "_ZN3vdn22softmax_sw_redo_kernel")),
            ("backward.hip", ("_ZN3vdn21softmax_bwd_kv_kernel",)))
 PREFIXES = tuple(p for _, ps in TARGETS for p in ps)
 # sources whose kernels write M0 in inline asm (the LDS DMA copies)

@@ -418,8 +418,9 @@ __device__ __forceinline__ void mfma_sum(f32x4& d, const bf16x8& a, const bf16x8
 }
 }  // namespace
 
+// One query tile (logical tile id lid: head, query group, 256 queries) of the bf16 kernel.
 template <int D, bool SAFE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_sw_kernel(SoftmaxArgs a) {
+__device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int lid) {
   constexpr int QB = 2, NW = 4, BM = 256;
   constexpr int BN = 64, BC = 32, NBUF = 4;  // keys per stage, keys per sub-tile, stage buffers
   constexpr int KS = D / 16;                 // MFMA k-steps over head_dim (K operands per sub-tile)
@@ -428,8 +429,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;              // rows one wave-wide 16-byte load covers
   constexpr int NI = BN * CPR / (64 * NW);   // loads per lane per stage (per tensor)
-  constexpr int LA = 2;                      // operand reads in flight ahead of their MFMAs
+  constexpr int LA = 3;                      // operand reads in flight ahead of their MFMAs
   constexpr int kExpSlot = 4;                // first MFMA slot of a first-pass block's exponentials
+  constexpr int kCopySlot = 4;               // slot (mod the copy spacing) of a block's stage copies
   constexpr int EMAX = 16 * QB / NV;         // max operations per P V slot
   constexpr int EEXP = 8 * QB / KS;          // exponential pairs per score slot
   static_assert(NI >= 1 && NW * QB * 32 == BM && NV >= LA && KS >= LA, "shape");
@@ -439,17 +441,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const Geo g = a.geo;
   const int per_head = count_tiles(g, BM);
-  const int total = per_head * g.H;
-  const int hid = blockIdx.x, xcd = hid & 7;
-  const int lid = xcd * (total >> 3) + imin(xcd, total & 7) + (hid >> 3);
   const int h = lid / per_head;
   int grp, t0, t1;
   if (!locate_tile(g, lid - h * per_head, BM, grp, t0, t1)) return;
-  if constexpr (SAFE) {
-    // the second pass redoes only the tiles the first pass flagged
-    const int4 f = *reinterpret_cast<const int4*>(a.flags + 4 * (size_t)lid);
-    if ((f.x | f.y | f.z | f.w) == 0) return;
-  }
   const KeyWalk<BN> kw(g.L, group_keys(g, grp));
   const int nst = kw.stages();
 
@@ -708,7 +702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (SAFE && sl == 0) fence_s(sc);
       if constexpr (CP != 0) {
         constexpr int GAP = NMF / NI;  // MFMA slots per copy instruction
-        if (sl % GAP == GAP / 2) {
+        if (sl % GAP == kCopySlot % GAP) {
           if (CP == 1) copy_k(cp, sl / GAP);
           else copy_v(cp, sl / GAP);
         }
@@ -941,6 +935,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// First pass: one workgroup per tile, numbered so that each XCD runs a contiguous range
+// of (head, group, tile).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_sw_kernel(SoftmaxArgs a) {
+  const int total = count_tiles(a.geo, 256) * a.geo.H;
+  const int hid = blockIdx.x, xcd = hid & 7;
+  softmax_sw_tile<D, false>(a, xcd * (total >> 3) + imin(xcd, total & 7) + (hid >> 3));
+}
+
+// Second pass: a persistent grid walks the tile flags and redoes the flagged tiles (none
+// on ordinary data, so its cost is the walk).  The barrier between tiles keeps a tile's
+// first stage copies off LDS buffers the other waves may still read for the last tile.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void softmax_sw_redo_kernel(SoftmaxArgs a) {
+  const int total = count_tiles(a.geo, 256) * a.geo.H;
+  for (int lid = blockIdx.x; lid < total; lid += gridDim.x) {
+    const int4 f = *reinterpret_cast<const int4*>(a.flags + 4 * (size_t)lid);
+    if ((f.x | f.y | f.z | f.w) == 0) continue;
+    softmax_sw_tile<D, true>(a, lid);
+    __syncthreads();
+  }
+}
+
 int softmax_bf16_flag_count(const Geo& g) { return 4 * count_tiles(g, 256) * g.H; }
 
 hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream) {
@@ -951,12 +968,14 @@ hipError_t launch_softmax_bf16(const SoftmaxArgs& a, hipStream_t stream) {
   // first pass: every tile against the reference its first keys set; second pass: the
   // tiles whose row sums showed a later score far above it, with the reference raised
   // as the walk goes
+  // the second pass: one workgroup per CU (each takes a whole CU's LDS)
+  dim3 redo(imin(256, tiles * a.geo.H));
   if (a.geo.d == 128) {
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128, false>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_redo_kernel<128>), redo, block, 0, stream, a);
   } else if (a.geo.d == 64) {
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64, false>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_kernel<64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(softmax_sw_redo_kernel<64>), redo, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }
