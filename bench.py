@@ -236,7 +236,7 @@ def main() -> int:
     if fp8:
         # e4m3 QK^T of the video keys at the fp8 MFMA rate, text QK^T and P V at the bf16 rate
         sm_peak = workload.softmax_mixed_peak(shape, PEAK_FP8_TFLOPS, PEAK_BF16_TFLOPS)
-        kernel, traffic = "softmax_fp8_kernel<128>", None
+        kernel, traffic = "softmax_sw8_kernel", None
         metric = METRIC_LONG
         dtype = "fp8 e4m3 QK^T + bf16 PV, linear branch, projections"
         data = "synthetic: seeded N(0,1) activations (per-tensor e4m3 q/k/v) and gate logits, scaled N(0,1) weights"

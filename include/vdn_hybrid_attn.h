@@ -109,8 +109,8 @@ typedef struct {
                            (heads concatenated) followed by its gated linear output */
   size_t value_stage;   /* FP8 only, bf16 [N + L, H, d]: the value codes converted to bf16,
                            then text values divided by v_scale (no bytes otherwise) */
-  size_t tile_flags;    /* BF16 only, int32 per (softmax query tile, wave): which tiles
-                           the softmax's second pass redoes (no bytes otherwise) */
+  size_t tile_flags;    /* BF16 and FP8, int32 per (softmax query tile, wave): which tiles
+                           the softmax's second pass redoes (no bytes for F32) */
   size_t gemm_ws;       /* GEMM library scratch */
   size_t gemm_ws_bytes;
   size_t total;         /* == vdn_hybrid_attn_workspace_bytes() */

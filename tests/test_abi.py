@@ -68,9 +68,9 @@ def test_workspace_layout(shape):
     assert L.value_stage == _align(L.branch_out + N * 2 * H * d * ab)
     stage = (N + shape.text_len) * H * d * 2 if shape.qkv_dtype == "fp8" else 0
     assert L.tile_flags == _align(L.value_stage + stage)
-    # bf16: one int per (256-query tile, wave) of every head, for the softmax's second pass
+    # bf16 and fp8: one int per (256-query tile, wave) of every head, for the softmax's second pass
     tiles = sum(-(-n // 256) for n in _group_sizes(shape))
-    flags = 4 * tiles * H * 4 if shape.qkv_dtype == "bf16" else 0
+    flags = 4 * tiles * H * 4 if shape.qkv_dtype in ("bf16", "fp8") else 0
     assert L.gemm_ws == _align(L.tile_flags + flags)
     assert L.total == _align(L.gemm_ws + L.gemm_ws_bytes) == binding.workspace_bytes(cfg)
 

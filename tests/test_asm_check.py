@@ -1,5 +1,5 @@
-"""The static wait-state check of the inline-asm MFMAs (bf16 softmax, merged dK/dV backward): the checker
-flags planted hazards in small assembly listings, and the kernel as compiled is clean."""
+"""The static wait-state check of the inline-asm MFMAs (bf16 and fp8 softmax, merged dK/dV backward): the
+checker flags planted hazards in small assembly listings, and the kernels as compiled are clean."""
 import shutil
 
 import pytest
@@ -27,6 +27,30 @@ def test_mfma_result_read_by_valu_flagged_until_fenced():
     mf = "v_mfma_f32_32x32x16_bf16 v[16:31], v[0:3], a[4:7], v[16:31]"
     assert asm_check.check_asm(listing(mf, "s_nop 7", "v_exp_f32_e32 v40, v20"))
     assert asm_check.check_asm(listing(mf, "s_nop 7", "s_nop 3", "v_exp_f32_e32 v40, v20")) == []
+
+
+def test_fp8_mfma_result_needs_twenty_wait_states():
+    """The 16-pass 32x32x64 fp8 MFMA: the 12 wait states that clear a bf16 result are not enough."""
+    mf = "v_mfma_f32_32x32x64_f8f6f4 v[16:31], v[0:7], a[0:7], v[16:31]"
+    assert asm_check.check_asm(listing(mf, "s_nop 7", "s_nop 3", "v_exp_f32_e32 v40, v20"))
+    assert asm_check.check_asm(listing(mf, "s_nop 7", "s_nop 7", "s_nop 2", "v_exp_f32_e32 v40, v20"))
+    assert asm_check.check_asm(listing(mf, "s_nop 7", "s_nop 7", "s_nop 3", "v_exp_f32_e32 v40, v20")) == []
+    # an unrelated bf16 MFMA in between counts one wait state: the fp8 result still needs its 20
+    bf = "v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], a[4:7], v[32:47]"
+    assert asm_check.check_asm(listing(mf, bf, "s_nop 7", "s_nop 3", "v_exp_f32_e32 v40, v20"))
+    assert asm_check.check_asm(listing(mf, "s_nop 7", bf, "s_nop 7", "s_nop 3", "v_exp_f32_e32 v40, v20")) == []
+
+
+def test_execz_jump_counts_only_where_lanes_can_be_off():
+    """s_cbranch_execz cannot jump while every lane is active (kernel entry, outside the
+    compiler's saveexec regions); inside one it can."""
+    body = ("\tv_mfma_f32_32x32x16_bf16 v[16:31], v[0:3], a[4:7], v[16:31]\n\ts_cbranch_execz .LBB0_2\n"
+            "\ts_nop 7\n\ts_nop 7\n.LBB0_2:\n\tv_mov_b32_e32 v20, 0\n\ts_endpgm\n")
+    assert asm_check.check_asm(HEAD + body) == []
+    divergent = HEAD + "\ts_and_saveexec_b64 s[0:1], vcc\n" + body
+    assert len(asm_check.check_asm(divergent)) == 1
+    restored = HEAD + "\ts_and_saveexec_b64 s[0:1], vcc\n\ts_or_b64 exec, exec, s[0:1]\n" + body
+    assert asm_check.check_asm(restored) == []
 
 
 def test_hazard_through_a_branch_flagged():

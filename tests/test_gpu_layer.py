@@ -2,7 +2,8 @@
 
 Small workloads (toy fp32, frame-7 geometry fp32, mid-size bf16, ragged bf16 cases at
 both head dims, one without text, two with a short last chunk, one frame-3 single-chunk
-case, one with two neighbour chunks, and a ragged fp8 case) are compared element by
+case, one with two neighbour chunks, and fp8 cases with 0, 40, 100, 150 and 250 text
+tokens, ragged) are compared element by
 element on every output and intermediate state: the whole-tensor rel-L2 (<= 1e-5 for
 fp32, <= 1.5e-2 for bf16 and fp8) and, for every (token, head) row, output-token row and
 state row, the row rel-L2 (tests/parity.py).  Index sets are bit-exact everywhere.
@@ -38,6 +39,18 @@ NOTEXT = shapes.LayerShape("notext_f7_t70_c1_h1_d128_bf16", frames=7, tokens_per
 FP8_SMALL = shapes.LayerShape("fp8_f12_t100_c3_h3_d128", frames=12, tokens_per_frame=100, heads=3, head_dim=128,
                               text_len=40, chunk_frames=3, model_dim=200, qkv_dtype="fp8", act_dtype="bf16",
                               seed=2004)
+# fp8 with no text (the key walk starts on e4m3 keys), and with 2, 3 and 4 text stages of
+# 64 keys (the text-to-video switch of the key walk at each stage-buffer position mod 4)
+FP8_NOTEXT = shapes.LayerShape("fp8_notext_f7_t70_c1_h1_d128", frames=7, tokens_per_frame=70, heads=1, head_dim=128,
+                               text_len=0, chunk_frames=1, model_dim=64, qkv_dtype="fp8", act_dtype="bf16", seed=2011)
+FP8_T100 = shapes.LayerShape("fp8_t100_f9_t53_c2_h2_d128", frames=9, tokens_per_frame=53, heads=2, head_dim=128,
+                             text_len=100, chunk_frames=2, model_dim=96, qkv_dtype="fp8", act_dtype="bf16", seed=2012)
+FP8_T150 = shapes.LayerShape("fp8_t150_f13_t45_c5_h2_d128", frames=13, tokens_per_frame=45, heads=2, head_dim=128,
+                             text_len=150, chunk_frames=5, model_dim=160, qkv_dtype="fp8", act_dtype="bf16",
+                             seed=2013)
+FP8_T250 = shapes.LayerShape("fp8_t250_f10_t64_c3_h1_d128", frames=10, tokens_per_frame=64, heads=1, head_dim=128,
+                             text_len=250, chunk_frames=3, model_dim=64, qkv_dtype="fp8", act_dtype="bf16", seed=2014)
+FP8_MORE = [FP8_NOTEXT, FP8_T100, FP8_T150, FP8_T250]
 # a short last chunk (F not a multiple of C: chunks {0-4} {5-9} {10-12}, and {0-3} {4-7}
 # {8-10}), with token and text counts off every tile size
 SHORT128 = shapes.LayerShape("shortchunk_f13_t45_c5_h2_d128_bf16", frames=13, tokens_per_frame=45, heads=2,
@@ -52,7 +65,7 @@ ONECHUNK = shapes.LayerShape("onechunk_f3_t1_c4_h1_d64_bf16", frames=3, tokens_p
 WIDE = shapes.LayerShape("r2_f9_t7_c1_h2_d128_bf16", frames=9, tokens_per_frame=7, heads=2, head_dim=128,
                          text_len=6, chunk_frames=1, neighbor_chunks=2, model_dim=64, seed=2008)
 SMALL = [shapes.TOY, shapes.WORKED, shapes.MID, RAGGED128, RAGGED64, NOTEXT, FP8_SMALL, SHORT128, SHORT64,
-         ONECHUNK, WIDE]
+         ONECHUNK, WIDE] + FP8_MORE
 TOL = {"f32": 1e-5, "bf16": 1.5e-2, "fp8": 1.5e-2}
 
 
@@ -144,7 +157,7 @@ def test_layer_parity(shape):
     check_layer(shape, inp, ref)
 
 
-PEAKY = [shapes.TOY, shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT64, WIDE]
+PEAKY = [shapes.TOY, shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT64, WIDE] + FP8_MORE
 
 
 @pytest.mark.parametrize("shape", PEAKY, ids=lambda s: s.name)
@@ -158,11 +171,11 @@ def test_layer_parity_peaky(shape):
     check_layer(shape, inp, oracle_of(shape, inp), states=False)
 
 
-@pytest.mark.parametrize("shape", [shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT64],
+@pytest.mark.parametrize("shape", [shapes.MID, RAGGED128, RAGGED64, FP8_SMALL, SHORT128, SHORT64] + FP8_MORE,
                          ids=lambda s: s.name)
 def test_layer_parity_peaky_high(shape):
     """The same plants 50 log2 units higher (64, 73, 82, then 91): far enough above every
-    query's first keys that the bf16 kernel's first pass, which keeps the reference its
+    query's first keys that the softmax's first pass, which keeps the reference its
     first keys set, flags every tile and its second pass recomputes them with the
     reference raised along the walk (four times per query); the mixture of the frame
     plants and the last plant still checks each rescaling."""
@@ -170,7 +183,7 @@ def test_layer_parity_peaky_high(shape):
     check_layer(shape, inp, oracle_of(shape, inp), states=False)
 
 
-@pytest.mark.parametrize("shape", [shapes.TOY, RAGGED128, RAGGED64, FP8_SMALL, SHORT64],
+@pytest.mark.parametrize("shape", [shapes.TOY, RAGGED128, RAGGED64, FP8_SMALL, SHORT64, FP8_NOTEXT, FP8_T250],
                          ids=lambda s: s.name)
 def test_rescale_branch_runs(shape):
     """One planted key, the last key of every walk, scores about 400 (log2 units; at

@@ -11,9 +11,11 @@ to these instructions:
 
   - a VALU write of a VGPR or AGPR that an MFMA then reads (A, B or C operand): at least
     2 wait states between them;
-  - an 8-pass MFMA's result (32x32x16 bf16) read or overwritten by the VALU, or read by a
-    store: at least 12 wait states (NumPasses + 3, plus one on gfx950);
-  - an MFMA's C operand overwritten by the VALU: at least 11 wait states.
+  - an MFMA's result read or overwritten by the VALU, or read by a store: NumPasses + 4
+    wait states (NumPasses + 3, plus one on gfx950): 12 after the 8-pass 32x32x16 bf16
+    MFMA (also taken for the shorter 16x16x32), 20 after the 16-pass 32x32x64 fp8 one
+    (the count hipcc's own hazard recognizer inserts after that builtin);
+  - an MFMA's C operand overwritten by the VALU: NumPasses + 3 wait states.
 
 A wait state is one issued instruction; s_nop N counts N + 1.
 
@@ -33,8 +35,18 @@ import tempfile
 VALU_TO_MFMA = 2
 MFMA_TO_VALU_READ = 12
 MFMA_SRCC_TO_VALU_WRITE = 11
+# MFMAs with more passes than the 8 the defaults above are for
+PASSES = {"v_mfma_f32_32x32x64_f8f6f4": 16, "v_mfma_scale_f32_32x32x64_f8f6f4": 16}
+MAX_PASSES = max(PASSES.values())
+
+
+def _passes(op: str) -> int:
+    return PASSES.get(op, 8)
+
+
 # (source file under csrc/, mangled-name prefixes of its kernels written with asm MFMAs)
-TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel", "_ZN3vdn22softmax_sw_redo_kernel")),
+TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel", "_ZN3vdn22softmax_sw_redo_kernel",
+                                 "_ZN3vdn18softmax_sw8_kernel", "_ZN3vdn23softmax_sw8_redo_kernel")),
            ("backward.hip", ("_ZN3vdn21softmax_bwd_kv_kernel",)))
 PREFIXES = tuple(p for _, ps in TARGETS for p in ps)
 # sources whose kernels write M0 in inline asm (the LDS DMA copies)
@@ -125,28 +137,79 @@ def _kernels(asm: str, prefixes=PREFIXES) -> dict[str, list]:
     return out
 
 
+_BIG = 99  # exec depth after an exec write of unknown effect
+
+
+def _exec_effect(inst, d: int) -> int:
+    """Divergence depth after `inst` (0: all lanes of the wave active)."""
+    if inst is None:
+        return d
+    if inst.op.startswith("s_") and "saveexec" in inst.op:
+        return min(d + 1, _BIG)  # entry of a divergent region
+    parts = inst.text.split(None, 1)
+    ops = [x.strip() for x in parts[1].split(",")] if len(parts) > 1 else []
+    if ops and ops[0] == "exec":
+        if inst.op == "s_or_b64" and len(ops) > 1 and ops[1] == "exec":
+            return max(d - 1, 0)  # end of a divergent region: the saved mask comes back
+        if inst.op == "s_xor_b64" and d > 0:
+            return d  # the else part of a divergent region
+        return _BIG
+    return d
+
+
 def _preds(items):
-    """Index -> list of predecessor instruction indices (program order plus branches)."""
+    """Index -> list of predecessor instruction indices (program order plus branches).
+
+    The kernels are launched with whole waves (workgroups of a multiple of 64 threads), so
+    every lane is active at entry.  A forward pass tracks the divergence depth (saveexec
+    regions the compiler opens, their s_or_b64 exec restores); an s_cbranch_execz where
+    the depth is 0 cannot be taken (exec is all ones), and its jump is not an edge.  The
+    compiler emits such branches around uniform code too."""
     idx_of_label = {}
     for i, (lab, _) in enumerate(items):
         if lab:
             idx_of_label[lab] = i
-    preds = {i: [] for i in range(len(items))}
+    n = len(items)
+    succ = {i: [] for i in range(n)}
     for i, (lab, inst) in enumerate(items):
-        if i + 1 < len(items):
-            prev_uncond = inst is not None and (inst.op in ("s_branch", "s_endpgm", "s_setpc_b64"))
-            if not prev_uncond:
-                preds[i + 1].append(i)
+        if i + 1 < n:
+            uncond = inst is not None and (inst.op in ("s_branch", "s_endpgm", "s_setpc_b64"))
+            if not uncond:
+                succ[i].append((i + 1, False))
         if inst is not None and inst.op.startswith(("s_branch", "s_cbranch")):
             target = inst.text.split()[-1]
             if target in idx_of_label:
-                preds[idx_of_label[target]].append(i)
+                succ[i].append((idx_of_label[target], inst.op == "s_cbranch_execz"))
+    depth_in = [None] * n
+    if n:
+        depth_in[0] = 0
+    work = [0] if n else []
+    while work:
+        i = work.pop()
+        out = _exec_effect(items[i][1], depth_in[i])
+        for j, _ in succ[i]:
+            if depth_in[j] is None or out > depth_in[j]:
+                depth_in[j] = out
+                work.append(j)
+    preds = {i: [] for i in range(n)}
+    for i in range(n):
+        if depth_in[i] is None:
+            continue  # unreachable
+        out = _exec_effect(items[i][1], depth_in[i])
+        for j, execz in succ[i]:
+            if execz and out == 0:
+                continue
+            preds[j].append(i)
     return preds
 
 
 def _search(items, preds, start, need, hit):
     """Walk back from instruction `start` through the CFG while fewer than `need` wait
-    states separate it; return the first instruction for which hit(inst) holds."""
+    states separate it; return the first instruction for which hit(inst) holds.  `need`
+    is a number or a function of the instruction found (then the walk goes back as far
+    as the largest requirement and reports a hit only inside its own)."""
+    need_of = need if callable(need) else (lambda inst: need)
+    reach = need if not callable(need) else MAX_PASSES + 4
     stack = [(p, 0) for p in preds[start]]
     seen = set()
     while stack:
@@ -158,10 +221,10 @@ def _search(items, preds, start, need, hit):
         if inst is None:
             stack.extend((p, waited) for p in preds[i])
             continue
-        if hit(inst):
+        if hit(inst) and waited < need_of(inst):
             return inst, waited
         waited += inst.nop
-        if waited < need:
+        if waited < reach:
             stack.extend((p, waited) for p in preds[i])
     return None
 
@@ -183,12 +246,14 @@ def check_asm(asm: str, prefixes=PREFIXES) -> list[str]:
                     problems.append(f"{name}: VALU write '{r[0].text}' then MFMA read after {r[1]} wait states: '{inst.text}'")
             if inst.valu or inst.op.startswith(_STORE):
                 touched = inst.src | (inst.dst if inst.valu else set())
-                r = _search(items, preds, i, MFMA_TO_VALU_READ, lambda p: p.mfma and (p.dst & touched))
+                r = _search(items, preds, i, lambda p: max(MFMA_TO_VALU_READ, _passes(p.op) + 4),
+                            lambda p: p.mfma and (p.dst & touched))
                 if r:
                     problems.append(f"{name}: MFMA result '{r[0].text}' used after {r[1]} wait states: '{inst.text}'")
                 if inst.valu and inst.dst:
                     w = inst.dst
-                    r = _search(items, preds, i, MFMA_SRCC_TO_VALU_WRITE, lambda p: p.mfma and (p.srcc & w) and not (p.dst & w))
+                    r = _search(items, preds, i, lambda p: max(MFMA_SRCC_TO_VALU_WRITE, _passes(p.op) + 3),
+                                lambda p: p.mfma and (p.srcc & w) and not (p.dst & w))
                     if r:
                         problems.append(f"{name}: MFMA C operand '{r[0].text}' overwritten after {r[1]} wait states: '{inst.text}'")
     return problems

@@ -116,7 +116,7 @@ void layout_of(const vdn_hybrid_cfg* c, vdn_workspace_layout* L) {
   L->value_stage = off;
   if (c->qkv_dtype == VDN_FP8_E4M3) off = align_up(off + (N + L_txt) * H * d * 2);
   L->tile_flags = off;
-  if (c->qkv_dtype == VDN_BF16) off = align_up(off + (size_t)softmax_bf16_flag_count(make_geo(c)) * 4);
+  if (c->qkv_dtype != VDN_F32) off = align_up(off + (size_t)softmax_flag_count(make_geo(c)) * 4);
   L->gemm_ws = off; L->gemm_ws_bytes = kGemmWs; off = align_up(off + kGemmWs);
   L->total = off;
 }
@@ -597,7 +597,8 @@ static vdn_status fwd_impl(const void* q, const void* k, const void* v, const vo
     e = launch_dequant_values(da, stream);
     if (e != hipSuccess) return fail(VDN_ERR_HIP, "value staging launch: %s", hipGetErrorString(e));
     SoftmaxArgs sm{q, k, vst, (const __bf16*)tk, tvst, (const __bf16*)gs, (__bf16*)acat, o_soft_dbg, g,
-                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale, nullptr, nullptr};
+                   c2 * cfg->q_scale, c2 * cfg->q_scale * cfg->k_scale, cfg->v_scale, nullptr,
+                   reinterpret_cast<int*>(ws + L.tile_flags)};
     e = launch_softmax_fp8(sm, stream);
   } else if (bf16) {
     SoftmaxArgs sm{q, k, (const __bf16*)v, (const __bf16*)tk, (const __bf16*)tv, (const __bf16*)gs, (__bf16*)acat,

@@ -25,12 +25,12 @@ struct SoftmaxArgs {
   float out_scale;
   float* lse;    // nullable [N,H]: m + log2(l), the log2-domain log-sum-exp of each query's
                  // scaled scores (the backward rebuilds P = exp2(c2 q.k - lse))
-  int* flags;    // bf16 kernel: softmax_bf16_flag_count(geo) ints of scratch, one per
-                 // (query tile, wave): written by the first pass, read by the second
+  int* flags;    // softmax_flag_count(geo) ints of scratch, one per (query tile, wave):
+                 // written by the first pass, read by the second
 };
 
-// Ints of scratch the bf16 softmax needs for its tile flags.
-int softmax_bf16_flag_count(const Geo& g);
+// Ints of scratch the bf16 and fp8 softmax kernels need for their tile flags.
+int softmax_flag_count(const Geo& g);
 
 // fp8 value staging: vout[n] = bf16(code value of v8[n]) for the video values and
 // tvout[n] = bf16(tv[n] / v_scale) for the text values.

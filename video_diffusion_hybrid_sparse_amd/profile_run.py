@@ -1,10 +1,12 @@
-"""Workload for rocprofv3 runs: N forwards of the 768p layer (or, with --projections,
+"""Workload for rocprofv3 runs: N forwards of the 768p layer (--workload long: the
+120-frame fp8 long-clip layer; with --projections,
 N steps of its MXFP8 input-side projections: quantise the token rows, then the
 block-scaled GEMM against the prepared weight), then one plain device copy of 1 GiB
 whose counter readings calibrate HBM byte counters (FETCH_SIZE / WRITE_SIZE): the copy
 reads and writes exactly 2**30 bytes.
 
-Usage: python -m video_diffusion_hybrid_sparse_amd.profile_run [--steps N] [--projections]
+Usage: python -m video_diffusion_hybrid_sparse_amd.profile_run [--steps N] [--workload 768p|long]
+       [--projections]
 """
 from __future__ import annotations
 
@@ -18,6 +20,7 @@ from . import binding, runner, shapes, synth
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--workload", choices=("768p", "long"), default="768p")
     ap.add_argument("--projections", action="store_true")
     args = ap.parse_args()
     if args.projections:
@@ -35,7 +38,7 @@ def main() -> None:
             binding.mxfp8_quantize(x, xc, xs)
             binding.mxfp8_linear(xc, xs, wc, ws, outs, bias)
     else:
-        dl = runner.upload(synth.make_inputs(shapes.P768))
+        dl = runner.upload(synth.make_inputs(shapes.P768 if args.workload == "768p" else shapes.LONG))
         for _ in range(args.steps):
             dl.run()
     torch.cuda.synchronize()
