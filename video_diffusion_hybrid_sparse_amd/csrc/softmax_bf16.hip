@@ -155,8 +155,9 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   constexpr int NI8 = BN * CPR8 / (64 * NW); // e4m3 key loads per lane per stage
   constexpr int LA = 3;                      // operand reads in flight ahead of their MFMAs
   constexpr int kExpSlot = 4;                // first MFMA slot of a first-pass block's exponentials
-  constexpr int kExpSlot8 = 4;               // the same after a block of fp8 score MFMAs
+  constexpr int kExpSlot8 = 3;               // the same after a block of fp8 score MFMAs (4, 6: slower)
   constexpr int kCopySlot = 4;               // slot (mod the copy spacing) of a block's stage copies
+  constexpr int kWpv = 8, kWsum = 4, kWqk8 = 16;  // slot weights of the fp8 blocks' exponentials
   // vector-memory instructions of the most recent stage copy that a wait may leave in
   // flight: the fewest one stage issues (fp8 video stages copy half the key bytes)
   constexpr int kStageOps = FP8 ? NI + NI8 : 2 * NI;
@@ -459,6 +460,17 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
     // wait states an MFMA result needs before a VALU read; asm_check verifies them)
     constexpr int E0 = (SAFE || !PREV) ? 0 : (FP8 ? kExpSlot8 : kExpSlot);
     static_assert(NMF > 0 && NMF > E0, "a block issues MFMAs");
+    // The exponentials: evenly over the slots from E0 on (bf16 scores next), or (fp8
+    // scores next) in proportion to each slot's MFMA passes (P V 8, row sums 4, fp8 scores
+    // 16), which measured 1% faster there and 3% slower with bf16 scores (as did leaving
+    // the last 2, 4 or 6 slots of a block without exponentials, 1.5-3%, either input
+    // type).  wcum(sl) = weight of slots E0 .. sl - 1.
+    constexpr bool WEIGHTED = N8;
+    auto wcum = [&](int sl) __attribute__((always_inline)) {
+      auto part = [&](int a, int b) { return imax(0, imin(sl, b) - imax(E0, a)); };
+      return WEIGHTED ? kWpv * part(0, QB * NOPV) + kWsum * part(QB * NOPV, NMP) + kWqk8 * part(NMP, NMF)
+                      : part(0, NMF);
+    };
     bf16x8 op[NOP + LA];
     i32x8 op8[N8 ? KS8 : 1];
     auto fetch = [&](int n) __attribute__((always_inline)) {
@@ -527,7 +539,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
       }
       if (sl >= E0) {
 #pragma unroll
-        for (int it = (sl - E0) * NIT / (NMF - E0); it < (sl - E0 + 1) * NIT / (NMF - E0); ++it)
+        for (int it = NIT * wcum(sl) / wcum(NMF); it < NIT * wcum(sl + 1) / wcum(NMF); ++it)
           expo_unit(sc, pc, it, c2c);
       }
       __builtin_amdgcn_sched_barrier(0);
