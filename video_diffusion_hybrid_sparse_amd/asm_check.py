@@ -50,7 +50,7 @@ TARGETS = (("softmax_bf16.hip", ("_ZN3vdn17softmax_sw_kernel", "_ZN3vdn22softmax
            ("backward.hip", ("_ZN3vdn21softmax_bwd_kv_kernel",)))
 PREFIXES = tuple(p for _, ps in TARGETS for p in ps)
 # sources whose kernels write M0 in inline asm (the LDS DMA copies)
-M0_SOURCES = ("softmax_bf16.hip", "backward.hip", "delta_bf16.hip", "mxfp8.hip", "proj_gemm.hip")
+M0_SOURCES = ("softmax_bf16.hip", "backward.hip", "delta_bf16.hip", "mxfp8.hip", "proj_gemm.hip", "linear_bf16.hip")
 
 _REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
 _STORE = ("ds_write", "ds_store", "global_store", "buffer_store", "scratch_store", "flat_store")

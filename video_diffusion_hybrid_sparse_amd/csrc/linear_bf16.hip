@@ -13,15 +13,37 @@ namespace vdn {
 
 // ---- state build: S = K^T V over the tokens of one frame (or the text), one head ------
 //
-// One workgroup per (frame or text, head).  Tokens are walked 32 at a time; K and V are
-// transposed into LDS as [channel][token] so that both MFMA operands (contraction over
-// tokens) read 16 contiguous bytes per lane.  Wave w owns a (D/2 x D/2) quadrant of the
-// d x d state.
+// One workgroup per (frame or text, head).  Tokens are walked 32 at a time in stages that
+// go from HBM straight into LDS (buffer loads with the LDS bit, written as inline asm so
+// that the loop waits for them itself; four stage buffers, so three stages are in flight
+// while one is computed).  Rows stay as stored ([token][channel], XOR-swizzled 16-byte
+// chunks) and both MFMA operands, whose contraction runs over tokens, are gathered with
+// the transposing LDS read.  Rows past the last token lie beyond the extent of the buffer
+// resource, which the hardware answers with zeros and no memory access.  Wave w owns a
+// (D/2 x D/2) quadrant of the d x d state.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from a raw buffer (base, extent) into LDS: lane i's bytes land at LDS
+// address m0 + 16 i; offsets at or beyond the extent read zeros.
+__device__ __forceinline__ void dma16_buf(const i32x4& rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(m0)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x4 raw_buffer(const void* base, uint32_t extent) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  // stride 0, raw (untyped) access; the last word selects 32-bit data
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xffff), (int)extent, 0x00020000};
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void build_bf16_kernel(BuildArgs<__bf16> a) {
-  constexpr int TB = 32, PAD = TB + 8, TPW = D / 64, NPO = TB / 2 * D / 8;
-  __shared__ __attribute__((aligned(16))) __bf16 Kt[2][D * PAD];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * PAD];
+  constexpr int TB = 32, NB = 4, TPW = D / 64, DT = D / 32, CPR = D / 8, RPI = 64 / CPR;
+  constexpr int NI = TB * CPR / 256;  // copies per thread, stage and tensor
+  static_assert(NI >= 1 && TB * CPR % 256 == 0, "whole copy rounds");
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[NB][TB * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[NB][TB * D];
   const Geo g = a.geo;
   const int fr = blockIdx.x, h = blockIdx.y;
   const size_t rs = (size_t)g.H * D;
@@ -55,62 +77,72 @@ __global__ __launch_bounds__(256) void build_bf16_kernel(BuildArgs<__bf16> a) {
     for (int j = 0; j < TPW; ++j) acc[i][j] = 0.0f;
 
   const int nsteps = (ntok + TB - 1) / TB;
-  // loader unit: tokens (2p, 2p+1) x 8 channels; p = tid % 16, channel octet = tid / 16
-  const int pr = tid & 15, oc = tid >> 4;
-  uint4 kr[2], vr[2];
-  auto load = [&](int step) {
-    if (tid < NPO) {
-      // rows past the end are loaded clamped, then replaced by zeros (selects on values)
-      const int t = step * TB + 2 * pr, col = oc * 8;
-      const size_t o0 = (size_t)imin(t, ntok - 1) * rs + col, o1 = (size_t)imin(t + 1, ntok - 1) * rs + col;
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 k0 = *reinterpret_cast<const uint4*>(kb + o0), v0 = *reinterpret_cast<const uint4*>(vb + o0);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(kb + o1), v1 = *reinterpret_cast<const uint4*>(vb + o1);
-      kr[0] = t < ntok ? k0 : z;
-      vr[0] = t < ntok ? v0 : z;
-      kr[1] = t + 1 < ntok ? k1 : z;
-      vr[1] = t + 1 < ntok ? v1 : z;
-    }
-  };
-  auto store = [&](int buf) {
-    if (tid < NPO) {
-      const int col = oc * 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t k0 = u4_at(kr[0], e), k1 = u4_at(kr[1], e), v0 = u4_at(vr[0], e), v1 = u4_at(vr[1], e);
-        uint32_t* kt = reinterpret_cast<uint32_t*>(&Kt[buf][(col + 2 * e) * PAD + 2 * pr]);
-        uint32_t* vt = reinterpret_cast<uint32_t*>(&Vt[buf][(col + 2 * e) * PAD + 2 * pr]);
-        kt[0] = (k0 & 0xffffu) | (k1 << 16);
-        kt[PAD / 2] = (k0 >> 16) | (k1 & 0xffff0000u);
-        vt[0] = (v0 & 0xffffu) | (v1 << 16);
-        vt[PAD / 2] = (v0 >> 16) | (v1 & 0xffff0000u);
-      }
-    }
-  };
-
   if (nsteps > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) load(st + 1);
+    // (byte offsets stay below 2^31 + 2^21: the tensors hold fewer than 2^31 elements)
+    const uint32_t rsb = (uint32_t)rs * 2, extent = (uint32_t)(ntok - 1) * rsb + D * 2;
+    const i32x4 rk = raw_buffer(kb, extent), rv = raw_buffer(vb, extent);
+    // copy i of this thread: stage row (wave NI + i) RPI + lane / CPR, swizzled chunk
+    uint32_t coff[NI];
 #pragma unroll
-    for (int ks = 0; ks < TB / 16; ++ks) {
-      bf16x8 av[TPW], bv[TPW];
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        av[i] = *reinterpret_cast<const bf16x8*>(&Kt[buf][(r0 + 32 * i + l32) * PAD + 16 * ks + 8 * half]);
-        bv[i] = *reinterpret_cast<const bf16x8*>(&Vt[buf][(c0 + 32 * i + l32) * PAD + 16 * ks + 8 * half]);
-      }
-#pragma unroll
-      for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int j = 0; j < TPW; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+    for (int i = 0; i < NI; ++i) {
+      const int r = (wave * NI + i) * RPI + lane / CPR;
+      coff[i] = (uint32_t)r * rsb + (uint32_t)((lane % CPR) ^ swz<CPR>(r)) * 16;
     }
-    if (st + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
+    const uint32_t m0k = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Ks[0][0] + wave * NI * RPI * D * 2);
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vs[0][0] + wave * NI * RPI * D * 2);
+    // stage st into buffer st % NB (stages past the last read zeros: no memory access)
+    auto issue = [&](int st) __attribute__((always_inline)) {
+      const uint32_t base = (uint32_t)st * TB * rsb, lb = (uint32_t)(st % NB) * (TB * D * 2);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16_buf(rk, base + coff[i], m0k + lb + i * RPI * D * 2);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16_buf(rv, base + coff[i], m0v + lb + i * RPI * D * 2);
+    };
+    // operand gather (the transposing read): lane (16-lane group grp16, i16) gets channel
+    // 32 dt + (lane % 32) of the 8 tokens of its k-group; K and V use the same token order
+    const int grp16 = lane >> 4, i16 = lane & 15;
+    int trd[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 4 * (grp16 >> 1) + 8 * c + (i16 >> 2);
+        const int d = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
+        trd[dt][c] = row * D + (((d >> 3) ^ swz<CPR>(row)) * 8) + (d & 7);
+      }
+    auto gather = [&](const __bf16* buf, int ks, int dt) __attribute__((always_inline)) {
+      const bf16x4 lo = lds_read_tr(buf + 16 * ks * D + trd[dt][0]);
+      const bf16x4 hi = lds_read_tr(buf + 16 * ks * D + trd[dt][1]);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st) issue(st);
+    for (int st = 0; st < nsteps; ++st) {
+      // stage st landed (the NB - 2 after it may be in flight), and every wave is done
+      // with stage st - 1, whose buffer the next copy fills
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NI * (NB - 2)) : "memory");
+      issue(st + NB - 1);
+      const __bf16* kbuf = Ks[st % NB];
+      const __bf16* vbuf = Vs[st % NB];
+#pragma unroll
+      for (int ks = 0; ks < TB / 16; ++ks) {
+        bf16x8 av[TPW], bv[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+          av[i] = gather(kbuf, ks, r0 / 32 + i);
+          bv[i] = gather(vbuf, ks, c0 / 32 + i);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+      }
+    }
+    // the copies of the stages past the last may still be landing
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // accumulator: row r0 + 32 i + 8 (r/4) + 4 half + r%4, column c0 + 32 j + l32
@@ -139,21 +171,27 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 // ---- state read: u = q.S_fwd + q.S_bwd, RMSNorm, gate --------------------------------
 //
 // One workgroup = up to 1024 query tokens of one query group and one head (the states'
-// load and split is paid once per 1024 tokens); each of the 4 waves walks 32-token
-// sub-tiles.  The group's two states are summed in float32 (the
+// load and split is paid once per 1024 tokens); each of its 8 waves walks 32-token
+// sub-tiles (the 64 KB of LDS allow two workgroups per CU, so 16 waves keep loads in
+// flight).  The group's two states are summed in float32 (the
 // identity feature map makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding
 // differs), split into bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled
 // 16-byte chunks) in LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes
 // with float32 accumulation (about 16 mantissa bits of the state kept); the S^T operand is
 // gathered with the transposing LDS read.  A lane owns one token, so RMSNorm needs one
 // lane-pair sum; a lane-pair swap then gives each lane 8 contiguous channels, so gate
-// loads and output stores are 16 bytes wide.
+// loads and output stores are 16 bytes wide.  A wave's next query and gate rows are in
+// flight while it computes the current sub-tile.
+constexpr int kReadWaves = 8;  // waves per readout workgroup (8: 7% faster than 4)
+
 template <int D>
-__global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
-  constexpr int BM = 1024, KS = D / 16, DT = D / 32, CPR = D / 8;
+__global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
+  constexpr int BM = 1024, KS = D / 16, DT = D / 32, CPR = D / 8, NW = kReadWaves, NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) __bf16 Shi[D * D];
   __shared__ __attribute__((aligned(16))) __bf16 Slo[D * D];
   const Geo g = a.geo;
+  // (tiles vary fastest: 2% faster than heads fastest; tiles of one group, which share
+  // its state pair, run side by side)
   const int h = blockIdx.y;
   int grp, t0, t1;
   if (!locate_tile(g, blockIdx.x, BM, grp, t0, t1)) return;
@@ -168,7 +206,11 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
     const float* fa = chunk >= 0 ? a.Sfwd + (size_t)chunk * g.H * D * D + hs : ta;
     const float* ba = chunk >= 0 ? a.Sbwd + (size_t)chunk * g.H * D * D + hs : ta;
     const float wf = chunk >= 0 ? 1.0f : 0.5f;
-    for (int u = tid; u < D * D / 4; u += 256) {
+    // (unrolled: all of a thread's state loads are issued before the first is used)
+    static_assert(D * D / 4 % NT == 0, "whole rounds of float4 per thread");
+#pragma unroll
+    for (int it = 0; it < D * D / 4 / NT; ++it) {
+      const int u = tid + NT * it;
       const int i = u / (D / 4), j = 4 * (u % (D / 4));
       const float4 f = *reinterpret_cast<const float4*>(fa + i * D + j);
       const float4 b = *reinterpret_cast<const float4*>(ba + i * D + j);
@@ -200,14 +242,40 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
     }
   const float* wrow = a.w + h * D;
 
-  for (int st = wave; st * 32 < t1 - t0; st += 4) {
-    int tok = t0 + st * 32 + l32;
-    const bool ok = tok < t1;
-    tok = ok ? tok : t1 - 1;
-    const size_t qrow = (size_t)tok * rs + h * D;
-    bf16x8 qreg[KS];
+  // The query and gate rows of a wave's next sub-tile are loaded while it computes the
+  // current one (each wave walks its sub-tiles one after another, so otherwise every
+  // sub-tile waits for its own loads).
+  auto row_of = [&](int st) __attribute__((always_inline)) {
+    const int tok = t0 + st * 32 + l32;
+    return (size_t)(tok < t1 ? tok : t1 - 1) * rs + h * D;
+  };
+  bf16x8 qn[KS];
+  uint4 gn[DT][2];
+  auto load_rows = [&](int st) __attribute__((always_inline)) {
+    const size_t qrow = row_of(st);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qreg[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+    for (int s = 0; s < KS; ++s) qn[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+        gn[dt][ip] = *reinterpret_cast<const uint4*>(a.gl + qrow + 32 * dt + 16 * ip + 8 * half);
+  };
+  if (wave * 32 < t1 - t0) load_rows(wave);
+
+  for (int st = wave; st * 32 < t1 - t0; st += NW) {
+    const int tok = t0 + st * 32 + l32;
+    const bool ok = tok < t1;
+    const size_t qrow = row_of(st);
+    bf16x8 qreg[KS];
+    uint4 gcur[DT][2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qreg[s] = qn[s];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) gcur[dt][ip] = gn[dt][ip];
+    if ((st + NW) * 32 < t1 - t0) load_rows(st + NW);
 
     // delta-rule variant: u = phi(q).S with phi(q) = q / sqrt(|q|^2 + eps); the lane and
     // its partner (lane +- 32) hold the two halves of token `tok`'s channels
@@ -264,7 +332,7 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
         permlane32_swap4(x, y);
         const int c0 = 32 * dt + 16 * ip + 8 * half;
         const float uv[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-        const uint4 graw = *reinterpret_cast<const uint4*>(a.gl + qrow + c0);
+        const uint4 graw = gcur[dt][ip];
         const float4 w0 = *reinterpret_cast<const float4*>(wrow + c0);
         const float4 w1 = *reinterpret_cast<const float4*>(wrow + c0 + 4);
         const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -290,7 +358,7 @@ __global__ __launch_bounds__(256) void readout_bf16_kernel(ReadoutArgs<__bf16> a
 hipError_t launch_readout_bf16(const ReadoutArgs<__bf16>& a, hipStream_t stream) {
   const int tiles = count_tiles(a.geo, 1024);
   if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles, a.geo.H), block(256);
+  dim3 grid(tiles, a.geo.H), block(64 * kReadWaves);
   if (a.geo.d == 128)
     hipLaunchKernelGGL(readout_bf16_kernel<128>, grid, block, 0, stream, a);
   else if (a.geo.d == 64)

@@ -153,7 +153,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   constexpr int CPR8 = D / 16;               // 16-byte chunks per e4m3 row
   constexpr int RPI8 = 64 / CPR8;
   constexpr int NI8 = BN * CPR8 / (64 * NW); // e4m3 key loads per lane per stage
-  constexpr int LA = 3;                      // operand reads in flight ahead of their MFMAs
+  constexpr int LA = 3;                      // operand reads in flight ahead of their MFMAs (4, 5: level or slower)
   constexpr int kExpSlot = 4;                // first MFMA slot of a first-pass block's exponentials
   constexpr int kExpSlot8 = 3;               // the same after a block of fp8 score MFMAs (4, 6: slower)
   constexpr int kCopySlot = 4;               // slot (mod the copy spacing) of a block's stage copies
