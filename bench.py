@@ -107,9 +107,11 @@ def cpu_baseline(shape, inp) -> dict:
     from video_diffusion_hybrid_sparse_amd import synth, workload
 
     F, T, C, R, H, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.neighbor_chunks, shape.heads, shape.head_dim
-    frames = [0, 1, 5, 10, F // 2, F - 5, F - 2]
+    # about 10-20 s of CPU work on a 16-core host: every head, ten frames (both anchors,
+    # the first and last chunks, the middle)
+    frames = sorted({f for f in (0, 1, 5, 10, 20, F // 2, F - 15, F - 5, F - 2, F - 1) if 0 <= f < F})
     rows = np.concatenate([np.arange(f * T, (f + 1) * T) for f in frames])
-    heads = list(range(min(24, H)))
+    heads = list(range(H))
     cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
     hs = torch.tensor(heads)
 
