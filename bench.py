@@ -39,11 +39,13 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
-PMC_TRAFFIC = {"source_sha256_16": "579dfc2da4ca06a7", "bytes": 22.803e9}
+PMC_TRAFFIC = {"source_sha256_16": "530864c3e64d2453", "bytes": 31.886e9}
+# the same for the fp8 kernel on the 120-frame workload (same source file)
+PMC_TRAFFIC_FP8 = {"source_sha256_16": "530864c3e64d2453", "bytes": 21.919e9}
 # the same for the MXFP8 GEMM (profiles/kernel_stats_768p_mxfp8_projections.md)
-PMC_TRAFFIC_MX = {"source_sha256_16": "cb0f1e10a0964a3b", "bytes": 25.021e9}
+PMC_TRAFFIC_MX = {"source_sha256_16": "23628d501f41ade5", "bytes": 24.763e9}
 MX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/mxfp8.hip", "video_diffusion_hybrid_sparse_amd/csrc/mxfp8.h",
-              "video_diffusion_hybrid_sparse_amd/csrc/common.h")
+              "video_diffusion_hybrid_sparse_amd/csrc/common.h", "video_diffusion_hybrid_sparse_amd/csrc/tile.h")
 SOFTMAX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/softmax_bf16.hip",
                    "video_diffusion_hybrid_sparse_amd/csrc/common.h",
                    "video_diffusion_hybrid_sparse_amd/csrc/kernels.h")
@@ -61,8 +63,8 @@ def measured_traffic(sources, record):
     return record["bytes"] if h.hexdigest()[:16] == record["source_sha256_16"] else None
 
 
-def softmax_traffic():
-    return measured_traffic(SOFTMAX_SOURCES, PMC_TRAFFIC)
+def softmax_traffic(fp8: bool = False):
+    return measured_traffic(SOFTMAX_SOURCES, PMC_TRAFFIC_FP8 if fp8 else PMC_TRAFFIC)
 
 
 def spread(per_call):
@@ -238,7 +240,7 @@ def main() -> int:
     if fp8:
         # e4m3 QK^T of the video keys at the fp8 MFMA rate, text QK^T and P V at the bf16 rate
         sm_peak = workload.softmax_mixed_peak(shape, PEAK_FP8_TFLOPS, PEAK_BF16_TFLOPS)
-        kernel, traffic = "softmax_sw8_kernel", None
+        kernel, traffic = "softmax_sw8_kernel", softmax_traffic(fp8=True)
         metric = METRIC_LONG
         dtype = "fp8 e4m3 QK^T + bf16 PV, linear branch, projections"
         data = "synthetic: seeded N(0,1) activations (per-tensor e4m3 q/k/v) and gate logits, scaled N(0,1) weights"
