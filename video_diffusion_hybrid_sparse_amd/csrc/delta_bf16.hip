@@ -18,13 +18,16 @@
 //
 // Work split: one workgroup per (head, direction, 64 value columns); wave w owns 16 value
 // columns.  A value column of S evolves independently of the others, so no reduction
-// crosses waves.  Per 64-token tile (double-buffered HBM -> LDS copies):
+// crosses waves.  Per 64-token tile (HBM -> LDS copies three tiles ahead, four buffers):
 //   W  = K S          16x16x32 MFMAs, S as the B operand split into bf16 hi + lo;
 //   R' = (V - W / |k|) / |k|   per token (zero for rows past the block);
 //   dS += K^T R'      A operand read with the transposing LDS read in the token order
 //                     the W accumulators hold, R' split into bf16 hi + lo.
 // K stays exact bf16 in both products; the key normalisation is applied in fp32 to W and
-// R'.  After a frame, S += (beta / T) dS in fp32 registers.
+// R'.  After a frame, S += (beta / T) dS in fp32 registers.  Copies three tiles ahead and
+// one barrier per tile measured level with double buffering and two barriers (2.35 ms
+// for both recurrences at 768p): a tile's dependent chain (LDS reads, K S, R', K^T R')
+// bounds it, with one wave per SIMD on 768 of the 1024 SIMDs.
 #include "kernels.h"
 
 namespace vdn {
@@ -33,6 +36,12 @@ namespace {
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x of another lane of the same 16-lane row, chosen by the DPP control CTRL
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 
 // a pointer the wave agrees on, as a scalar value
@@ -58,11 +67,12 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
   constexpr int NKI = TT * CPR / 256;     // K-tile copies per thread
   constexpr int NVI = TT * (VC / 8) / 256;  // V-tile copies per thread
   constexpr int SXS = D + 4;              // padded column stride of the state transfer buffer
+  constexpr int NB = 4;                   // tile buffers: tiles j + 1 .. j + 3 in flight during tile j
   static_assert(NKI >= 1 && NVI >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) __bf16 Kt[2][TT * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][TT * VC];
+  __shared__ __attribute__((aligned(16))) __bf16 Kt[NB][TT * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[NB][TT * VC];
   __shared__ __attribute__((aligned(16))) float Sx[4][16 * SXS];
-  __shared__ __attribute__((aligned(16))) float invs[2][TT];
+  __shared__ __attribute__((aligned(16))) float invs[NB][TT];
 
   const Geo g = a.geo;
   const int h = blockIdx.x, dir = blockIdx.y, slice = blockIdx.z;
@@ -195,34 +205,52 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
     }
   };
 
+  // 1 / sqrt(|k|^2 + eps_phi) for the key rows this thread's wave copied into buffer b:
+  // copy i of thread tid filled 16-byte slot i 256 + tid of the tile (row (i 256 + tid) /
+  // CPR), and the CPR lanes of a row are consecutive lanes of one wave, so the wave needs
+  // only its own copies to have landed
+  // (the CPR partial sums of a row are added by DPP lane moves inside each 16-lane row:
+  // lane swaps within pairs and quads, then the half-row and row mirrors)
+  auto row_sum = [](float v) __attribute__((always_inline)) {
+    static_assert(CPR == 8 || CPR == 16, "a key row's lanes lie inside one 16-lane row");
+    v += dpp_f32<0xB1>(v);                            // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4E>(v);                            // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x141>(v);                           // row_half_mirror
+    if constexpr (CPR == 16) v += dpp_f32<0x140>(v);  // row_mirror
+    return v;
+  };
+  auto key_norms = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NKI; ++i) {
+      const int q = i * 256 + tid;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(&Kt[b][q * 8]);
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += (float)x[e] * (float)x[e];
+      ss = row_sum(ss);
+      if (q % CPR == 0) invs[b][q / CPR] = __builtin_amdgcn_rsqf(ss + kEpsPhi);
+    }
+  };
+
   if (ntx == 0) store_states(0);  // no text: both recurrences start at zero
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Tiles 0 .. NB - 2 in flight; tile j + NB - 1 is issued at the start of tile j (past the
+  // last tile: the last tile again, so that every tile issues the same copies and the
+  // waits count alike).  Before the barrier that ends tile j, each wave's copies of tile
+  // j + 1 have landed (the NB - 2 tiles after it may still be in flight: loads complete
+  // in issue order) and it has written their key norms, so each tile takes one barrier.
+  constexpr int kTileOps = NKI + NVI;
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t) issue(imin(t, ntiles - 1), t);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * kTileOps) : "memory");
+  key_norms(0);
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
+    const int buf = j & (NB - 1);
+    issue(imin(j + NB - 1, ntiles - 1), (j + NB - 1) & (NB - 1));
     int first, valid;
     bool text;
     tile_at(j, first, valid, text);
-
-    // 1 / sqrt(|k|^2 + eps_phi) per token: four threads per token, a quarter of the dims each
-    {
-      const int tok = tid >> 2, qd = tid & 3;
-      float ss = 0.0f;
-#pragma unroll
-      for (int m = 0; m < CPR / 4; ++m) {
-        const int c = qd * (CPR / 4) + m;
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(&Kt[buf][tok * D + ((c ^ swz<CPR>(tok)) * 8)]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += (float)x[e] * (float)x[e];
-      }
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      if (qd == 0) invs[buf][tok] = 1.0f / sqrtf(ss + kEpsPhi);
-    }
-    __syncthreads();
 
     // W = K S and R' for the four 16-token row tiles; R' goes straight into B operands
     bf16x8 rbh[2], rbl[2];
@@ -285,9 +313,14 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
       rebuild_operand();
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wave's copies of tile j + 1 landed and their key norms written; after the
+    // barrier every wave's are, and every wave is done with tile j (its buffer takes the
+    // copy issued at the start of tile j + 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * kTileOps) : "memory");
+    key_norms((j + 1) & (NB - 1));
     __syncthreads();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (ntx == 0 && dir == 0) {
     float* dst = a.Stext + (size_t)h * D * D + vcol0 + 16 * wave + l16;
 #pragma unroll
