@@ -109,9 +109,10 @@ def cpu_baseline(shape, inp) -> dict:
     from video_diffusion_hybrid_sparse_amd import synth, workload
 
     F, T, C, R, H, d = shape.frames, shape.tokens_per_frame, shape.chunk_frames, shape.neighbor_chunks, shape.heads, shape.head_dim
-    # about 10-20 s of CPU work on a 16-core host: every head, ten frames (both anchors,
+    # about 15 s of CPU work on a 16-core host: every head, fourteen frames (both anchors,
     # the first and last chunks, the middle)
-    frames = sorted({f for f in (0, 1, 5, 10, 20, F // 2, F - 15, F - 5, F - 2, F - 1) if 0 <= f < F})
+    frames = sorted({f for f in (0, 1, 3, 5, 10, 15, 20, F // 2, F - 20, F - 15, F - 10, F - 5, F - 2, F - 1)
+                     if 0 <= f < F})
     rows = np.concatenate([np.arange(f * T, (f + 1) * T) for f in frames])
     heads = list(range(H))
     cols = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
