@@ -551,7 +551,8 @@ static vdn_status fwd_impl(const void* q, const void* k, const void* v, const vo
       g_prof.used++;
     }
   }
-  auto mark = [&](int i) { if (ev) hipEventRecord(ev[i], stream); };
+  // (a failed profiling event only loses that step's timing)
+  auto mark = [&](int i) { if (ev) (void)hipEventRecord(ev[i], stream); };
 
   hipError_t e = hipSuccess;
   const bool delta = cfg->linear_variant == 1;
