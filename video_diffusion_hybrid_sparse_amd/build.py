@@ -51,14 +51,19 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs, "-L", os.path.join(ROCM, "lib"),
           "-lhipblaslt", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"])
-    os.replace(tmp, LIB)
     # the bf16 softmax and the merged dK/dV backward write their MFMAs as inline asm:
     # check the wait states around them, and that no compiler-generated code uses M0 in
-    # the sources whose LDS copies write it from inline asm
+    # the sources whose LDS copies write it from inline asm.  The library is installed
+    # only when the check passes; on failure the previous one is removed as well, so that
+    # nothing loads a library built from other sources.
     from .asm_check import check
     problems = check()
     if problems:
+        for f in (tmp, LIB):
+            if os.path.exists(f):
+                os.remove(f)
         raise RuntimeError("static check of the compiled kernels failed:\n" + "\n".join(problems))
+    os.replace(tmp, LIB)
     return LIB
 
 
