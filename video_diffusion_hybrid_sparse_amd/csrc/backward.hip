@@ -608,21 +608,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // stage j into buffer buf: waves 0 and 1 copy the 64 log-sum-exps / Deltas (one dword
   // per lane), every wave its share of the Q and dO rows
   const float* stat_src = wave == 0 ? a.lse : a.delta;
-  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+  auto issue_stats = [&](int j, int buf) __attribute__((always_inline)) {
     int start, valid;
     stage_at(j, start, valid);
     if (wave < 2) {
       const float* sb = stat_src + (size_t)start * g.H + h;
       dma4(sb, (uint32_t)imin(lane, valid - 1) * (uint32_t)g.H * 4, m0s + (uint32_t)buf * (2 * BQ * 4));
     }
+  };
+  // the Q and dO rows of a stage: prepared at the stage's start, issued half before each
+  // 32-query half (issued together they hold the wave behind the vector memory queue)
+  struct RowCopy {
+    const __bf16* qb;
+    const __bf16* ob;
+    int valid;
+    uint32_t m0;
+  };
+  auto prep_rows = [&](int j, int buf) __attribute__((always_inline)) {
+    int start, valid;
+    stage_at(j, start, valid);
     const size_t base = (size_t)start * rs + h * D;
+    // (wave-uniform: scalar registers, live through the half)
+    auto uni = [](const __bf16* p) __attribute__((always_inline)) {
+      const uint64_t v = reinterpret_cast<uint64_t>(p);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      return reinterpret_cast<const __bf16*>(((uint64_t)hi << 32) | lo);
+    };
+    return RowCopy{uni(a.q + base), uni(a.dO + base), __builtin_amdgcn_readfirstlane(valid),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(m0q + (uint32_t)buf * (2 * TB))};
+  };
+  auto copy_rows = [&](const RowCopy& c, int i) __attribute__((always_inline)) {
+    // (the lane's offsets are recomputed per copy: kept live through the loop they would
+    // push the registers past the file)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lrow = (wave * NI + i) * RPI + ln / CPR;
+    const uint32_t off = (uint32_t)imin(lrow, c.valid - 1) * rs2 + (uint32_t)((ln % CPR) ^ swz<CPR>(lrow)) * 16;
+    dma16(c.qb, off, c.m0 + i * RPI * D * 2);
+    dma16(c.ob, off, c.m0 + TB + i * RPI * D * 2);
+  };
+  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
+    issue_stats(j, buf);
+    const RowCopy c = prep_rows(j, buf);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int lrow = (wave * NI + i) * RPI + lane / CPR;
-      const uint32_t off = (uint32_t)imin(lrow, valid - 1) * rs2 + (uint32_t)((lane % CPR) ^ swz<CPR>(lrow)) * 16;
-      dma16(a.q + base, off, m0q + (uint32_t)buf * (2 * TB) + i * RPI * D * 2);
-      dma16(a.dO + base, off, m0q + (uint32_t)buf * (2 * TB) + TB + i * RPI * D * 2);
-    }
+    for (int i = 0; i < NI; ++i) copy_rows(c, i);
   };
   // per-lane LDS read addresses (buffer 0, Q, half 0), opaque to the compiler so that the
   // buffer, tensor, half and k-group terms become the reads' immediate offsets:
@@ -668,104 +697,151 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     asm volatile("s_nop 1" : "+a"(dv[dt][0]), "+a"(dv[dt][1]), "+a"(dk[dt][0]), "+a"(dk[dt][1]));
   const float c2 = a.c2;
 
-  // one 32-query half RT of the stage in buffer BUF (`valid` queries in the stage)
-  auto half_body = [&](auto bufc, auto rtc, int valid) __attribute__((always_inline)) {
+  // one 32-query half RT of the stage in buffer BUF (`valid` queries in the stage): a
+  // stream of 32 MFMA slots (two MFMAs each, one LDS operand each) in four steps,
+  //   1. S = Q K^T                      (slots 0-7:   Q row operands)
+  //   2. dP = dO V^T, beside P          (slots 8-15:  dO row operands)
+  //   3. dV^T += dO^T P, beside dS      (slots 16-23: dO^T by the transposing read)
+  //   4. dK^T += Q^T dS                 (slots 24-31: Q^T by the transposing read)
+  // so that the exponentials run beside the dP MFMAs and dS beside the dV MFMAs; LDS
+  // operands are read kLa slots ahead of their MFMAs.
+  auto half_body = [&](auto bufc, auto rtc, const RowCopy& cp) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value, RT = decltype(rtc)::value;
     constexpr uint32_t QOFF = BUF * 2 * TB + RT * 32 * D * 2, OOFF = QOFF + TB;
     constexpr uint32_t LOFF = BUF * 2 * BQ * 4 + RT * 32 * 4, DOFF = LOFF + BQ * 4;
+    constexpr int NS = 4 * KS;  // slots (KS = 2 DT)
+    constexpr int kLa = 2;      // operand reads ahead of their MFMAs
+    constexpr int NU = 8;       // vector units (key sub-tile t, row group r4) per step
+    // operand of slot n
+    auto fetch = [&](int n) __attribute__((always_inline)) {
+      if (n < KS) return *(lds_b128*)(uintptr_t)(rad[n] + QOFF);
+      if (n < 2 * KS) return *(lds_b128*)(uintptr_t)(rad[n - KS] + OOFF);
+      const uint32_t toff = n < 3 * KS ? OOFF : QOFF;
+      const int m = n % KS, G = m / DT, dt = m % DT;
+      const uint32_t go = 16 * G * D * 2;
+      const bf16x4 lo = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_b64*)(uintptr_t)(tad[dt][0] + toff + go)));
+      const bf16x4 hi = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_b64*)(uintptr_t)(tad[dt][1] + toff + go)));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 op[NS];
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const bf16x8 qa = *(lds_b128*)(uintptr_t)(rad[k] + QOFF);
-      const bf16x8 oa = *(lds_b128*)(uintptr_t)(rad[k] + OOFF);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (k == 0) {
-          mma_first(s[t], qa, kreg[t][k]);
-          mma_first(dp[t], oa, vreg[t][k]);
-        } else {
-          mma_v(s[t], qa, kreg[t][k]);
-          mma_v(dp[t], oa, vreg[t][k]);
-        }
-      }
-    }
-    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(dp[0]), "+v"(dp[1]));
-    // accumulator row r = query 32 RT + 8 (r/4) + 4 half + r%4 of the stage, column = key
     bf16x8 pb[2][2], sb[2][2];
-    const bool ragged = valid < 32 * (RT + 1);
+    f32x4 st[4];  // log-sum-exps (step 2), then Deltas (step 3), of rows 8 r4 + 4 half + e
+    // accumulator row r = query 32 RT + 8 (r/4) + 4 half + r%4 of the stage, column = key.
+    // P of unit u = (t, r4), packed into pb
+    auto p_unit = [&](int u) __attribute__((always_inline)) {
+      const int t = u & 1, r4 = u >> 1;
+      float p[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4 lv = *(lds_f4*)(uintptr_t)(sad + LOFF + 32 * r4);
-      const f32x4 dv4 = *(lds_f4*)(uintptr_t)(sad + DOFF + 32 * r4);
-      if (__builtin_expect(ragged, 0)) {
-        // queries past the stage's end: P = exp2(-inf) = 0, dS = 0
-        const int q0 = RT * 32 + 8 * r4 + 4 * half;
-        const float inf = __builtin_inff();
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[t][4 * r4 + e] * c2 - st[r4][e]);
+      uint4 w = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
+      if (r4 & 1) { w.z = pack_bf16x2(p[0], p[1]); w.w = pack_bf16x2(p[2], p[3]); }
+      else { w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]); }
+      pb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, w);
+    };
+    // dS = P (dP - Delta) of unit u, with P as packed (bf16), packed into sb
+    auto ds_unit = [&](int u) __attribute__((always_inline)) {
+      const int t = u & 1, r4 = u >> 1;
+      const uint4 w0 = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
+      const uint32_t plo = (r4 & 1) ? w0.z : w0.x, phi = (r4 & 1) ? w0.w : w0.y;
+      const float p[4] = {__builtin_bit_cast(float, plo << 16), __builtin_bit_cast(float, plo & 0xffff0000u),
+                          __builtin_bit_cast(float, phi << 16), __builtin_bit_cast(float, phi & 0xffff0000u)};
+      float ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lv[e] = q0 + e < valid ? lv[e] : inf;
-      }
-      const float lq[4] = {lv[0], lv[1], lv[2], lv[3]}, dq4[4] = {dv4[0], dv4[1], dv4[2], dv4[3]};
+      for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp[t][4 * r4 + e] - st[r4][e]);
+      uint4 w = __builtin_bit_cast(uint4, sb[t][r4 >> 1]);
+      if (r4 & 1) { w.z = pack_bf16x2(ds[0], ds[1]); w.w = pack_bf16x2(ds[2], ds[3]); }
+      else { w.x = pack_bf16x2(ds[0], ds[1]); w.y = pack_bf16x2(ds[2], ds[3]); }
+      sb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, w);
+    };
+    auto load_stats = [&](uint32_t off) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float p[4], ds[4];
+      for (int r4 = 0; r4 < 4; ++r4) st[r4] = *(lds_f4*)(uintptr_t)(sad + off + 32 * r4);
+    };
+    // this half's share of the next stage's row copies (inside the slot stream they make
+    // the register allocator move the dK/dV accumulators through scratch memory)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          p[e] = __builtin_amdgcn_exp2f(s[t][r] * c2 - lq[e]);
-          ds[e] = p[e] * (dp[t][r] - dq4[e]);
-        }
-        uint4 wp = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
-        uint4 ws = __builtin_bit_cast(uint4, sb[t][r4 >> 1]);
-        if (r4 & 1) {
-          wp.z = pack_bf16x2(p[0], p[1]); wp.w = pack_bf16x2(p[2], p[3]);
-          ws.z = pack_bf16x2(ds[0], ds[1]); ws.w = pack_bf16x2(ds[2], ds[3]);
-        } else {
-          wp.x = pack_bf16x2(p[0], p[1]); wp.y = pack_bf16x2(p[2], p[3]);
-          ws.x = pack_bf16x2(ds[0], ds[1]); ws.y = pack_bf16x2(ds[2], ds[3]);
-        }
-        pb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, wp);
-        sb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, ws);
-      }
-    }
-    asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(sb[0][0]),
-                 "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
+    for (int i = RT * NI / 2; i < (RT + 1) * NI / 2; ++i) copy_rows(cp, i);
 #pragma unroll
-    for (int G = 0; G < 2; ++G)
+    for (int n = 0; n < kLa; ++n) op[n] = fetch(n);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint32_t go = 16 * G * D * 2;
-        const bf16x4 olo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                          (lds_b64*)(uintptr_t)(tad[dt][0] + OOFF + go)));
-        const bf16x4 ohi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                          (lds_b64*)(uintptr_t)(tad[dt][1] + OOFF + go)));
-        const bf16x8 oa = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
-        const bf16x4 qlo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                          (lds_b64*)(uintptr_t)(tad[dt][0] + QOFF + go)));
-        const bf16x4 qhi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                          (lds_b64*)(uintptr_t)(tad[dt][1] + QOFF + go)));
-        const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+    for (int n = 0; n < NS; ++n) {
+      if (n + kLa < NS) op[n + kLa] = fetch(n + kLa);
+      const int m = n % KS;
+      if (n < KS) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          mma_a(dv[dt][t], oa, pb[t][G]);  // dV^T += dO^T P
-          mma_a(dk[dt][t], qa, sb[t][G]);  // dK^T += Q^T dS
+          if (m == 0) mma_first(s[t], op[n], kreg[t][m]);
+          else mma_v(s[t], op[n], kreg[t][m]);
         }
+        if (n == KS - 1) load_stats(LOFF);
+      } else if (n < 2 * KS) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (m == 0) mma_first(dp[t], op[n], vreg[t][m]);
+          else mma_v(dp[t], op[n], vreg[t][m]);
+        }
+        // the scores' last MFMAs, before the vector unit reads them
+        if (m == 0) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+        else {
+#pragma unroll
+          for (int u = NU * (m - 1) / (KS - 1); u < NU * m / (KS - 1); ++u) p_unit(u);
+        }
+        if (m == KS - 1) {
+          // vector writes of P, read next by MFMAs; the Deltas replace the log-sum-exps
+          asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
+          load_stats(DOFF);
+        }
+      } else if (n < 3 * KS) {
+        const int G = m / DT, dt = m % DT;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) mma_a(dv[dt][t], op[n], pb[t][G]);  // dV^T += dO^T P
+        if (m == 0) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(dp[0]), "+v"(dp[1]));
+        else {
+#pragma unroll
+          for (int u = NU * (m - 1) / (KS - 1); u < NU * m / (KS - 1); ++u) ds_unit(u);
+        }
+        if (m == KS - 1) asm volatile("s_nop 1" : "+v"(sb[0][0]), "+v"(sb[0][1]), "+v"(sb[1][0]), "+v"(sb[1][1]));
+      } else {
+        const int G = m / DT, dt = m % DT;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) mma_a(dk[dt][t], op[n], sb[t][G]);  // dK^T += Q^T dS
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // queries past a ragged stage's end get log-sum-exp +inf (P = exp2(-inf) = 0, dS = 0):
+  // written over the copied (repeated) values by the wave that copied them, after its
+  // copy landed and before the barrier that publishes the stage
+  auto inf_tail = [&](int j, int buf) __attribute__((always_inline)) {
+    if (wave == 0) {
+      int start, valid;
+      stage_at(j, start, valid);
+      if (lane >= valid) ST[buf][0][lane] = __builtin_inff();
+    }
   };
   // stage j in buffer BUF: copy stage j + 1 into the other buffer (free since the last
   // barrier), run the halves, wait for the copy, barrier
   auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
-    if (j + 1 < nst) issue(j + 1, BUF ^ 1);
-    int start, valid;
-    stage_at(j, start, valid);
-    half_body(bufc, std::integral_constant<int, 0>{}, valid);
-    if (valid > 32) half_body(bufc, std::integral_constant<int, 1>{}, valid);
+    // (after the last stage, its rows again into the free buffer: no branch in the half)
+    if (j + 1 < nst) issue_stats(j + 1, BUF ^ 1);
+    const RowCopy cp = prep_rows(imin(j + 1, nst - 1), BUF ^ 1);
+    // both halves always (a stage of at most 32 queries gives its second half P = dS = 0
+    // through the +inf log-sum-exps): a branch here makes the register allocator move the
+    // dK/dV accumulators through scratch memory
+    half_body(bufc, std::integral_constant<int, 0>{}, cp);
+    half_body(bufc, std::integral_constant<int, 1>{}, cp);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (j + 1 < nst) inf_tail(j + 1, BUF ^ 1);
     __syncthreads();
   };
 
   if (nst > 0) issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (nst > 0) inf_tail(0, 0);
   __syncthreads();
   for (int j = 0; j < nst; j += 2) {
     stage(j, std::integral_constant<int, 0>{});
