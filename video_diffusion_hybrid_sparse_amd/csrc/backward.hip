@@ -494,8 +494,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // matrix registers.  Queries stream through LDS in 64-query stages (double-buffered),
 // with their log-sum-exp and Delta; each stage runs as two 32-query halves.  Per half:
 // S = Q K^T and dP = dO V^T (Q and dO rows from LDS are the A operands, each feeding both
-// 32-key sub-tiles); P = exp2(S c2 - lse), dS = P (dP - Delta); dV^T += dO^T P and
-// dK^T += Q^T dS (dO^T and Q^T by the transposing LDS read, each feeding both sub-tiles).
+// 32-key sub-tiles); P = exp2(S c2 - lse), dS = P (dP - Delta) with P as rounded to
+// bf16 for dV; dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by the transposing LDS
+// read, each feeding both sub-tiles).
 // Per (query, key) pair 8 d multiply-adds against 10 d for separate dV and dK passes,
 // and every LDS operand read feeds two MFMAs.  The stage loop is unrolled over the two
 // buffers and the halves, so every LDS read is one per-lane base register plus an
