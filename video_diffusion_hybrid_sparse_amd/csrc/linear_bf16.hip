@@ -172,8 +172,10 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 //
 // One workgroup = up to 1024 query tokens of one query group and one head (the states'
 // load and split is paid once per 1024 tokens); each of its 8 waves walks 32-token
-// sub-tiles (the 64 KB of LDS allow two workgroups per CU, so 16 waves keep loads in
-// flight).  The group's two states are summed in float32 (the
+// sub-tiles, loading the next sub-tile's rows while it computes the current one.  That
+// takes about 250 registers per lane, so one workgroup runs per CU (capped at 128
+// registers without the early loads, two workgroups per CU ran 13% slower).  The
+// group's two states are summed in float32 (the
 // identity feature map makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding
 // differs), split into bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled
 // 16-byte chunks) in LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes
