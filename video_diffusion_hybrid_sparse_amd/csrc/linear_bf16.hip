@@ -202,6 +202,28 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
   const size_t rs = (size_t)g.H * D;
   const size_t hs = (size_t)h * D * D;
 
+  // The query and gate rows of a wave's next sub-tile are loaded while it computes the
+  // current one (each wave walks its sub-tiles one after another, so otherwise every
+  // sub-tile waits for its own loads).
+  auto row_of = [&](int st) __attribute__((always_inline)) {
+    const int tok = t0 + st * 32 + l32;
+    return (size_t)(tok < t1 ? tok : t1 - 1) * rs + h * D;
+  };
+  bf16x8 qn[KS];
+  uint4 gn[DT][2];
+  auto load_rows = [&](int st) __attribute__((always_inline)) {
+    const size_t qrow = row_of(st);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qn[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+        gn[dt][ip] = *reinterpret_cast<const uint4*>(a.gl + qrow + 32 * dt + 16 * ip + 8 * half);
+  };
+  // (the first sub-tile's rows are in flight during the state prologue)
+  if (wave * 32 < t1 - t0) load_rows(wave);
+
   // S_sum = S_fwd + S_bwd (anchors: text/2 + text/2) into LDS as bf16 hi + lo
   {
     const float* ta = a.Stext + hs;
@@ -244,26 +266,6 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
     }
   const float* wrow = a.w + h * D;
 
-  // The query and gate rows of a wave's next sub-tile are loaded while it computes the
-  // current one (each wave walks its sub-tiles one after another, so otherwise every
-  // sub-tile waits for its own loads).
-  auto row_of = [&](int st) __attribute__((always_inline)) {
-    const int tok = t0 + st * 32 + l32;
-    return (size_t)(tok < t1 ? tok : t1 - 1) * rs + h * D;
-  };
-  bf16x8 qn[KS];
-  uint4 gn[DT][2];
-  auto load_rows = [&](int st) __attribute__((always_inline)) {
-    const size_t qrow = row_of(st);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qn[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int ip = 0; ip < 2; ++ip)
-        gn[dt][ip] = *reinterpret_cast<const uint4*>(a.gl + qrow + 32 * dt + 16 * ip + 8 * half);
-  };
-  if (wave * 32 < t1 - t0) load_rows(wave);
 
   for (int st = wave; st * 32 < t1 - t0; st += NW) {
     const int tok = t0 + st * 32 + l32;
