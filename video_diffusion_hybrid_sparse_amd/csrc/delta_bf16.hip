@@ -16,18 +16,20 @@
 // chunk c reads the forward state after the frames before its window and the backward
 // state after the frames behind it, so only states at chunk boundaries are stored.
 //
-// Work split: one workgroup per (head, direction, 64 value columns); wave w owns 16 value
-// columns.  A value column of S evolves independently of the others, so no reduction
-// crosses waves.  Per 64-token tile (HBM -> LDS copies three tiles ahead, four buffers):
+// Work split: one workgroup per (head, direction, 64 value columns), eight waves in two
+// groups of four; wave wq of a group owns 16 value columns.  A value column of S evolves
+// independently of the others, and S is fixed over a frame, so a frame's tiles are
+// independent: the two groups take alternate tiles (two waves per SIMD), and at the end
+// of a frame group 1's dS is added to group 0's through LDS.  Per 64-token tile (HBM ->
+// LDS copies one step ahead, two buffers per group):
 //   W  = K S          16x16x32 MFMAs, S as the B operand split into bf16 hi + lo;
 //   R' = (V - W / |k|) / |k|   per token (zero for rows past the block);
 //   dS += K^T R'      A operand read with the transposing LDS read in the token order
 //                     the W accumulators hold, R' split into bf16 hi + lo.
 // K stays exact bf16 in both products; the key normalisation is applied in fp32 to W and
-// R'.  After a frame, S += (beta / T) dS in fp32 registers.  Copies three tiles ahead and
-// one barrier per tile measured level with double buffering and two barriers (2.35 ms
-// for both recurrences at 768p): a tile's dependent chain (LDS reads, K S, R', K^T R')
-// bounds it, with one wave per SIMD on 768 of the 1024 SIMDs.
+// R'.  After a frame, S += (beta / T) dS in fp32 registers.  The recurrence is bound by a
+// tile's dependent chain (LDS reads, K S, R', K^T R'): one group of four waves walking
+// every tile took 2.38 ms for both recurrences at 768p, the two groups take 1.78 ms.
 #include "kernels.h"
 
 namespace vdn {
@@ -58,45 +60,54 @@ __device__ __forceinline__ int bwd_frames_taken(const Geo& g, int c) { return im
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
+__global__ __launch_bounds__(512) void delta_bf16_kernel(DeltaArgs a) {
   constexpr int TT = 64;                  // tokens per tile
   constexpr int VC = 64;                  // value columns per workgroup
   constexpr int CPR = D / 8;              // 16-byte chunks per K row
   constexpr int NT = D / 16;              // 16-row tiles of the state (key dims)
   constexpr int KS1 = D / 32;             // 32-dim k-steps of K S
-  constexpr int NKI = TT * CPR / 256;     // K-tile copies per thread
+  constexpr int NKI = TT * CPR / 256;     // K-tile copies per thread (a group's 256 threads)
   constexpr int NVI = TT * (VC / 8) / 256;  // V-tile copies per thread
   constexpr int SXS = D + 4;              // padded column stride of the state transfer buffer
-  constexpr int NB = 4;                   // tile buffers: tiles j + 1 .. j + 3 in flight during tile j
+  constexpr int NB = 2;                   // tile buffers per group: the next step's tile in flight
   static_assert(NKI >= 1 && NVI >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) __bf16 Kt[NB][TT * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[NB][TT * VC];
+  __shared__ __attribute__((aligned(16))) __bf16 Kt[2][NB][TT * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][NB][TT * VC];
   __shared__ __attribute__((aligned(16))) float Sx[4][16 * SXS];
-  __shared__ __attribute__((aligned(16))) float invs[NB][TT];
+  __shared__ __attribute__((aligned(16))) float invs[2][NB][TT];
 
   const Geo g = a.geo;
   const int h = blockIdx.x, dir = blockIdx.y, slice = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  // two groups of four waves take alternate tiles of a block; wave wq of a group owns
+  // value columns 16 wq .. 16 wq + 15 of the slice
+  const int grp = wave >> 2, wq = wave & 3, gt = tid & 255;
   const size_t rs = (size_t)g.H * D;
   const int vcol0 = slice * VC;
 
-  // Tile walk: text tiles first, then the frames in direction order.  The source of a
-  // tile is the video tensor plus a byte offset (text: the offset to the text tensor).
+  // Blocks: the text tiles, then the frames in direction order.  Step s gives a block's
+  // tiles 2 p (group 0) and 2 p + 1 (group 1); a group without a tile in the block's last
+  // step copies its partner's tile and computes it with no valid rows (R' = 0).
   const int ntx = (g.L + TT - 1) / TT;
   const int tpf = (g.T + TT - 1) / TT;
-  const int ntiles = ntx + (g.F - 2) * tpf;
+  const int stx = (ntx + 1) / 2, spf = (tpf + 1) / 2;
+  const int nsteps = stx + (g.F - 2) * spf;
   const intptr_t tk_off = reinterpret_cast<intptr_t>(a.tk) - reinterpret_cast<intptr_t>(a.k);
   const intptr_t tv_off = reinterpret_cast<intptr_t>(a.tv) - reinterpret_cast<intptr_t>(a.v);
-  auto tile_at = [&](int j, int& first_row, int& valid, bool& text) __attribute__((always_inline)) {
-    text = j < ntx;
+  // tile of group gr in step s: first row, rows to copy, rows that count (0: none)
+  auto tile_at = [&](int s, int gr, int& first_row, int& rows, int& valid, bool& text) __attribute__((always_inline)) {
+    text = s < stx;
     if (text) {
-      first_row = j * TT;
-      valid = imin(TT, g.L - first_row);
+      const int j = 2 * s + gr, jj = j < ntx ? j : j - 1;
+      first_row = jj * TT;
+      rows = imin(TT, g.L - first_row);
+      valid = j < ntx ? rows : 0;
     } else {
-      const int jj = j - ntx, fi = jj / tpf, tt = jj - fi * tpf;
+      const int ss = s - stx, fi = ss / spf, t = 2 * (ss - fi * spf) + gr, tt = t < tpf ? t : t - 1;
       const int frame = dir == 0 ? 1 + fi : g.F - 2 - fi;
       first_row = frame * g.T + tt * TT;
-      valid = imin(TT, g.T - tt * TT);
+      rows = imin(TT, g.T - tt * TT);
+      valid = t < tpf ? rows : 0;
     }
   };
   // Tile copies as untracked LDS DMA (dma16: the compiler does not wait for them before
@@ -105,13 +116,13 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
   // swizzled chunk).  Rows past the block are copies, zeroed in R'.
   const uint32_t rs2 = (uint32_t)rs * 2;
   const uint32_t m0k = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Kt[0][0] + wave * 64 * 16);
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Kt[grp][0][0] + wq * 64 * 16);
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vt[0][0] + wave * 64 * 16);
-  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
-    int first, valid;
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Vt[grp][0][0] + wq * 64 * 16);
+  auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+    int first, rows, valid;
     bool text;
-    tile_at(j, first, valid, text);
+    tile_at(s, grp, first, rows, valid, text);
     const size_t base = (size_t)first * rs + h * D;
     const __bf16* kb = static_cast<const __bf16*>(uniform_ptr(
         reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.k) + (text ? tk_off : 0)) + base));
@@ -119,14 +130,14 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
         reinterpret_cast<const __bf16*>(reinterpret_cast<intptr_t>(a.v) + (text ? tv_off : 0)) + base + vcol0));
 #pragma unroll
     for (int i = 0; i < NKI; ++i) {
-      const int q = i * 256 + tid, row = q / CPR, c = q % CPR;
-      dma16(kb, (uint32_t)imin(row, valid - 1) * rs2 + (uint32_t)(c ^ swz<CPR>(row)) * 16,
+      const int q = i * 256 + gt, row = q / CPR, c = q % CPR;
+      dma16(kb, (uint32_t)imin(row, rows - 1) * rs2 + (uint32_t)(c ^ swz<CPR>(row)) * 16,
             m0k + (uint32_t)buf * (TT * D * 2) + i * 256 * 16);
     }
 #pragma unroll
     for (int i = 0; i < NVI; ++i) {
-      const int q = i * 256 + tid, row = q / 8, c = q % 8;
-      dma16(vb, (uint32_t)imin(row, valid - 1) * rs2 + (uint32_t)(c ^ swz<8>(row)) * 16,
+      const int q = i * 256 + gt, row = q / 8, c = q % 8;
+      dma16(vb, (uint32_t)imin(row, rows - 1) * rs2 + (uint32_t)(c ^ swz<8>(row)) * 16,
             m0v + (uint32_t)buf * (TT * VC * 2) + i * 256 * 16);
     }
   };
@@ -139,21 +150,27 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
   // dS += K^T R': transposing reads; source lane l16 points at token K0 + l16/4 and dims
   // 16 dt + 4 (l16 & 3) .. +3, with K0 = 32 s + 16 c + 4 g4; lane j receives dim 16 dt + j
   // of tokens K0 .. K0 + 3.
-  int k2off[NT][2];
+  // (offsets formed at each read from a per-row base and swizzle: a table of all 2 NT
+  // would hold registers the two waves per SIMD do not have)
+  int k2base[2], k2swz[2];
+  const int k2b = (l16 & 3) >> 1;  // chunk bit of the lane's dims inside a 16-dim group
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int row = 16 * c + 4 * g4 + (l16 >> 2), col = 16 * dt + 4 * (l16 & 3);
-      k2off[dt][c] = row * D + (((col >> 3) ^ swz<CPR>(row)) * 8) + (col & 7);
-    }
-  // V values in the W accumulator layout (tokens 16 rt + 4 g4 + r, column 16 wave + l16)
+  for (int c = 0; c < 2; ++c) {
+    const int row = 16 * c + 4 * g4 + (l16 >> 2);
+    k2base[c] = row * D + 4 * (l16 & 1);
+    k2swz[c] = swz<CPR>(row);
+  }
+  auto k2off = [&](int dt, int c) __attribute__((always_inline)) {
+    return k2base[c] + (((2 * dt + k2b) ^ k2swz[c]) * 8);
+  };
+  // V values in the W accumulator layout (tokens 16 rt + 4 g4 + r, column 16 wq + l16)
   int voff;
   {
-    const int row = 4 * g4 + (l16 >> 2), col = 16 * wave + 4 * (l16 & 3);
+    const int row = 4 * g4 + (l16 >> 2), col = 16 * wq + 4 * (l16 & 3);
     voff = row * VC + (((col >> 3) ^ swz<8>(row)) * 8) + (col & 7);
   }
 
+  // S lives in group 0 (group 1 keeps only its operand form); dS is each group's part
   f32x4 S[NT], dS[NT];
   bf16x8 sbh[KS1], sbl[KS1];
 #pragma unroll
@@ -167,15 +184,15 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
     sbl[s] = bf16x8{};
   }
 
-  float* sx = Sx[wave];
-  // S (accumulator layout: dim 16 t + 4 g4 + r, column l16) -> B operand (dims 32 s + 8 g4
-  // .. +7 of column l16) as bf16 hi + lo, through this wave's transfer buffer
-  auto rebuild_operand = [&]() __attribute__((always_inline)) {
+  // accumulator layout (dim 16 t + 4 g4 + r, column l16) to and from this column
+  // quarter's transfer buffer
+  float* sx = Sx[wq];
+  auto put = [&](const f32x4 (&x)[NT]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<f32x4*>(&sx[l16 * SXS + 16 * t + 4 * g4]) = S[t];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(&sx[l16 * SXS + 16 * t + 4 * g4]) = x[t];
+  };
+  // the B operand (dims 32 s + 8 g4 .. +7 of column l16) as bf16 hi + lo, from the buffer
+  auto load_operand = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < KS1; ++s) {
       const f32x4 x0 = *reinterpret_cast<const f32x4*>(&sx[l16 * SXS + 32 * s + 8 * g4]);
@@ -188,8 +205,6 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
         sbl[s][e] = (__bf16)(xv[e] - (float)hi);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
   };
   // store S into the states of every chunk that reads it after `taken` frames
   auto store_states = [&](int taken) __attribute__((always_inline)) {
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
     for (int c = 0; c < g.nC; ++c) {
       const int need = dir == 0 ? fwd_frames_taken(g, c) : bwd_frames_taken(g, c);
       if (need != taken) continue;
-      float* dst = base + ((size_t)c * g.H + h) * D * D + vcol0 + 16 * wave + l16;
+      float* dst = base + ((size_t)c * g.H + h) * D * D + vcol0 + 16 * wq + l16;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -205,10 +220,10 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
     }
   };
 
-  // 1 / sqrt(|k|^2 + eps_phi) for the key rows this thread's wave copied into buffer b:
-  // copy i of thread tid filled 16-byte slot i 256 + tid of the tile (row (i 256 + tid) /
-  // CPR), and the CPR lanes of a row are consecutive lanes of one wave, so the wave needs
-  // only its own copies to have landed
+  // 1 / sqrt(|k|^2 + eps_phi) for the key rows this wave copied into buffer b of its
+  // group: copy i of group thread gt filled 16-byte slot i 256 + gt of the tile (row
+  // (i 256 + gt) / CPR), and the CPR lanes of a row are consecutive lanes of one wave, so
+  // the wave needs only its own copies to have landed
   // (the CPR partial sums of a row are added by DPP lane moves inside each 16-lane row:
   // lane swaps within pairs and quads, then the half-row and row mirrors)
   auto row_sum = [](float v) __attribute__((always_inline)) {
@@ -222,35 +237,34 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
   auto key_norms = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NKI; ++i) {
-      const int q = i * 256 + tid;
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(&Kt[b][q * 8]);
+      const int q = i * 256 + gt;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(&Kt[grp][b][q * 8]);
       float ss = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += (float)x[e] * (float)x[e];
       ss = row_sum(ss);
-      if (q % CPR == 0) invs[b][q / CPR] = __builtin_amdgcn_rsqf(ss + kEpsPhi);
+      if (q % CPR == 0) invs[grp][b][q / CPR] = __builtin_amdgcn_rsqf(ss + kEpsPhi);
     }
   };
 
-  if (ntx == 0) store_states(0);  // no text: both recurrences start at zero
-  // Tiles 0 .. NB - 2 in flight; tile j + NB - 1 is issued at the start of tile j (past the
-  // last tile: the last tile again, so that every tile issues the same copies and the
-  // waits count alike).  Before the barrier that ends tile j, each wave's copies of tile
-  // j + 1 have landed (the NB - 2 tiles after it may still be in flight: loads complete
-  // in issue order) and it has written their key norms, so each tile takes one barrier.
-  constexpr int kTileOps = NKI + NVI;
-#pragma unroll
-  for (int t = 0; t < NB - 1; ++t) issue(imin(t, ntiles - 1), t);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * kTileOps) : "memory");
+  if (ntx == 0 && grp == 0) store_states(0);  // no text: both recurrences start at zero
+  // Step 0's tiles in flight and landed; step s + 1's are issued at the start of step s
+  // (past the last step: the last step's again, so every step issues the same copies) and
+  // have landed, with their key norms written, before the barrier that ends step s.
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   key_norms(0);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & (NB - 1);
-    issue(imin(j + NB - 1, ntiles - 1), (j + NB - 1) & (NB - 1));
-    int first, valid;
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & (NB - 1);
+    issue(imin(s + 1, nsteps - 1), (s + 1) & (NB - 1));
+    int first, rows, valid;
     bool text;
-    tile_at(j, first, valid, text);
+    tile_at(s, grp, first, rows, valid, text);
+    const __bf16* kt = Kt[grp][buf];
+    const __bf16* vt = Vt[grp][buf];
+    const float* iv = invs[grp][buf];
 
     // W = K S and R' for the four 16-token row tiles; R' goes straight into B operands
     bf16x8 rbh[2], rbl[2];
@@ -258,13 +272,13 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
     for (int rt = 0; rt < 4; ++rt) {
       f32x4 w = 0.0f;
 #pragma unroll
-      for (int s = 0; s < KS1; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[buf][rt * 16 * D + k1off[s]]);
-        w = mfma16x16x32(ka, sbh[s], w);
-        w = mfma16x16x32(ka, sbl[s], w);
+      for (int ks = 0; ks < KS1; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kt[rt * 16 * D + k1off[ks]]);
+        w = mfma16x16x32(ka, sbh[ks], w);
+        w = mfma16x16x32(ka, sbl[ks], w);
       }
-      const bf16x4 vv = lds_read_tr(&Vt[buf][rt * 16 * VC + voff]);
-      const f32x4 inv = *reinterpret_cast<const f32x4*>(&invs[buf][16 * rt + 4 * g4]);
+      const bf16x4 vv = lds_read_tr(&vt[rt * 16 * VC + voff]);
+      const f32x4 inv = *reinterpret_cast<const f32x4*>(&iv[16 * rt + 4 * g4]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = 16 * rt + 4 * g4 + r;
@@ -276,53 +290,67 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
     }
     // dS += K^T R' over the tile's two 32-token k-steps
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
-        const bf16x4 lo = lds_read_tr(&Kt[buf][32 * s * D + k2off[dt][0]]);
-        const bf16x4 hi = lds_read_tr(&Kt[buf][32 * s * D + k2off[dt][1]]);
+        const bf16x4 lo = lds_read_tr(&kt[32 * ks * D + k2off(dt, 0)]);
+        const bf16x4 hi = lds_read_tr(&kt[32 * ks * D + k2off(dt, 1)]);
         const bf16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dS[dt] = mfma16x16x32(ka, rbh[s], dS[dt]);
-        dS[dt] = mfma16x16x32(ka, rbl[s], dS[dt]);
+        dS[dt] = mfma16x16x32(ka, rbh[ks], dS[dt]);
+        dS[dt] = mfma16x16x32(ka, rbl[ks], dS[dt]);
       }
 
-    // end of a block: fold dS into S, store chunk-boundary states, refresh the operand
-    const bool text_end = text && j == ntx - 1;
-    const bool frame_end = !text && (j - ntx) % tpf == tpf - 1;
+    // end of a block: group 1's dS joins group 0's, which folds it into S and stores the
+    // chunk-boundary states; both groups then take the new S as their operand
+    const bool text_end = text && s == stx - 1;
+    const bool frame_end = !text && (s - stx) % spf == spf - 1;
     if (text_end || frame_end) {
-      if (text_end) {
-        const float w = a.beta / (float)g.L;
-        // the text state (anchors read it, half from each side)
-        if (dir == 0) {
-          float* dst = a.Stext + (size_t)h * D * D + vcol0 + 16 * wave + l16;
+      if (grp == 1) {
+        put(dS);
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t) dS[t] = 0.0f;
+      }
+      __syncthreads();
+      if (grp == 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(size_t)(16 * t + 4 * g4 + r) * D] = w * dS[t][r];
+        for (int t = 0; t < NT; ++t)
+          dS[t] += *reinterpret_cast<const f32x4*>(&sx[l16 * SXS + 16 * t + 4 * g4]);
+        if (text_end) {
+          const float w = a.beta / (float)g.L;
+          // the text state (anchors read it, half from each side)
+          if (dir == 0) {
+            float* dst = a.Stext + (size_t)h * D * D + vcol0 + 16 * wq + l16;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) dst[(size_t)(16 * t + 4 * g4 + r) * D] = w * dS[t][r];
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) S[t] = (0.5f * w) * dS[t];
+        } else {
+          const float w = a.beta / (float)g.T;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) S[t] += w * dS[t];
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) S[t] = (0.5f * w) * dS[t];
-      } else {
-        const float w = a.beta / (float)g.T;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) S[t] += w * dS[t];
+        for (int t = 0; t < NT; ++t) dS[t] = 0.0f;
+        store_states(text_end ? 0 : (s - stx) / spf + 1);
+        put(S);
       }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) dS[t] = 0.0f;
-      store_states(text_end ? 0 : (j - ntx) / tpf + 1);
-      rebuild_operand();
+      __syncthreads();
+      load_operand();
     }
 
-    // this wave's copies of tile j + 1 landed and their key norms written; after the
-    // barrier every wave's are, and every wave is done with tile j (its buffer takes the
-    // copy issued at the start of tile j + 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * kTileOps) : "memory");
-    key_norms((j + 1) & (NB - 1));
+    // this wave's copies of step s + 1 landed and their key norms written; after the
+    // barrier every wave's are, and every wave is done with step s (its buffers take the
+    // copies issued at the start of step s + 1; the transfer buffer is next written at
+    // the next block's end, many barriers later)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    key_norms((s + 1) & (NB - 1));
     __syncthreads();
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (ntx == 0 && dir == 0) {
-    float* dst = a.Stext + (size_t)h * D * D + vcol0 + 16 * wave + l16;
+  if (ntx == 0 && dir == 0 && grp == 0) {
+    float* dst = a.Stext + (size_t)h * D * D + vcol0 + 16 * wq + l16;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -333,7 +361,7 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(DeltaArgs a) {
 hipError_t launch_delta_bf16(const DeltaArgs& a, hipStream_t stream) {
   const int d = a.geo.d;
   if (d != 64 && d != 128) return hipErrorInvalidValue;
-  dim3 grid(a.geo.H, 2, d / 64), block(256);
+  dim3 grid(a.geo.H, 2, d / 64), block(512);
   if (d == 128)
     hipLaunchKernelGGL(delta_bf16_kernel<128>, grid, block, 0, stream, a);
   else
