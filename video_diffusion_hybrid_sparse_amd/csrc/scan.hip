@@ -109,7 +109,9 @@ __global__ __launch_bounds__(256) void scan_lds_kernel(ScanArgs a) {
       const int f = j * g.C + k;
       const bool counts = live && j < g.nC && k < g.C && f < g.F && !is_anchor(g, f);
       const uint32_t off = counts ? (uint32_t)((f * n4 + e) * 16) : 0x80000000u;
-      acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      // (non-temporal, cache policy bit 1: each frame state is read once, and a miss
+      // must not evict the states still to be read when they outgrow the last-level cache)
+      acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
     }
     csum[j][lane] = acc;
   }
