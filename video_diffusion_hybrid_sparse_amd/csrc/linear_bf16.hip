@@ -175,25 +175,33 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 //
 // One workgroup = up to 1024 query tokens of one query group and one head (the states'
 // load and split is paid once per 1024 tokens); each of its 8 waves walks 32-token
-// sub-tiles, loading the next sub-tile's rows while it computes the current one.  That
-// takes about 250 registers per lane, so one workgroup runs per CU (capped at 128
-// registers without the early loads, two workgroups per CU ran 13% slower).  The
-// group's two states are summed in float32 (the
-// identity feature map makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding
-// differs), split into bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled
-// 16-byte chunks) in LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes
-// with float32 accumulation (about 16 mantissa bits of the state kept); the S^T operand is
-// gathered with the transposing LDS read.  A lane owns one token, so RMSNorm needs one
-// lane-pair sum; a lane-pair swap then gives each lane 8 contiguous channels, so gate
-// loads and output stores are 16 bytes wide.  A wave's next query and gate rows are in
-// flight while it computes the current sub-tile.
+// sub-tiles.  The group's two states are summed in float32 (the identity feature map
+// makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding differs), split into
+// bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled 16-byte chunks) in
+// LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes with float32
+// accumulation (about 16 mantissa bits of the state kept); the S^T operand is gathered
+// with the transposing LDS read.
+//
+// A sub-tile's query rows go from HBM straight into the wave's own LDS buffer (buffer
+// loads with the LDS bit, four whole 256-byte rows per instruction; rows past the tile's
+// last token lie beyond the buffer resource's extent and read as zeros), copied while the
+// wave computes the sub-tile before; the MFMA operands are then read from LDS.  Loaded as
+// MFMA operands straight from HBM instead, every load instruction touched 32 rows at 32
+// bytes each.  The gate rows of the next sub-tile are loaded into registers beside the
+// copy.  A lane owns one token, so RMSNorm needs one lane-pair sum; a lane-pair swap then
+// gives each lane 8 contiguous channels, so gate loads and output stores are 16 bytes wide.
 constexpr int kReadWaves = 8;  // waves per readout workgroup (8: 7% faster than 4)
 
 template <int D>
 __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
   constexpr int BM = 1024, KS = D / 16, DT = D / 32, CPR = D / 8, NW = kReadWaves, NT = 64 * NW;
+  constexpr int RPI = 64 / CPR;   // query rows one copy instruction covers
+  constexpr int NQ = 32 / RPI;    // copy instructions per lane and sub-tile
+  constexpr int NG = 2 * DT;      // gate loads per lane and sub-tile
   __shared__ __attribute__((aligned(16))) __bf16 Shi[D * D];
   __shared__ __attribute__((aligned(16))) __bf16 Slo[D * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[NW][32 * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Os[NW][32 * 64];
   const Geo g = a.geo;
   // (tiles vary fastest: 2% faster than heads fastest; tiles of one group, which share
   // its state pair, run side by side)
@@ -205,19 +213,30 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
   const size_t rs = (size_t)g.H * D;
   const size_t hs = (size_t)h * D * D;
 
-  // The query and gate rows of a wave's next sub-tile are loaded while it computes the
-  // current one (each wave walks its sub-tiles one after another, so otherwise every
-  // sub-tile waits for its own loads).
   auto row_of = [&](int st) __attribute__((always_inline)) {
     const int tok = t0 + st * 32 + l32;
     return (size_t)(tok < t1 ? tok : t1 - 1) * rs + h * D;
   };
-  bf16x8 qn[KS];
-  uint4 gn[DT][2];
-  auto load_rows = [&](int st) __attribute__((always_inline)) {
-    const size_t qrow = row_of(st);
+  // query rows of the tile through a raw buffer whose extent ends at the tile's last row
+  // (byte offsets fit 32 bits: at most 1024 rows of the token row stride H d 2)
+  const uint32_t rsb = (uint32_t)rs * 2;
+  const i32x4 rq = raw_buffer(a.q + (size_t)t0 * rs + h * D, (uint32_t)(t1 - t0 - 1) * rsb + D * 2);
+  uint32_t qoff[NQ];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qn[s] = load_bf16x8(a.q + qrow + half * 8 + 16 * s);
+  for (int i = 0; i < NQ; ++i) {
+    const int r = i * RPI + lane / CPR;
+    qoff[i] = (uint32_t)r * rsb + (uint32_t)((lane % CPR) ^ swz<CPR>(r)) * 16;
+  }
+  const uint32_t m0q = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Qs[0][0] + wave * 32 * D * 2);
+  uint4 gn[DT][2];
+  // sub-tile st: its query rows into this wave's buffer, its gate rows into gn (the copy
+  // first: the wait for it counts the NG gate loads issued after it)
+  auto fetch = [&](int st) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)st * 32 * rsb;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) dma16_buf(rq, base + qoff[i], m0q + i * RPI * D * 2);
+    const size_t qrow = row_of(st);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
         gn[dt][ip] = *reinterpret_cast<const uint4*>(a.gl + qrow + 32 * dt + 16 * ip + 8 * half);
   };
   // (the first sub-tile's rows are in flight during the state prologue)
-  if (wave * 32 < t1 - t0) load_rows(wave);
+  if (wave * 32 < t1 - t0) fetch(wave);
 
   // S_sum = S_fwd + S_bwd (anchors: text/2 + text/2) into LDS as bf16 hi + lo
   {
@@ -267,22 +286,32 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
       const int col = 32 * dt + 16 * (grp16 & 1) + 4 * (i16 & 3);
       srd[dt][c] = row * D + (((col >> 3) ^ swz<CPR>(row)) * 8) + (col & 7);
     }
+  // q^T operand k-step s: row l32 of the buffer, channels 16 s + 8 half .. + 7
+  int qrd[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qrd[s] = l32 * D + (((2 * s + half) ^ swz<CPR>(l32)) * 8);
   const float* wrow = a.w + h * D;
-
 
   for (int st = wave; st * 32 < t1 - t0; st += NW) {
     const int tok = t0 + st * 32 + l32;
     const bool ok = tok < t1;
     const size_t qrow = row_of(st);
+    // this sub-tile's rows landed: only the NG gate loads issued after its copy (and the
+    // stores after those) may still be in flight
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NG) : "memory");
     bf16x8 qreg[KS];
-    uint4 gcur[DT][2];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qreg[s] = qn[s];
+    for (int s = 0; s < KS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(&Qs[wave][qrd[s]]);
+    uint4 gcur[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int ip = 0; ip < 2; ++ip) gcur[dt][ip] = gn[dt][ip];
-    if ((st + NW) * 32 < t1 - t0) load_rows(st + NW);
+    if ((st + NW) * 32 < t1 - t0) {
+      // the buffer's reads are done before the next copy overwrites it
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      fetch(st + NW);
+    }
 
     // delta-rule variant: u = phi(q).S with phi(q) = q / sqrt(|q|^2 + eps); the lane and
     // its partner (lane +- 32) hold the two halves of token `tok`'s channels
@@ -323,42 +352,58 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
 #pragma unroll
       for (int r = 0; r < 16; ++r) ss += u[dt][r] * u[dt][r];
     const float rinv = rsqrtf(pair_sum(ss) / D + a.eps);
-    __bf16* arow = a.acat + (size_t)tok * 2 * rs + rs + h * D;
+    // The output rows go through the wave's LDS buffer one half row (8 chunks, channels
+    // 64 P .. 64 P + 63) of all 32 tokens at a time and are stored as whole 128-byte half
+    // rows, 8 per store instruction.  Stored straight from the MFMA layout, every store
+    // instruction touched 32 rows at 32 bytes each (the store traffic then cost two fifths
+    // of the kernel's time).
+    const int sub0 = t0 + st * 32;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int P = 0; P < DT / 2; ++P) {
 #pragma unroll
-      for (int ip = 0; ip < 2; ++ip) {
-        // after the swap: lanes 0-31 hold channels c0 .. c0+7 with c0 = 32 dt + 16 ip,
-        // lanes 32-63 hold c0 + 8 .. c0 + 15
-        float x[4], y[4];
+      for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = u[dt][4 * (2 * ip) + e];
-          y[e] = u[dt][4 * (2 * ip + 1) + e];
-        }
-        permlane32_swap4(x, y);
-        const int c0 = 32 * dt + 16 * ip + 8 * half;
-        const float uv[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-        const uint4 graw = gcur[dt][ip];
-        const float4 w0 = *reinterpret_cast<const float4*>(wrow + c0);
-        const float4 w1 = *reinterpret_cast<const float4*>(wrow + c0 + 4);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
-        float r[8];
+        for (int ip = 0; ip < 2; ++ip) {
+          const int dt = 2 * P + dd;
+          // after the swap: lanes 0-31 hold channels c0 .. c0+7 with c0 = 32 dt + 16 ip,
+          // lanes 32-63 hold c0 + 8 .. c0 + 15
+          float x[4], y[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float gv = bf16_to_f32((e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffff));
-          r[e] = sigmoid(gv) * (uv[e] * rinv * wv[e]);
-        }
-        if (ok) {
-          *reinterpret_cast<uint4*>(arow + c0) = make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]),
-                                                             pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7]));
-          if (a.u_dbg) {
+          for (int e = 0; e < 4; ++e) {
+            x[e] = u[dt][4 * (2 * ip) + e];
+            y[e] = u[dt][4 * (2 * ip + 1) + e];
+          }
+          permlane32_swap4(x, y);
+          const int c0 = 32 * dt + 16 * ip + 8 * half;
+          const float uv[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+          const uint4 graw = gcur[dt][ip];
+          const float4 w0 = *reinterpret_cast<const float4*>(wrow + c0);
+          const float4 w1 = *reinterpret_cast<const float4*>(wrow + c0 + 4);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
+          float r[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float gv = bf16_to_f32((e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffff));
+            r[e] = sigmoid(gv) * (uv[e] * rinv * wv[e]);
+          }
+          // chunk 4 dd + 2 ip + half of the half row, row l32 of the buffer
+          *reinterpret_cast<uint4*>(&Os[wave][l32 * 64 + (((4 * dd + 2 * ip + half) ^ swz<8>(l32)) * 8)]) =
+              make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                         pack_bf16x2(r[6], r[7]));
+          if (ok && a.u_dbg) {
             *reinterpret_cast<float4*>(a.u_dbg + qrow + c0) = make_float4(uv[0], uv[1], uv[2], uv[3]);
             *reinterpret_cast<float4*>(a.u_dbg + qrow + c0 + 4) = make_float4(uv[4], uv[5], uv[6], uv[7]);
           }
         }
+      // lane: row 8 i + lane / 8, chunk lane % 8 of the half row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + (lane >> 3), c = lane & 7, t = sub0 + row;
+        const uint4 v = *reinterpret_cast<const uint4*>(&Os[wave][row * 64 + ((c ^ swz<8>(row)) * 8)]);
+        if (t < t1) *reinterpret_cast<uint4*>(a.acat + (size_t)t * 2 * rs + rs + h * D + 64 * P + c * 8) = v;
       }
+    }
   }
 }
 
