@@ -64,6 +64,15 @@ def test_agpr_write_then_mfma_accumulate_flagged():
     assert len(asm_check.check_asm(asm)) == 1
 
 
+def test_m0_write_right_before_lds_dma_flagged():
+    """The LDS DMA copy reads its destination from M0: one wait state after the M0 write."""
+    dma = "global_load_lds_dwordx4 v1, s[4:5]"
+    assert len(asm_check.check_asm(listing("s_mov_b32 m0, s6", dma))) == 1
+    assert asm_check.check_asm(listing("s_mov_b32 m0, s6", "s_nop 0", dma)) == []
+    mf = "v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]"
+    assert asm_check.check_asm(listing("s_mov_b32 m0, s6", mf, dma)) == []
+
+
 def test_compiler_use_of_m0_flagged_outside_inline_asm():
     plain = "\ts_mov_b32 m0, s4\n\tds_read_addtid_b32 v1\n"
     assert len(asm_check.check_m0(plain)) == 1

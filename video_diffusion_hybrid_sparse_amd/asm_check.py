@@ -15,7 +15,8 @@ to these instructions:
     wait states (NumPasses + 3, plus one on gfx950): 12 after the 8-pass 32x32x16 bf16
     MFMA (also taken for the shorter 16x16x32), 20 after the 16-pass 32x32x64 fp8 one
     (the count hipcc's own hazard recognizer inserts after that builtin);
-  - an MFMA's C operand overwritten by the VALU: NumPasses + 3 wait states.
+  - an MFMA's C operand overwritten by the VALU: NumPasses + 3 wait states;
+  - an M0 write (the LDS destination of a DMA copy) then the copy: 1 wait state.
 
 A wait state is one issued instruction; s_nop N counts N + 1.
 
@@ -229,6 +230,11 @@ def _search(items, preds, start, need, hit):
     return None
 
 
+def _writes_m0(inst) -> bool:
+    ops = inst.text.split(None, 1)
+    return inst.op.startswith("s_") and len(ops) > 1 and ops[1].split(",")[0].strip() == "m0"
+
+
 def check_asm(asm: str, prefixes=PREFIXES) -> list[str]:
     problems = []
     kernels = _kernels(asm, prefixes)
@@ -239,6 +245,10 @@ def check_asm(asm: str, prefixes=PREFIXES) -> list[str]:
         for i, (lab, inst) in enumerate(items):
             if inst is None:
                 continue
+            if inst.op.startswith("global_load_lds") or (inst.op.startswith("buffer_load") and " lds" in inst.text):
+                r = _search(items, preds, i, 1, _writes_m0)
+                if r:
+                    problems.append(f"{name}: M0 write '{r[0].text}' then LDS DMA after {r[1]} wait states: '{inst.text}'")
             if inst.mfma:
                 reads = inst.src
                 r = _search(items, preds, i, VALU_TO_MFMA, lambda p: p.valu and (p.dst & reads))

@@ -131,6 +131,13 @@ __device__ __forceinline__ void mfma_pv(f32x16& d, const bf16x8& v, const bf16x8
 __device__ __forceinline__ void mfma_sum(f32x4& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
+// The LDS DMA of dma16 split in two: set_m0 writes the LDS destination, dma16_at_m0 issues
+// the copy (16 bytes per lane from sbase + voff to M0 + 16 lane).  At least one
+// instruction must separate them (asm_check verifies it); nothing else here writes M0.
+__device__ __forceinline__ void set_m0(uint32_t m0) { asm volatile("s_mov_b32 m0, %0" ::"s"(m0) : "m0"); }
+__device__ __forceinline__ void dma16_at_m0(const void* sbase, uint32_t voff) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase) : "memory");
+}
 }  // namespace
 
 // One query tile (logical tile id lid: head, query group, 256 queries) of the pipelined
@@ -256,43 +263,90 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
     uint32_t off[NI];
     uint32_t koff8[FP8 ? NI8 : 1];
     uint32_t m0k, m0v;
+    int src, valid;  // the stage and its keys from the stage's first one to its segment's end
     bool k8;
+  };
+  // per-lane offsets of a stage whose rows are all valid
+  uint32_t foff[NI], foff8[FP8 ? NI8 : 1];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) foff[i] = __umul24((uint32_t)lrow[i], rs2) + loff[i];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < NI8; ++i) foff8[i] = __umul24((uint32_t)lrow8[i], (uint32_t)rs) + loff8[i];
+  }
+  auto set_offsets = [&](Copy& c) __attribute__((always_inline)) {
+    if (c.valid >= BN) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) c.off[i] = foff[i];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < NI8; ++i) c.koff8[i] = foff8[i];
+      }
+    } else {
+      // (24-bit products: the row is below 64 and the row stride H d 2 below 2^24)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) c.off[i] = __umul24((uint32_t)imin(lrow[i], c.valid - 1), rs2) + loff[i];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < NI8; ++i)
+          c.koff8[i] = __umul24((uint32_t)imin(lrow8[i], c.valid - 1), (uint32_t)rs) + loff8[i];
+      }
+    }
   };
   auto prep = [&](int src, int buf) __attribute__((always_inline)) {
     bool text;
-    int start, valid;
-    kw.stage_at(src, text, start, valid);
+    int start;
     Copy c;
+    kw.stage_at(src, text, start, c.valid);
+    c.src = src;
     const size_t base = (size_t)start * rs + h * D;
     c.k8 = FP8 && !text;
     if (c.k8) c.kb = static_cast<const uint8_t*>(a.k) + base;
     else c.kb = (text ? k_text : static_cast<const __bf16*>(a.k)) + base;
     c.vb = (text ? v_text : v_video) + base;
-#pragma unroll
-    // (24-bit products: the row is below 64 and the row stride H d 2 below 2^24)
-    for (int i = 0; i < NI; ++i) c.off[i] = __umul24((uint32_t)imin(lrow[i], valid - 1), rs2) + loff[i];
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < NI8; ++i) c.koff8[i] = __umul24((uint32_t)imin(lrow8[i], valid - 1), (uint32_t)rs) + loff8[i];
-    }
+    set_offsets(c);
     c.m0k = (c.k8 ? lds_k8 : lds_k) + (uint32_t)buf * (BN * D * 2);
     c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
     return c;
   };
+  // The copy of stage src (the previous copy's stage or the one after it) into buffer buf.
+  // Inside a segment the source rows move on by BN and, for a full stage, the per-lane
+  // offsets are the fixed ones; only a segment's first stage goes through stage_at.
+  auto advance = [&](Copy& c, int src, int buf) __attribute__((always_inline)) {
+    if (src != c.src) {
+      if (c.valid > BN) {
+        c.src = src;
+        c.valid -= BN;
+        c.kb = static_cast<const char*>(c.kb) + (size_t)BN * rs * (c.k8 ? 1 : 2);
+        c.vb += (size_t)BN * rs;
+        set_offsets(c);
+      } else {
+        c = prep(src, buf);
+        return;
+      }
+    }
+    c.m0k = (c.k8 ? lds_k8 : lds_k) + (uint32_t)buf * (BN * D * 2);
+    c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
+  };
+  // A copy instruction in two parts: its M0 write (LDS destination) goes before the MFMA
+  // of its slot and the copy after it, so the MFMA is the wait state between them.
+  auto m0_k = [&](const Copy& c, int i) __attribute__((always_inline)) {
+    if constexpr (FP8) set_m0(c.k8 ? c.m0k + i * RPI8 * D : c.m0k + i * RPI * D * 2);
+    else set_m0(c.m0k + i * RPI * D * 2);
+  };
   auto copy_k = [&](const Copy& c, int i) __attribute__((always_inline)) {
     if constexpr (FP8) {
       if (c.k8) {
-        if (i < NI8) dma16(c.kb, c.koff8[i], c.m0k + i * RPI8 * D);
+        if (i < NI8) dma16_at_m0(c.kb, c.koff8[i]);
       } else {
-        dma16(c.kb, c.off[i], c.m0k + i * RPI * D * 2);
+        dma16_at_m0(c.kb, c.off[i]);
       }
     } else {
-      dma16(c.kb, c.off[i], c.m0k + i * RPI * D * 2);
+      dma16_at_m0(c.kb, c.off[i]);
     }
   };
-  auto copy_v = [&](const Copy& c, int i) __attribute__((always_inline)) {
-    dma16(c.vb, c.off[i], c.m0v + i * RPI * D * 2);
-  };
+  auto m0_v = [&](const Copy& c, int i) __attribute__((always_inline)) { set_m0(c.m0v + i * RPI * D * 2); };
+  auto copy_v = [&](const Copy& c, int i) __attribute__((always_inline)) { dma16_at_m0(c.vb, c.off[i]); };
 
   int krd[KS];
 #pragma unroll
@@ -471,6 +525,36 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
       return WEIGHTED ? kWpv * part(0, QB * NOPV) + kWsum * part(QB * NOPV, NMP) + kWqk8 * part(NMP, NMF)
                       : part(0, NMF);
     };
+    // The exponentials as 3 NIT steps: E(u, 0) and E(u, 1) take the fma and exponential of
+    // the two scores of pair u, P(u) packs them into pc.  A VALU read of a transcendental
+    // result needs one wait state, and the compiler counts none for the asm MFMAs, so P(u)
+    // comes after E(u + 1, 0): E(0,0) E(0,1), then E(u,0) P(u-1) E(u,1) for u >= 1, then
+    // P(NIT-1).
+    constexpr int NMI = 3 * NIT;
+    float ex[NIT][2];
+    auto expo_e = [&](int u, int e) __attribute__((always_inline)) {
+      const int qb = u / 8, r = 2 * (u % 8) + e;
+      ex[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][r], c2c, nm[qb]));
+    };
+    auto expo_p = [&](int u) __attribute__((always_inline)) {
+      const int qb = u / 8, r = 2 * (u % 8);
+      const uint32_t pk = pack_bf16x2(ex[u][0], ex[u][1]);
+      uint4 w = __builtin_bit_cast(uint4, pc[qb][r >> 3]);
+      const int e = (r & 7) >> 1;
+      if (e == 0) w.x = pk; else if (e == 1) w.y = pk; else if (e == 2) w.z = pk; else w.w = pk;
+      pc[qb][r >> 3] = __builtin_bit_cast(bf16x8, w);
+    };
+    auto expo_step = [&](int mi) __attribute__((always_inline)) {
+      if (mi == 0) expo_e(0, 0);
+      else if (mi == 1) expo_e(0, 1);
+      else if (mi == NMI - 1) expo_p(NIT - 1);
+      else {
+        const int k = mi - 2, u = k / 3 + 1;
+        if (k % 3 == 0) expo_e(u, 0);
+        else if (k % 3 == 1) expo_p(u - 1);
+        else expo_e(u, 1);
+      }
+    };
     bf16x8 op[NOP + LA];
     i32x8 op8[N8 ? KS8 : 1];
     auto fetch = [&](int n) __attribute__((always_inline)) {
@@ -499,6 +583,12 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
 #pragma unroll
     for (int sl = 0; sl < NMF; ++sl) {
       const int qb = sl % QB;
+      constexpr int GAP = CP != 0 ? NMF / NI : 1;  // MFMA slots per copy instruction
+      const bool copy_slot = CP != 0 && sl % GAP == kCopySlot % GAP;
+      if (copy_slot) {
+        if (CP == 1) m0_k(cp, sl / GAP);
+        else m0_v(cp, sl / GAP);
+      }
       if (sl < QB * NOPV) {
         // P V: operand n of the stream
         const int n = sl / QB;
@@ -523,12 +613,9 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
       // the first pass reads them only beside the score MFMAs, after this block's P V
       // MFMAs (asm_check verifies the wait states either way)
       if (SAFE && sl == 0) fence_s(sc);
-      if constexpr (CP != 0) {
-        constexpr int GAP = NMF / NI;  // MFMA slots per copy instruction
-        if (sl % GAP == kCopySlot % GAP) {
-          if (CP == 1) copy_k(cp, sl / GAP);
-          else copy_v(cp, sl / GAP);
-        }
+      if (copy_slot) {
+        if (CP == 1) copy_k(cp, sl / GAP);
+        else copy_v(cp, sl / GAP);
       }
       // the vector work spread over all the block's MFMA slots (the exponentials write the
       // other P buffer, so they need not wait for the P V MFMAs): the second pass's maxima
@@ -538,9 +625,15 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
         for (int it = sl * NIT / NMF; it < (sl + 1) * NIT / NMF; ++it) max_item(it);
       }
       if (sl >= E0) {
+        if constexpr (SAFE) {
+          // (the second pass, with the maxima beside them, keeps whole pairs: fewer live values)
 #pragma unroll
-        for (int it = NIT * wcum(sl) / wcum(NMF); it < NIT * wcum(sl + 1) / wcum(NMF); ++it)
-          expo_unit(sc, pc, it, c2c);
+          for (int it = NIT * wcum(sl) / wcum(NMF); it < NIT * wcum(sl + 1) / wcum(NMF); ++it)
+            expo_unit(sc, pc, it, c2c);
+        } else {
+#pragma unroll
+          for (int mi = NMI * wcum(sl) / wcum(NMF); mi < NMI * wcum(sl + 1) / wcum(NMF); ++mi) expo_step(mi);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -625,9 +718,17 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   for (int st = 0; st < 3; ++st) {
     const Copy c = prep(imin(st, nst - 1), buf_of(st));
 #pragma unroll
-    for (int i = 0; i < NI; ++i) copy_k(c, i);
+    for (int i = 0; i < NI; ++i) {
+      m0_k(c, i);
+      asm volatile("s_nop 0");
+      copy_k(c, i);
+    }
 #pragma unroll
-    for (int i = 0; i < NI; ++i) copy_v(c, i);
+    for (int i = 0; i < NI; ++i) {
+      m0_v(c, i);
+      asm volatile("s_nop 0");
+      copy_v(c, i);
+    }
   }
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kStageOps) : "memory");
   // scores of sub-tile 0 (fp8: e4m3 keys when there is no text)
@@ -688,7 +789,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   // the segment then overlaps those MFMAs instead of holding the next ones after the
   // barrier.
   auto pin = [&](const Copy& c, int v) __attribute__((always_inline)) {
-    asm volatile("" ::"s"(c.kb), "s"(c.vb), "s"(c.m0k), "s"(c.m0v), "s"(v));
+    asm volatile("" ::"s"(c.kb), "s"(c.vb), "s"(c.m0k), "s"(c.m0v), "s"(v), "s"(c.src), "s"(c.valid));
 #pragma unroll
     for (int i = 0; i < NI; ++i) asm volatile("" ::"v"(c.off[i]));
     if constexpr (FP8) {
@@ -707,10 +808,16 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
     block(T{}, T{}, T{}, CK{}, P0{}, next8, cp, B, 0, va, S[1], c2_of(j), vj - BC, B1, 0, S[0], B, 1, vb);
     // P V of sub-tile 2 j + 1; sub-tile 2 j + 2 (stage j + 1, keys 0..31); scores of 2 j + 3
     block(T{}, T{}, T{}, CV{}, P1{}, next8, cp, B, 1, vb, S[0], c2_of(j + 1), vn, B1, 1, S[1], B1, 0, va);
-    vj = vn;
     // the next iteration's: stage j + 4 into buffer (B + 4) % 4 = B, valid count of j + 2
-    cp = prep(imin(j + 4, nst - 1), B);
-    vn = valid_of(j + 2);
+    // (the count of j + 1 less BN while j + 2 is in the same segment)
+    advance(cp, imin(j + 4, nst - 1), B);
+    if (vn > BN) {
+      vj = vn;
+      vn -= BN;
+    } else {
+      vj = vn;
+      vn = valid_of(j + 2);
+    }
     pin(cp, vn);
   };
   // (fp8: iterations whose next scores are of text keys first, one at a time: few of them)
