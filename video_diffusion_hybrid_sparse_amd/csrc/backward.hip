@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void epi_bwd_kernel(EpiBwdArgs a) {
         *reinterpret_cast<FV*>(a.dgl + o) = dgl;
         *reinterpret_cast<BV*>(a.du + o) = dub;
         *reinterpret_cast<BV*>(a.dO + o) = dOb;
-        if (l == 0) a.delta[(size_t)t * g.H + h] = delta;
+        if (l == 0) a.delta[(size_t)t * g.H + h] = -delta;  // stored negated: see the kernels
       }
     }
   }
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   }
   const float lse = a.lse[(size_t)qtok * g.H + h];
-  const float delta = a.delta[(size_t)qtok * g.H + h];
+  const float ndelta = a.delta[(size_t)qtok * g.H + h];  // -Delta
   __builtin_amdgcn_s_waitcnt(0);
 
   // stage copies (dma16, waited for explicitly): SGPR base per stage, per-lane offsets.
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const float p = __builtin_amdgcn_exp2f(s[rt][r + e] * c2 - lse);
-          ds2[e] = p * (dp[rt][r + e] - delta);
+          ds2[e] = p * (dp[rt][r + e] + ndelta);
         }
         uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
         const uint32_t pk = pack_bf16x2(ds2[0], ds2[1]);
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     bf16x8 op[NS];
     f32x16 s[2], dp[2];
     bf16x8 pb[2][2], sb[2][2];
-    f32x4 st[4];  // log-sum-exps (step 2), then Deltas (step 3), of rows 8 r4 + 4 half + e
+    f32x4 st[4];  // log-sum-exps (step 2) of rows 8 r4 + 4 half + e
     // accumulator row r = query 32 RT + 8 (r/4) + 4 half + r%4 of the stage, column = key.
     // P of unit u = (t, r4), packed into pb
     auto p_unit = [&](int u) __attribute__((always_inline)) {
@@ -742,7 +742,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       else { w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]); }
       pb[t][r4 >> 1] = __builtin_bit_cast(bf16x8, w);
     };
-    // dS = P (dP - Delta) of unit u, with P as packed (bf16), packed into sb
+    // dS = P (dP - Delta) of unit u, with P as packed (bf16), packed into sb; dp already
+    // holds dP - Delta (its accumulators start at the stage's -Delta)
     auto ds_unit = [&](int u) __attribute__((always_inline)) {
       const int t = u & 1, r4 = u >> 1;
       const uint4 w0 = __builtin_bit_cast(uint4, pb[t][r4 >> 1]);
@@ -751,7 +752,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                           __builtin_bit_cast(float, phi << 16), __builtin_bit_cast(float, phi & 0xffff0000u)};
       float ds[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp[t][4 * r4 + e] - st[r4][e]);
+      for (int e = 0; e < 4; ++e) ds[e] = p[e] * dp[t][4 * r4 + e];
       uint4 w = __builtin_bit_cast(uint4, sb[t][r4 >> 1]);
       if (r4 & 1) { w.z = pack_bf16x2(ds[0], ds[1]); w.w = pack_bf16x2(ds[2], ds[3]); }
       else { w.x = pack_bf16x2(ds[0], ds[1]); w.y = pack_bf16x2(ds[2], ds[3]); }
@@ -777,13 +778,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           if (m == 0) mma_first(s[t], op[n], kreg[t][m]);
           else mma_v(s[t], op[n], kreg[t][m]);
         }
+        // dP's accumulators start at -Delta of their rows (the Delta stage holds it
+        // negated), so the MFMAs leave dP - Delta: one VALU instruction less per element
+        // (each t loads its own copy, its address opaque so that the two loads are not
+        // merged into one load and vector moves next to the MFMAs)
+        if (n == KS - 3) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            uint32_t da = sad + DOFF;
+            asm volatile("" : "+v"(da));
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 v = *(lds_f4*)(uintptr_t)(da + 32 * r4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dp[t][4 * r4 + e] = v[e];
+            }
+          }
+        }
         if (n == KS - 1) load_stats(LOFF);
       } else if (n < 2 * KS) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          if (m == 0) mma_first(dp[t], op[n], vreg[t][m]);
-          else mma_v(dp[t], op[n], vreg[t][m]);
-        }
+        for (int t = 0; t < 2; ++t) mma_v(dp[t], op[n], vreg[t][m]);
         // the scores' last MFMAs, before the vector unit reads them
         if (m == 0) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
         else {
@@ -791,9 +806,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           for (int u = NU * (m - 1) / (KS - 1); u < NU * m / (KS - 1); ++u) p_unit(u);
         }
         if (m == KS - 1) {
-          // vector writes of P, read next by MFMAs; the Deltas replace the log-sum-exps
+          // vector writes of P, read next by MFMAs
           asm volatile("s_nop 1" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]));
-          load_stats(DOFF);
         }
       } else if (n < 3 * KS) {
         const int G = m / DT, dt = m % DT;

@@ -127,7 +127,7 @@ struct EpiBwdArgs {
   __bf16* du;          // [N,H,d] gradient of u
   float* dgs;          // [N,H,d]
   float* dgl;
-  float* delta;        // [N,H]: dO . o per token and head
+  float* delta;        // [N,H]: -(dO . o) per token and head (stored negated)
   float* dw_part;      // [ceil(N/64),H,d] per-block partial sums of the weight gradient
   float* dw;           // [H,d]
   Geo geo;
