@@ -34,6 +34,8 @@ __device__ __forceinline__ void dma16_buf(const i32x4& rsrc, uint32_t voff, uint
                : "memory", "m0");
 }
 
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
 __device__ __forceinline__ i32x4 raw_buffer(const void* base, uint32_t extent) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   // stride 0, raw (untyped) access; the last word selects 32-bit data
@@ -173,17 +175,20 @@ hipError_t launch_build_bf16(const BuildArgs<__bf16>& a, hipStream_t stream) {
 
 // ---- state read: u = q.S_fwd + q.S_bwd, RMSNorm, gate --------------------------------
 //
-// One workgroup = up to 1024 query tokens of one query group and one head (the states'
-// load and split is paid once per 1024 tokens); each of its 8 waves walks 32-token
-// sub-tiles.  The group's two states are summed in float32 (the identity feature map
-// makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd); only rounding differs), split into
-// bf16 hi + lo parts and stored row-major ([d_in][d_out], XOR-swizzled 16-byte chunks) in
-// LDS once per workgroup.  u^T = S^T q^T runs as two bf16 MFMA passes with float32
-// accumulation (about 16 mantissa bits of the state kept); the S^T operand is gathered
-// with the transposing LDS read.
+// A persistent grid, one workgroup per CU: the launch's 32-token sub-tiles, numbered head
+// by head and, within a head, group by group, are split into equal contiguous shares, one
+// per workgroup (the workgroup takes the whole LDS, so a grid of 1024-token tiles left
+// the last of its 11.25 rounds a quarter full at 768p).  A share crosses few (head, group)
+// boundaries; at each, the workgroup loads the new group's two states, sums them in
+// float32 (the identity feature map makes q.S_fwd + q.S_bwd equal to q.(S_fwd + S_bwd);
+// only rounding differs), splits the sum into bf16 hi + lo parts and stores them
+// row-major ([d_in][d_out], XOR-swizzled 16-byte chunks) in LDS.  Its 8 waves then take
+// the group's sub-tiles of the share in turn.  u^T = S^T q^T runs as two bf16 MFMA
+// passes with float32 accumulation (about 16 mantissa bits of the state kept); the S^T
+// operand is gathered with the transposing LDS read.
 //
 // A sub-tile's query rows go from HBM straight into the wave's own LDS buffer (buffer
-// loads with the LDS bit, four whole 256-byte rows per instruction; rows past the tile's
+// loads with the LDS bit, four whole 256-byte rows per instruction; rows past the group's
 // last token lie beyond the buffer resource's extent and read as zeros), copied while the
 // wave computes the sub-tile before; the MFMA operands are then read from LDS.  Loaded as
 // MFMA operands straight from HBM instead, every load instruction touched 32 rows at 32
@@ -194,7 +199,7 @@ constexpr int kReadWaves = 8;  // waves per readout workgroup (8: 7% faster than
 
 template <int D>
 __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutArgs<__bf16> a) {
-  constexpr int BM = 1024, KS = D / 16, DT = D / 32, CPR = D / 8, NW = kReadWaves, NT = 64 * NW;
+  constexpr int KS = D / 16, DT = D / 32, CPR = D / 8, NW = kReadWaves, NT = 64 * NW;
   constexpr int RPI = 64 / CPR;   // query rows one copy instruction covers
   constexpr int NQ = 32 / RPI;    // copy instructions per lane and sub-tile
   constexpr int NG = 2 * DT;      // gate loads per lane and sub-tile
@@ -203,77 +208,20 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
   __shared__ __attribute__((aligned(16))) __bf16 Qs[NW][32 * D];
   __shared__ __attribute__((aligned(16))) __bf16 Os[NW][32 * 64];
   const Geo g = a.geo;
-  // (tiles vary fastest: 2% faster than heads fastest; tiles of one group, which share
-  // its state pair, run side by side)
-  const int h = blockIdx.y;
-  int grp, t0, t1;
-  if (!locate_tile(g, blockIdx.x, BM, grp, t0, t1)) return;
-  const int chunk = group_chunk(grp);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const size_t rs = (size_t)g.H * D;
-  const size_t hs = (size_t)h * D * D;
-
-  auto row_of = [&](int st) __attribute__((always_inline)) {
-    const int tok = t0 + st * 32 + l32;
-    return (size_t)(tok < t1 ? tok : t1 - 1) * rs + h * D;
-  };
-  // query rows of the tile through a raw buffer whose extent ends at the tile's last row
-  // (byte offsets fit 32 bits: at most 1024 rows of the token row stride H d 2)
+  // (byte offsets inside a group fit 32 bits: the host checks C T H d 2 < 2^32)
   const uint32_t rsb = (uint32_t)rs * 2;
-  const i32x4 rq = raw_buffer(a.q + (size_t)t0 * rs + h * D, (uint32_t)(t1 - t0 - 1) * rsb + D * 2);
-  uint32_t qoff[NQ];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int r = i * RPI + lane / CPR;
-    qoff[i] = (uint32_t)r * rsb + (uint32_t)((lane % CPR) ^ swz<CPR>(r)) * 16;
-  }
+  // (the lane's copy offsets are formed at each copy: kept live across the segment loop
+  // they push the registers past the 256 of two waves per SIMD)
+  auto qoff = [&](int i) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int r = i * RPI + ln / CPR;
+    return (uint32_t)r * rsb + (uint32_t)((ln % CPR) ^ swz<CPR>(r)) * 16;
+  };
   const uint32_t m0q = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)&Qs[0][0] + wave * 32 * D * 2);
-  uint4 gn[DT][2];
-  // sub-tile st: its query rows into this wave's buffer, its gate rows into gn (the copy
-  // first: the wait for it counts the NG gate loads issued after it)
-  auto fetch = [&](int st) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)st * 32 * rsb;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) dma16_buf(rq, base + qoff[i], m0q + i * RPI * D * 2);
-    const size_t qrow = row_of(st);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int ip = 0; ip < 2; ++ip)
-        gn[dt][ip] = *reinterpret_cast<const uint4*>(a.gl + qrow + 32 * dt + 16 * ip + 8 * half);
-  };
-  // (the first sub-tile's rows are in flight during the state prologue)
-  if (wave * 32 < t1 - t0) fetch(wave);
-
-  // S_sum = S_fwd + S_bwd (anchors: text/2 + text/2) into LDS as bf16 hi + lo
-  {
-    const float* ta = a.Stext + hs;
-    const float* fa = chunk >= 0 ? a.Sfwd + (size_t)chunk * g.H * D * D + hs : ta;
-    const float* ba = chunk >= 0 ? a.Sbwd + (size_t)chunk * g.H * D * D + hs : ta;
-    const float wf = chunk >= 0 ? 1.0f : 0.5f;
-    // (unrolled: all of a thread's state loads are issued before the first is used)
-    static_assert(D * D / 4 % NT == 0, "whole rounds of float4 per thread");
-#pragma unroll
-    for (int it = 0; it < D * D / 4 / NT; ++it) {
-      const int u = tid + NT * it;
-      const int i = u / (D / 4), j = 4 * (u % (D / 4));
-      const float4 f = *reinterpret_cast<const float4*>(fa + i * D + j);
-      const float4 b = *reinterpret_cast<const float4*>(ba + i * D + j);
-      const float sv[4] = {wf * f.x + wf * b.x, wf * f.y + wf * b.y, wf * f.z + wf * b.z, wf * f.w + wf * b.w};
-      float hv[4], lv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hv[e] = (float)(__bf16)sv[e];
-        lv[e] = sv[e] - hv[e];
-      }
-      const int off = i * D + (((j >> 3) ^ swz<CPR>(i)) * 8) + (j & 7);
-      *reinterpret_cast<uint2*>(&Shi[off]) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-      *reinterpret_cast<uint2*>(&Slo[off]) = make_uint2(pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3]));
-    }
-  }
-  __syncthreads();
-
   // S^T operand via the transposing read: 16-lane group grp16 reads d_in rows K0..K0+3 and
   // d_out columns D0..D0+15; lane j of the group gets column D0 + j of rows K0..K0+3
   const int grp16 = lane >> 4, i16 = lane & 15;
@@ -290,11 +238,83 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
   int qrd[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) qrd[s] = l32 * D + (((2 * s + half) ^ swz<CPR>(l32)) * 8);
-  const float* wrow = a.w + h * D;
 
-  for (int st = wave; st * 32 < t1 - t0; st += NW) {
-    const int tok = t0 + st * 32 + l32;
-    const bool ok = tok < t1;
+  // this workgroup's share [cur, end) of the sub-tiles of every head
+  const int per_head = count_tiles(g, 32);
+  const int64_t total = (int64_t)per_head * g.H;
+  int64_t cur = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t end = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
+  for (bool first = true; cur < end; first = false) {
+    // the segment: sub-tiles s0 .. s1 - 1 of group grp of head h
+    const int h = (int)(cur / per_head);
+    int grp, t0, t1;
+    locate_tile(g, (int)(cur - (int64_t)h * per_head), 32, grp, t0, t1);
+    int f0, f1;
+    group_frames(g, grp, f0, f1);
+    const int g0 = f0 * g.T, g1 = f1 * g.T;
+    const int s0 = (t0 - g0) / 32;
+    const int s1 = (int)(s0 + imin64((int64_t)((g1 - g0 + 31) / 32 - s0), end - cur));
+    cur += s1 - s0;
+    // every wave is done with the previous segment's states and buffers
+    if (!first) __syncthreads();
+    const int chunk = group_chunk(grp);
+    const size_t hs = (size_t)h * D * D;
+
+    auto row_of = [&](int st) __attribute__((always_inline)) {
+      const int tok = g0 + st * 32 + l32;
+      return (size_t)(tok < g1 ? tok : g1 - 1) * rs + h * D;
+    };
+    // query rows of the group through a raw buffer whose extent ends at its last row
+    const i32x4 rq = raw_buffer(a.q + (size_t)g0 * rs + h * D, (uint32_t)(g1 - g0 - 1) * rsb + D * 2);
+    uint4 gn[DT][2];
+    // sub-tile st: its query rows into this wave's buffer, its gate rows into gn (the copy
+    // first: the wait for it counts the NG gate loads issued after it)
+    auto fetch = [&](int st) __attribute__((always_inline)) {
+      const uint32_t base = (uint32_t)st * 32 * rsb;
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) dma16_buf(rq, base + qoff(i), m0q + i * RPI * D * 2);
+      const size_t qrow = row_of(st);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip)
+          gn[dt][ip] = *reinterpret_cast<const uint4*>(a.gl + qrow + 32 * dt + 16 * ip + 8 * half);
+    };
+    // (the first sub-tile's rows are in flight during the state prologue)
+    if (s0 + wave < s1) fetch(s0 + wave);
+
+    // S_sum = S_fwd + S_bwd (anchors: text/2 + text/2) into LDS as bf16 hi + lo
+    {
+      const float* ta = a.Stext + hs;
+      const float* fa = chunk >= 0 ? a.Sfwd + (size_t)chunk * g.H * D * D + hs : ta;
+      const float* ba = chunk >= 0 ? a.Sbwd + (size_t)chunk * g.H * D * D + hs : ta;
+      const float wf = chunk >= 0 ? 1.0f : 0.5f;
+      // (unrolled: all of a thread's state loads are issued before the first is used)
+      static_assert(D * D / 4 % NT == 0, "whole rounds of float4 per thread");
+#pragma unroll
+      for (int it = 0; it < D * D / 4 / NT; ++it) {
+        const int u = tid + NT * it;
+        const int i = u / (D / 4), j = 4 * (u % (D / 4));
+        const float4 f = *reinterpret_cast<const float4*>(fa + i * D + j);
+        const float4 b = *reinterpret_cast<const float4*>(ba + i * D + j);
+        const float sv[4] = {wf * f.x + wf * b.x, wf * f.y + wf * b.y, wf * f.z + wf * b.z, wf * f.w + wf * b.w};
+        float hv[4], lv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hv[e] = (float)(__bf16)sv[e];
+          lv[e] = sv[e] - hv[e];
+        }
+        const int off = i * D + (((j >> 3) ^ swz<CPR>(i)) * 8) + (j & 7);
+        *reinterpret_cast<uint2*>(&Shi[off]) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        *reinterpret_cast<uint2*>(&Slo[off]) = make_uint2(pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3]));
+      }
+    }
+    __syncthreads();
+    const float* wrow = a.w + h * D;
+
+  for (int st = s0 + wave; st < s1; st += NW) {
+    const int tok = g0 + st * 32 + l32;
+    const bool ok = tok < g1;
     const size_t qrow = row_of(st);
     // this sub-tile's rows landed: only the NG gate loads issued after its copy (and the
     // stores after those) may still be in flight
@@ -307,7 +327,7 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int ip = 0; ip < 2; ++ip) gcur[dt][ip] = gn[dt][ip];
-    if ((st + NW) * 32 < t1 - t0) {
+    if (st + NW < s1) {
       // the buffer's reads are done before the next copy overwrites it
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       fetch(st + NW);
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
     // rows, 8 per store instruction.  Stored straight from the MFMA layout, every store
     // instruction touched 32 rows at 32 bytes each (the store traffic then cost two fifths
     // of the kernel's time).
-    const int sub0 = t0 + st * 32;
+    const int sub0 = g0 + st * 32;
 #pragma unroll
     for (int P = 0; P < DT / 2; ++P) {
 #pragma unroll
@@ -401,16 +421,25 @@ __global__ __launch_bounds__(64 * kReadWaves) void readout_bf16_kernel(ReadoutAr
       for (int i = 0; i < 4; ++i) {
         const int row = 8 * i + (lane >> 3), c = lane & 7, t = sub0 + row;
         const uint4 v = *reinterpret_cast<const uint4*>(&Os[wave][row * 64 + ((c ^ swz<8>(row)) * 8)]);
-        if (t < t1) *reinterpret_cast<uint4*>(a.acat + (size_t)t * 2 * rs + rs + h * D + 64 * P + c * 8) = v;
+        if (t < g1) *reinterpret_cast<uint4*>(a.acat + (size_t)t * 2 * rs + rs + h * D + 64 * P + c * 8) = v;
       }
     }
+  }
   }
 }
 
 hipError_t launch_readout_bf16(const ReadoutArgs<__bf16>& a, hipStream_t stream) {
-  const int tiles = count_tiles(a.geo, 1024);
-  if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles, a.geo.H), block(64 * kReadWaves);
+  const Geo& g = a.geo;
+  const int64_t subtiles = (int64_t)count_tiles(g, 32) * g.H;
+  if (subtiles == 0) return hipSuccess;
+  // a group's query rows are addressed with 32-bit byte offsets (at most C T rows)
+  if ((int64_t)g.C * g.T * g.H * g.d * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  // one workgroup per CU (each takes the whole LDS)
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)(subtiles < cus ? subtiles : cus)), block(64 * kReadWaves);
   if (a.geo.d == 128)
     hipLaunchKernelGGL(readout_bf16_kernel<128>, grid, block, 0, stream, a);
   else if (a.geo.d == 64)
