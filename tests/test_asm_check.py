@@ -73,6 +73,16 @@ def test_m0_write_right_before_lds_dma_flagged():
     assert asm_check.check_asm(listing("s_mov_b32 m0, s6", mf, dma)) == []
 
 
+def test_valu_sgpr_write_then_memory_read_flagged():
+    """v_readfirstlane into a copy's base address: five wait states before the copy."""
+    rfl = "v_readfirstlane_b32 s5, v3"
+    dma = "global_load_lds_dwordx4 v1, s[4:5]"
+    assert len(asm_check.check_asm(listing(rfl, "s_mov_b32 m0, s6", "s_nop 0", dma))) == 1
+    assert asm_check.check_asm(listing(rfl, "s_mov_b32 m0, s6", "s_nop 3", dma)) == []
+    # an SGPR the copy does not read is no hazard
+    assert asm_check.check_asm(listing("v_readfirstlane_b32 s9, v3", "s_mov_b32 m0, s6", "s_nop 0", dma)) == []
+
+
 def test_compiler_use_of_m0_flagged_outside_inline_asm():
     plain = "\ts_mov_b32 m0, s4\n\tds_read_addtid_b32 v1\n"
     assert len(asm_check.check_m0(plain)) == 1

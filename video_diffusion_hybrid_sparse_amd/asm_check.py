@@ -16,7 +16,9 @@ to these instructions:
     MFMA (also taken for the shorter 16x16x32), 20 after the 16-pass 32x32x64 fp8 one
     (the count hipcc's own hazard recognizer inserts after that builtin);
   - an MFMA's C operand overwritten by the VALU: NumPasses + 3 wait states;
-  - an M0 write (the LDS destination of a DMA copy) then the copy: 1 wait state.
+  - an M0 write (the LDS destination of a DMA copy) then the copy: 1 wait state;
+  - a VALU write of an SGPR (v_readfirstlane, ...) then a vector memory instruction that
+    reads it (a copy's base address): 5 wait states.
 
 A wait state is one issued instruction; s_nop N counts N + 1.
 
@@ -36,6 +38,7 @@ import tempfile
 VALU_TO_MFMA = 2
 MFMA_TO_VALU_READ = 12
 MFMA_SRCC_TO_VALU_WRITE = 11
+VMEM_SGPR_AFTER_VALU = 5
 # MFMAs with more passes than the 8 the defaults above are for
 PASSES = {"v_mfma_f32_32x32x64_f8f6f4": 16, "v_mfma_scale_f32_32x32x64_f8f6f4": 16}
 MAX_PASSES = max(PASSES.values())
@@ -230,6 +233,27 @@ def _search(items, preds, start, need, hit):
     return None
 
 
+_SREG = re.compile(r"\bs\[(\d+):(\d+)\]|\bs(\d+)\b")
+
+
+def _sregs(text: str) -> set[int]:
+    out = set()
+    for m in _SREG.finditer(text):
+        if m.group(1):
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+        else:
+            out.add(int(m.group(3)))
+    return out
+
+
+def _valu_sgpr_dst(inst) -> set[int]:
+    """SGPRs a VALU instruction writes (v_readfirstlane, v_readlane, a v_cmp into SGPRs)."""
+    if not inst.valu:
+        return set()
+    ops = inst.text.split(None, 1)
+    return _sregs(ops[1].split(",")[0]) if len(ops) > 1 else set()
+
+
 def _writes_m0(inst) -> bool:
     ops = inst.text.split(None, 1)
     return inst.op.startswith("s_") and len(ops) > 1 and ops[1].split(",")[0].strip() == "m0"
@@ -245,6 +269,13 @@ def check_asm(asm: str, prefixes=PREFIXES) -> list[str]:
         for i, (lab, inst) in enumerate(items):
             if inst is None:
                 continue
+            if inst.op.startswith(("global_", "buffer_")):
+                # a vector memory instruction reading an SGPR the VALU wrote: 5 wait states
+                # (the compiler places them for its own memory instructions, not for asm)
+                sr = _sregs(inst.text.split(None, 1)[1]) if " " in inst.text else set()
+                r = _search(items, preds, i, VMEM_SGPR_AFTER_VALU, lambda p: bool(_valu_sgpr_dst(p) & sr))
+                if r:
+                    problems.append(f"{name}: VALU write of an SGPR '{r[0].text}' then memory read of it after {r[1]} wait states: '{inst.text}'")
             if inst.op.startswith("global_load_lds") or (inst.op.startswith("buffer_load") and " lds" in inst.text):
                 r = _search(items, preds, i, 1, _writes_m0)
                 if r:

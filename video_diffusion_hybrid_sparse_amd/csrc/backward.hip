@@ -342,6 +342,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
   const float lse = a.lse[(size_t)qtok * g.H + h];
   const float ndelta = a.delta[(size_t)qtok * g.H + h];  // -Delta
+  f32x16 ndv;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndv[r] = ndelta;
   __builtin_amdgcn_s_waitcnt(0);
 
   // stage copies (dma16, waited for explicitly): SGPR base per stage, per-lane offsets.
@@ -412,11 +415,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     if (j + 1 < nst) issue(j + 1, BUF ^ 1);
     int start, valid;
     stage_at(j, start, valid);
+    // dP^T's accumulators start at the query's -Delta (lane-local), so the MFMAs leave
+    // dP^T - Delta
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       s[rt] = 0.0f;
-      dp[rt] = 0.0f;
+      dp[rt] = ndv;
     }
 #pragma unroll
     for (int k = 0; k < KS; ++k)
@@ -444,7 +449,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const float p = __builtin_amdgcn_exp2f(s[rt][r + e] * c2 - lse);
-          ds2[e] = p * (dp[rt][r + e] + ndelta);
+          ds2[e] = p * dp[rt][r + e];
         }
         uint4 w = __builtin_bit_cast(uint4, pb[2 * rt + (r >> 3)]);
         const uint32_t pk = pack_bf16x2(ds2[0], ds2[1]);
