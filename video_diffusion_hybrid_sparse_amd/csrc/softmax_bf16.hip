@@ -266,6 +266,17 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
     int src, valid;  // the stage and its keys from the stage's first one to its segment's end
     bool k8;
   };
+  // the same for the iterations that score video keys next with fp8 inputs: every stage
+  // they copy is a video stage (the text stages come first), so its key rows are e4m3
+  // and the descriptor needs no kind
+  struct Copy8 {
+    const uint8_t* kb;
+    const __bf16* vb;
+    uint32_t off[NI];
+    uint32_t koff8[FP8 ? NI8 : 1];
+    uint32_t m0k, m0v;
+    int src, valid;
+  };
   // per-lane offsets of a stage whose rows are all valid
   uint32_t foff[NI], foff8[FP8 ? NI8 : 1];
 #pragma unroll
@@ -274,7 +285,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
 #pragma unroll
     for (int i = 0; i < NI8; ++i) foff8[i] = __umul24((uint32_t)lrow8[i], (uint32_t)rs) + loff8[i];
   }
-  auto set_offsets = [&](Copy& c) __attribute__((always_inline)) {
+  auto set_offsets = [&](auto& c) __attribute__((always_inline)) {
     if (c.valid >= BN) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) c.off[i] = foff[i];
@@ -309,33 +320,72 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
     c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
     return c;
   };
+  auto prep8 = [&](int src, int buf) __attribute__((always_inline)) {
+    bool text;
+    int start;
+    Copy8 c;
+    kw.stage_at(src, text, start, c.valid);
+    c.src = src;
+    const size_t base = (size_t)start * rs + h * D;
+    c.kb = static_cast<const uint8_t*>(a.k) + base;
+    c.vb = v_video + base;
+    set_offsets(c);
+    c.m0k = lds_k8 + (uint32_t)buf * (BN * D * 2);
+    c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
+    return c;
+  };
+  auto to8 = [&](const Copy& c) __attribute__((always_inline)) {
+    Copy8 d;
+    d.kb = static_cast<const uint8_t*>(c.kb);
+    d.vb = c.vb;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) d.off[i] = c.off[i];
+#pragma unroll
+    for (int i = 0; i < (FP8 ? NI8 : 1); ++i) d.koff8[i] = c.koff8[i];
+    d.m0k = c.m0k;
+    d.m0v = c.m0v;
+    d.src = c.src;
+    d.valid = c.valid;
+    return d;
+  };
   // The copy of stage src (the previous copy's stage or the one after it) into buffer buf.
   // Inside a segment the source rows move on by BN and, for a full stage, the per-lane
   // offsets are the fixed ones; only a segment's first stage goes through stage_at.
-  auto advance = [&](Copy& c, int src, int buf) __attribute__((always_inline)) {
+  auto advance = [&](auto& c, int src, int buf) __attribute__((always_inline)) {
+    constexpr bool V8 = std::is_same_v<std::decay_t<decltype(c)>, Copy8>;
     if (src != c.src) {
       if (c.valid > BN) {
         c.src = src;
         c.valid -= BN;
-        c.kb = static_cast<const char*>(c.kb) + (size_t)BN * rs * (c.k8 ? 1 : 2);
+        if constexpr (V8) c.kb += (size_t)BN * rs;
+        else c.kb = static_cast<const char*>(c.kb) + (size_t)BN * rs * (c.k8 ? 1 : 2);
         c.vb += (size_t)BN * rs;
         set_offsets(c);
       } else {
-        c = prep(src, buf);
+        if constexpr (V8) c = prep8(src, buf);
+        else c = prep(src, buf);
         return;
       }
     }
-    c.m0k = (c.k8 ? lds_k8 : lds_k) + (uint32_t)buf * (BN * D * 2);
+    if constexpr (V8) c.m0k = lds_k8 + (uint32_t)buf * (BN * D * 2);
+    else c.m0k = (c.k8 ? lds_k8 : lds_k) + (uint32_t)buf * (BN * D * 2);
     c.m0v = lds_v + (uint32_t)buf * (BN * D * 2);
   };
   // A copy instruction in two parts: its M0 write (LDS destination) goes before the MFMA
   // of its slot and the copy after it, so the MFMA is the wait state between them.
-  auto m0_k = [&](const Copy& c, int i) __attribute__((always_inline)) {
-    if constexpr (FP8) set_m0(c.k8 ? c.m0k + i * RPI8 * D : c.m0k + i * RPI * D * 2);
-    else set_m0(c.m0k + i * RPI * D * 2);
+  auto m0_k = [&](const auto& c, int i) __attribute__((always_inline)) {
+    if constexpr (std::is_same_v<std::decay_t<decltype(c)>, Copy8>) {
+      if (i < NI8) set_m0(c.m0k + i * RPI8 * D);
+    } else if constexpr (FP8) {
+      set_m0(c.k8 ? c.m0k + i * RPI8 * D : c.m0k + i * RPI * D * 2);
+    } else {
+      set_m0(c.m0k + i * RPI * D * 2);
+    }
   };
-  auto copy_k = [&](const Copy& c, int i) __attribute__((always_inline)) {
-    if constexpr (FP8) {
+  auto copy_k = [&](const auto& c, int i) __attribute__((always_inline)) {
+    if constexpr (std::is_same_v<std::decay_t<decltype(c)>, Copy8>) {
+      if (i < NI8) dma16_at_m0(c.kb, c.koff8[FP8 ? i : 0]);
+    } else if constexpr (FP8) {
       if (c.k8) {
         if (i < NI8) dma16_at_m0(c.kb, c.koff8[i]);
       } else {
@@ -345,8 +395,8 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
       dma16_at_m0(c.kb, c.off[i]);
     }
   };
-  auto m0_v = [&](const Copy& c, int i) __attribute__((always_inline)) { set_m0(c.m0v + i * RPI * D * 2); };
-  auto copy_v = [&](const Copy& c, int i) __attribute__((always_inline)) { dma16_at_m0(c.vb, c.off[i]); };
+  auto m0_v = [&](const auto& c, int i) __attribute__((always_inline)) { set_m0(c.m0v + i * RPI * D * 2); };
+  auto copy_v = [&](const auto& c, int i) __attribute__((always_inline)) { dma16_at_m0(c.vb, c.off[i]); };
 
   int krd[KS];
 #pragma unroll
@@ -494,7 +544,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   // CP: 0 none, 1 the K rows of copy cp, 2 its V rows, spread over the MFMA slots.
   // NEXT8 (fp8): the next sub-tile's keys are e4m3 (fp8 score MFMAs); c2c: the c2 of
   // the current sub-tile's keys.
-  auto block = [&](auto prev, auto next_s, auto next_v, auto cpk, auto pbi, auto next8, const Copy& cp, int pbuf,
+  auto block = [&](auto prev, auto next_s, auto next_v, auto cpk, auto pbi, auto next8, const auto& cp, int pbuf,
                    int psub, const bf16x8 (&vin)[LA], f32x16 (&sc)[QB], float c2c, int vc, int nbuf, int nsub,
                    f32x16 (&sn)[QB], int xbuf, int xsub, bf16x8 (&vout)[LA]) __attribute__((always_inline)) {
     constexpr int CP = decltype(cpk)::value;
@@ -788,12 +838,12 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   // iteration before, after its blocks' MFMAs have been issued: the scalar work of picking
   // the segment then overlaps those MFMAs instead of holding the next ones after the
   // barrier.
-  auto pin = [&](const Copy& c, int v) __attribute__((always_inline)) {
+  auto pin = [&](const auto& c, int v) __attribute__((always_inline)) {
     asm volatile("" ::"s"(c.kb), "s"(c.vb), "s"(c.m0k), "s"(c.m0v), "s"(v), "s"(c.src), "s"(c.valid));
 #pragma unroll
     for (int i = 0; i < NI; ++i) asm volatile("" ::"v"(c.off[i]));
     if constexpr (FP8) {
-      asm volatile("" ::"s"((int)c.k8));
+      if constexpr (!std::is_same_v<std::decay_t<decltype(c)>, Copy8>) asm volatile("" ::"s"((int)c.k8));
 #pragma unroll
       for (int i = 0; i < NI8; ++i) asm volatile("" ::"v"(c.koff8[i]));
     }
@@ -801,7 +851,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   Copy cp = prep(imin(3, nst - 1), buf_of(3));
   int vn = valid_of(1);
   // next8: the scores this iteration computes are of e4m3 keys (stage j + 1 is video)
-  auto iter = [&](int j, int B, auto next8) __attribute__((always_inline)) {
+  auto iter = [&](int j, int B, auto next8, auto& cp) __attribute__((always_inline)) {
     const int B1 = (B + 1) & (NBUF - 1);
     barrier_wait();
     // P V of sub-tile 2 j; sub-tile 2 j + 1 (stage j, keys 32..63); scores of 2 j + 2
@@ -820,20 +870,27 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
     }
     pin(cp, vn);
   };
-  // (fp8: iterations whose next scores are of text keys first, one at a time: few of them)
-  int j = 0;
-  if constexpr (FP8) {
-    for (; j + 1 < kw.n0; ++j) iter(j, buf_of(j), F{});
-  }
   // the rest (fp8: video keys next); here buf_of(j) == 0
   using N8 = std::integral_constant<bool, FP8>;
-  for (; j + 4 < nst; j += 4) {
-    iter(j, 0, N8{});
-    iter(j + 1, 1, N8{});
-    iter(j + 2, 2, N8{});
-    iter(j + 3, 3, N8{});
+  int j = 0;
+  auto rest = [&](auto& c) __attribute__((always_inline)) {
+    for (; j + 4 < nst; j += 4) {
+      iter(j, 0, N8{}, c);
+      iter(j + 1, 1, N8{}, c);
+      iter(j + 2, 2, N8{}, c);
+      iter(j + 3, 3, N8{}, c);
+    }
+    for (; j + 1 < nst; ++j) iter(j, buf_of(j), N8{}, c);
+  };
+  if constexpr (FP8) {
+    // iterations whose next scores are of text keys first, one at a time (few of them);
+    // the copy descriptor then names a video stage (stage n0 + 2 or the last)
+    for (; j + 1 < kw.n0; ++j) iter(j, buf_of(j), F{}, cp);
+    Copy8 cp8 = to8(cp);
+    rest(cp8);
+  } else {
+    rest(cp);
   }
-  for (; j + 1 < nst; ++j) iter(j, buf_of(j), N8{});
   // the gate logits of the output, loaded now so that their latency hides behind the
   // last stage's MFMAs (lane: channels 32 dt + 16 ip + 8 half .. + 7 of its query; 0.2%
   // faster than loading them after it)
