@@ -364,10 +364,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     start = base + BN * jj;
     valid = len - BN * jj;
   };
-  auto issue = [&](int j, int buf) __attribute__((always_inline)) {
-    int start, valid;
-    stage_at(j, start, valid);
-    const bool text = j < n0;
+  // The stage to copy next: inside a segment it moves on by BN keys; only a segment's
+  // first stage goes through stage_at's selects.
+  int nx_start = 0, nx_valid = 0, cur_valid = 0;
+  bool nx_text = false;
+  auto walk_to = [&](int j) __attribute__((always_inline)) {
+    if (nx_valid > BN) {
+      nx_start += BN;
+      nx_valid -= BN;
+    } else {
+      stage_at(j, nx_start, nx_valid);
+      nx_text = j < n0;
+    }
+  };
+  auto issue = [&](int buf) __attribute__((always_inline)) {
+    const int start = nx_start, valid = nx_valid;
+    const bool text = nx_text;
     const size_t base = (size_t)start * rs + h * D;
     const __bf16* kb = (text ? a.tk : a.k) + base;
     const __bf16* vb = (text ? a.tv : a.v) + base;
@@ -412,9 +424,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr uint32_t KOFF = BUF * 2 * TB, VOFF = KOFF + TB;
-    if (j + 1 < nst) issue(j + 1, BUF ^ 1);
-    int start, valid;
-    stage_at(j, start, valid);
+    // (the valid count of stage j, copied by the previous stage)
+    const int valid = cur_valid;
+    if (j + 1 < nst) {
+      walk_to(j + 1);
+      issue(BUF ^ 1);
+    }
     // dP^T's accumulators start at the query's -Delta (lane-local), so the MFMAs leave
     // dP^T - Delta
     f32x16 s[2], dp[2];
@@ -468,11 +483,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         const bf16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dq[dt] = mfma32x32x16(ka, pb[G], dq[dt]);
       }
+    cur_valid = nx_valid;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
-  if (nst > 0) issue(0, 0);
+  if (nst > 0) {
+    stage_at(0, nx_start, nx_valid);
+    nx_text = 0 < n0;
+    issue(0);
+    cur_valid = nx_valid;
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int j = 0; j < nst; j += 2) {
