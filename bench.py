@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per softmax launch from rocprofv3 FETCH_SIZE (x2.000) + WRITE_SIZE (x1.000),
 # scaled by a plain 1 GiB copy (profiles/hbm_traffic_768p_bf16_layer.md); valid only for
 # the kernel source it was measured on.
-PMC_TRAFFIC = {"source_sha256_16": "2ba0843e05bf32d5", "bytes": 15.541e9}
+PMC_TRAFFIC = {"source_sha256_16": "8084566fdbde4b79", "bytes": 13.359e9}
 # the same for the fp8 kernel on the 120-frame workload (same source file)
-PMC_TRAFFIC_FP8 = {"source_sha256_16": "2ba0843e05bf32d5", "bytes": 25.436e9}
+PMC_TRAFFIC_FP8 = {"source_sha256_16": "8084566fdbde4b79", "bytes": 25.528e9}
 # the same for the MXFP8 GEMM (profiles/kernel_stats_768p_mxfp8_projections.md)
 PMC_TRAFFIC_MX = {"source_sha256_16": "23628d501f41ade5", "bytes": 24.763e9}
 MX_SOURCES = ("video_diffusion_hybrid_sparse_amd/csrc/mxfp8.hip", "video_diffusion_hybrid_sparse_amd/csrc/mxfp8.h",

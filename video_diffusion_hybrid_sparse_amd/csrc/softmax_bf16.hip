@@ -163,7 +163,7 @@ __device__ __forceinline__ void softmax_sw_tile(const SoftmaxArgs& a, const int 
   constexpr int LA = 3;                      // operand reads in flight ahead of their MFMAs (4, 5: level or slower)
   constexpr int kExpSlot = 4;                // first MFMA slot of a first-pass block's exponentials
   constexpr int kExpSlot8 = 3;               // the same after a block of fp8 score MFMAs (4, 6: slower)
-  constexpr int kCopySlot = 4;               // slot (mod the copy spacing) of a block's stage copies
+  constexpr int kCopySlot = 2;               // slot (mod the copy spacing) of a block's stage copies (0, 4, 6: slower)
   constexpr int kWpv = 8, kWsum = 4, kWqk8 = 16;  // slot weights of the fp8 blocks' exponentials
   // vector-memory instructions of the most recent stage copy that a wait may leave in
   // flight: the fewest one stage issues (fp8 video stages copy half the key bytes)
